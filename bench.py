@@ -1,0 +1,217 @@
+#!/usr/bin/env python3
+"""Throughput of the stacked-LSTM forward pass on one MI355X.
+
+One step = one lstm_fwd call: the whole forward pass (every layer, every
+timestep) over one batch of the seeded synthetic workload, inputs resident in
+HBM.  Prints one JSON line:
+
+  value        TFLOP/s of the whole step, FLOPs = sum_l 2*4H*(I_l+H)*B*T
+  ms_per_step  mean wall time of one step (HIP events around K steps)
+  roofline     the dominant kernel: algorithmic FLOPs per launch / its mean
+               launch time (HIP events the library records on its stream),
+               against the MI355X dense MFMA peak of the workload's dtype
+  cpu_baseline the fp64 oracle timed on the host cores (a baseline only)
+
+Default workload: 4-layer LSTM, I = H = 512, B = 64, T = 100, fp32.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}  # MI355X dense MFMA, published
+WORKLOAD_TEXT = {
+    "c1": "1-layer LSTM I=H=128 B=8 T=16 fp32",
+    "c2": "4-layer LSTM I=H=512 B=64 T=100 fp32",
+    "c3": "8-layer LSTM I=H=256 B=64 T=200 bf16 (fp32 accumulate and cell state)",
+    "c4": "4-layer LSTM I=H=4096 B=32 T=50 bf16 (fp32 accumulate and cell state)",
+    "c5": "1-layer LSTM I=H=1536 B=4 T=2048 bf16 (fp32 accumulate and cell state)",
+}
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_flops(cfg, kind: int, regime: int, launch_index: int) -> float:
+    """Algorithmic FLOPs of one launch (2 per multiply-add; bias and gate math excluded)."""
+    H, B, T, L, I = cfg.H, cfg.B, cfg.T, cfg.L, cfg.I
+    if kind == 1:  # input GEMM of one layer; launch 0 is layer 0
+        layer = 0 if regime == 2 else launch_index // 2
+        il = I if layer == 0 else H
+        return 2.0 * 4 * H * il * B * T
+    if regime == 2:  # wavefront: R h for every layer + fused W u for layers >= 1
+        return 2.0 * 4 * H * H * B * T * L + 2.0 * 4 * H * H * B * T * (L - 1)
+    return 2.0 * 4 * H * H * B * T  # layerwise: one layer's recurrence
+
+
+def cpu_baseline(inp, cfg, min_seconds: float) -> dict:
+    import numpy as np  # noqa: F401
+    from oracle.lstm_oracle import lstm_forward_inputs
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        lstm_forward_inputs(inp)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds or reps >= 50:
+            break
+    return {"value": cfg.flops * reps / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"the whole workload ({cfg.name}) run {reps}x by the fp64 NumPy oracle in {el:.1f} s "
+                      f"({el / reps * 1e3:.0f} ms per forward)"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="c2", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--regime", type=int, default=0, help="0 auto, 1 layerwise, 2 wavefront")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the forward pass here runs on a single MI355X and this build "
+              "has no multi-GPU path (sharding is described in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    import lstm_inputs as li
+    import stacked_lstm_forward_amd as sl
+    from stacked_lstm_forward_amd import runner
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device", file=sys.stderr)
+        return 1
+    sl.load_library()
+    cfg = li.CONFIGS[args.config]
+    log(f"workload {cfg.name}: {WORKLOAD_TEXT[cfg.name]}; generating inputs")
+    inp = li.make_inputs(cfg)
+    prob = runner.prepare(inp, "cuda:0")
+    plan = sl.lstm_fwd_plan(prob.desc, args.regime).as_dict()
+    regime = 2 if plan["regime"] == "wavefront" else 1
+    log(f"plan {plan}")
+
+    stream = torch.cuda.current_stream()
+    maxl = 16
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * maxl)] for _ in range(args.steps)]
+    for row in evs:  # torch creates the HIP event on first record
+        for e in row:
+            e.record(stream)
+    torch.cuda.synchronize()
+    kinds = [(ctypes.c_int32 * maxl)() for _ in range(args.steps)]
+    nls = [ctypes.c_int32(0) for _ in range(args.steps)]
+    opts_list = []
+    keep = []
+    for k in range(args.steps):
+        st_arr = (ctypes.c_void_p * maxl)(*[e.cuda_event for e in evs[k][:maxl]])
+        sp_arr = (ctypes.c_void_p * maxl)(*[e.cuda_event for e in evs[k][maxl:]])
+        keep += [st_arr, sp_arr]
+        o = sl.LstmOpts()
+        o.force_regime = args.regime
+        o.max_launches = maxl
+        o.ev_start = ctypes.cast(st_arr, ctypes.POINTER(ctypes.c_void_p))
+        o.ev_stop = ctypes.cast(sp_arr, ctypes.POINTER(ctypes.c_void_p))
+        o.launch_kind = kinds[k]
+        o.num_launches = ctypes.pointer(nls[k])
+        opts_list.append(o)
+    plain = sl.LstmOpts()
+    plain.force_regime = args.regime
+
+    for _ in range(args.warmup):
+        prob.run(stream, plain)
+    torch.cuda.synchronize()
+    st = sl.lstm_fwd_last_error(prob.ws, stream)
+    if st != sl.LSTM_OK:
+        print(f"warm-up failed: {sl.lstm_status_string(st)}", file=sys.stderr)
+        return 1
+    log(f"warm-up done ({args.warmup} steps); timing {args.steps} steps")
+
+    t_start, t_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for k in range(args.steps):
+        prob.run(stream, opts_list[k])
+    t_stop.record(stream)
+    torch.cuda.synchronize()
+    st = sl.lstm_fwd_last_error(prob.ws, stream)
+    if st != sl.LSTM_OK:
+        print(f"timed run failed: {sl.lstm_status_string(st)}", file=sys.stderr)
+        return 1
+    total_ms = t_start.elapsed_time(t_stop)
+    ms_step = total_ms / args.steps
+
+    # per-kernel durations from the library's launch events
+    per_kind: dict = {}
+    flops_kind: dict = {}
+    for k in range(args.steps):
+        n = nls[k].value
+        for j in range(n):
+            kind = kinds[k][j]
+            d = evs[k][j].elapsed_time(evs[k][maxl + j])
+            per_kind.setdefault(kind, []).append(d)
+            flops_kind.setdefault(kind, []).append(kernel_flops(cfg, kind, regime, j))
+    dom = max(per_kind, key=lambda kk: sum(per_kind[kk]))
+    dom_ms = sum(per_kind[dom]) / len(per_kind[dom])
+    dom_flops = sum(flops_kind[dom]) / len(flops_kind[dom])
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[cfg.dtype]
+    value = cfg.flops / (ms_step * 1e-3) / 1e12
+    y, hT, cT = prob.outputs_f32()
+    import numpy as np
+    if not (np.all(np.isfinite(y)) and np.all(np.isfinite(cT))):
+        print("non-finite outputs", file=sys.stderr)
+        return 1
+    log(f"{ms_step:.4f} ms/step, {value:.2f} TFLOP/s; dominant kernel kind {dom}: {dom_ms:.4f} ms/launch")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on the host (cpu_baseline)")
+        cpu = cpu_baseline(inp, cfg, args.cpu_seconds)
+
+    kname = {1: "lstm_input_gemm", 2: "lstm_rec_kernel"}
+    out = {
+        "metric": "stacked-LSTM fwd TFLOPS (% of MI355X roofline) and ms/sequence",
+        "value": round(value, 4),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "ms_per_sequence": round(ms_step / cfg.B, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if cfg.dtype == "f32" else "bf16",
+        "data": "synthetic (seeded: W,R,b ~ U(-1/sqrt(H),1/sqrt(H)), x ~ N(0,1), h0=c0=0)",
+        "config": {"workload": WORKLOAD_TEXT[cfg.name], "L": cfg.L, "I": cfg.I, "H": cfg.H, "B": cfg.B,
+                   "T": cfg.T, "regime": plan["regime"], "gflop_per_step": round(cfg.flops / 1e9, 3)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel": kname.get(dom, str(dom)), "ms_per_launch": round(dom_ms, 5),
+                     "gflop_per_launch": round(dom_flops / 1e9, 3)},
+        "whole_step_frac_of_mfma_peak": round(value / peak, 4),
+        "kernels_ms_per_launch": {kname.get(kk, str(kk)): round(sum(v) / len(v), 5) for kk, v in per_kind.items()},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,162 @@
+"""Python binding of the gfx950 stacked-LSTM forward library (``include/lstm_fwd.h``).
+
+Argument marshalling only: every step of the forward pass runs in the HIP
+kernels of ``lib/liblstm_fwd.so``.  PyTorch supplies device memory and streams.
+If the library is not built, loading it raises; there is no fallback.
+
+The functions carry the C names:
+
+    lstm_fwd_workspace_size(desc) -> int
+    lstm_fwd(desc, x, h0, c0, W, R, b, y, hT, cT, ws, stream=None) -> status
+    lstm_fwd_ex(desc, ..., ws, stream=None, opts=None) -> status
+    lstm_fwd_validate(desc, x, W, R, b, y, ws, ws_bytes) -> status
+    lstm_fwd_last_error(ws, stream=None) -> status
+    lstm_fwd_plan(desc, force_regime=0, num_cus=0, lds_per_cu=0) -> PlanInfo
+    lstm_status_string(status) -> str
+
+Tensor arguments may be torch tensors (their ``data_ptr()``), raw integer
+device addresses, or None for the nullable ones (h0, c0, hT, cT).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "lib", "liblstm_fwd.so")
+
+LSTM_F32, LSTM_BF16 = 0, 1
+LSTM_OK, LSTM_ERR_INVALID_ARG, LSTM_ERR_UNSUPPORTED, LSTM_ERR_WORKSPACE, LSTM_ERR_HIP, LSTM_ERR_BARRIER_TIMEOUT = range(6)
+LSTM_REGIME_AUTO, LSTM_REGIME_LAYERWISE, LSTM_REGIME_WAVEFRONT = 0, 1, 2
+LSTM_KERNEL_INPUT_GEMM, LSTM_KERNEL_RECURRENT = 1, 2
+
+EXPORTED = ("lstm_fwd_workspace_size", "lstm_fwd", "lstm_fwd_ex", "lstm_status_string",
+            "lstm_fwd_validate", "lstm_fwd_last_error", "lstm_fwd_plan")
+
+
+class LstmDesc(ctypes.Structure):
+    _fields_ = [("L", ctypes.c_int32), ("I", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("B", ctypes.c_int32), ("T", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class LstmOpts(ctypes.Structure):
+    _fields_ = [("force_regime", ctypes.c_int32), ("max_launches", ctypes.c_int32),
+                ("ev_start", ctypes.POINTER(ctypes.c_void_p)), ("ev_stop", ctypes.POINTER(ctypes.c_void_p)),
+                ("launch_kind", ctypes.POINTER(ctypes.c_int32)), ("num_launches", ctypes.POINTER(ctypes.c_int32)),
+                ("wait_timeout_us", ctypes.c_int64)]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("regime", ctypes.c_int32), ("num_launches", ctypes.c_int32), ("grid", ctypes.c_int32),
+                ("block", ctypes.c_int32), ("lds_bytes", ctypes.c_int32), ("ksplit", ctypes.c_int32),
+                ("weights_on_chip", ctypes.c_int32), ("layers_per_launch", ctypes.c_int32),
+                ("wg_per_layer", ctypes.c_int32 * 16), ("mtiles_per_wg", ctypes.c_int32 * 16)]
+
+    def as_dict(self) -> dict:
+        n = self.layers_per_launch
+        return {"regime": {1: "layerwise", 2: "wavefront"}.get(self.regime, self.regime),
+                "num_launches": self.num_launches, "grid": self.grid, "block": self.block,
+                "lds_bytes": self.lds_bytes, "ksplit": self.ksplit, "weights_on_chip": bool(self.weights_on_chip),
+                "layers_per_launch": n, "wg_per_layer": list(self.wg_per_layer[:n]),
+                "mtiles_per_wg": list(self.mtiles_per_wg[:n])}
+
+
+class LstmError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        super().__init__(f"{what}: {lstm_status_string(status)} ({status})")
+
+
+_lib = None
+
+
+def load_library() -> ctypes.CDLL:
+    """Load lib/liblstm_fwd.so (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m stacked_lstm_forward_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    pdesc = ctypes.POINTER(LstmDesc)
+    lib.lstm_fwd_workspace_size.argtypes = [pdesc]
+    lib.lstm_fwd_workspace_size.restype = sz
+    lib.lstm_fwd.argtypes = [pdesc, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.lstm_fwd.restype = i32
+    lib.lstm_fwd_ex.argtypes = [pdesc, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(LstmOpts)]
+    lib.lstm_fwd_ex.restype = i32
+    lib.lstm_status_string.argtypes = [i32]
+    lib.lstm_status_string.restype = ctypes.c_char_p
+    lib.lstm_fwd_validate.argtypes = [pdesc, vp, vp, vp, vp, vp, vp, sz]
+    lib.lstm_fwd_validate.restype = i32
+    lib.lstm_fwd_last_error.argtypes = [vp, vp]
+    lib.lstm_fwd_last_error.restype = i32
+    lib.lstm_fwd_plan.argtypes = [pdesc, i32, i32, i32, ctypes.POINTER(PlanInfo)]
+    lib.lstm_fwd_plan.restype = i32
+    _lib = lib
+    return lib
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def make_desc(L: int, I: int, H: int, B: int, T: int, dtype) -> LstmDesc:
+    dt = {"f32": LSTM_F32, "bf16": LSTM_BF16}.get(dtype, dtype)
+    return LstmDesc(L, I, H, B, T, dt)
+
+
+def lstm_status_string(status: int) -> str:
+    return load_library().lstm_status_string(status).decode()
+
+
+def lstm_fwd_workspace_size(desc: LstmDesc) -> int:
+    return int(load_library().lstm_fwd_workspace_size(ctypes.byref(desc)))
+
+
+def lstm_fwd(desc, x, h0, c0, W, R, b, y, hT, cT, ws, stream=None) -> int:
+    return int(load_library().lstm_fwd(ctypes.byref(desc), _ptr(x), _ptr(h0), _ptr(c0), _ptr(W), _ptr(R), _ptr(b),
+                                       _ptr(y), _ptr(hT), _ptr(cT), _ptr(ws), _stream(stream)))
+
+
+def lstm_fwd_ex(desc, x, h0, c0, W, R, b, y, hT, cT, ws, stream=None, opts: Optional[LstmOpts] = None) -> int:
+    return int(load_library().lstm_fwd_ex(ctypes.byref(desc), _ptr(x), _ptr(h0), _ptr(c0), _ptr(W), _ptr(R),
+                                          _ptr(b), _ptr(y), _ptr(hT), _ptr(cT), _ptr(ws), _stream(stream),
+                                          None if opts is None else ctypes.byref(opts)))
+
+
+def lstm_fwd_validate(desc, x, W, R, b, y, ws, ws_bytes: int) -> int:
+    return int(load_library().lstm_fwd_validate(None if desc is None else ctypes.byref(desc), _ptr(x), _ptr(W),
+                                                _ptr(R), _ptr(b), _ptr(y), _ptr(ws), ws_bytes))
+
+
+def lstm_fwd_last_error(ws, stream=None) -> int:
+    return int(load_library().lstm_fwd_last_error(_ptr(ws), _stream(stream)))
+
+
+def lstm_fwd_plan(desc, force_regime: int = 0, num_cus: int = 0, lds_per_cu: int = 0) -> PlanInfo:
+    info = PlanInfo()
+    st = load_library().lstm_fwd_plan(ctypes.byref(desc), force_regime, num_cus, lds_per_cu, ctypes.byref(info))
+    if st != LSTM_OK:
+        raise LstmError(st, "lstm_fwd_plan")
+    return info
+
+
+def check(status: int, what: str = "lstm_fwd") -> None:
+    if status != LSTM_OK:
+        raise LstmError(status, what)

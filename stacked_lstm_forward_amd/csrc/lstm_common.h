@@ -1,0 +1,139 @@
+// Shared definitions of the stacked-LSTM forward kernels (gfx950 / CDNA4).
+//
+// Tile convention used by every kernel.  The four per-gate weight matrices are
+// grouped into one 4H-row matrix ("Optimizing Performance of Recurrent Neural
+// Networks on GPUs", proposed method: gate grouping).  Kernels walk that matrix
+// in 16-row "M-tiles" whose rows are gate-interleaved:
+//
+//     tile mt, row rho (0..15)  <->  hidden unit j = 4*mt + rho/4, gate k = rho%4
+//     caller row                 =   k*H + j           (gate blocks i, f, g, o)
+//
+// With the 16x16 MFMA output layout (lane l holds rows 4*(l/16)+r, column
+// l%16, r = 0..3) each lane ends up holding the four gate pre-activations of
+// one (unit, column) pair, so the gate non-linearities and the cell update run
+// in registers straight after the product.
+//
+// Operand fragments: per MFMA group a lane loads 32 contiguous bytes of one
+// row (8 fp32 or 16 bf16).  A "chunk" is the K range one 16-row tile covers
+// with one such load per lane: 32 fp32 or 64 bf16 columns (128 bytes per row).
+// The weight fragment and the activation fragment of a lane cover the same K
+// indices, so the sum over K is exact whatever order the hardware uses inside
+// one MFMA.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lstm {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct Frag {
+  uint4 v[2];  // 32 bytes: 8 fp32 or 16 bf16 of one row
+};
+
+template <bool BF16>
+struct Dt;
+template <>
+struct Dt<false> {
+  typedef float T;
+  static constexpr int KC = 32;  // K columns per chunk
+  static constexpr int SZ = 4;
+};
+template <>
+struct Dt<true> {
+  typedef uint16_t T;
+  static constexpr int KC = 64;
+  static constexpr int SZ = 2;
+};
+
+__device__ __forceinline__ Frag zero_frag() {
+  Frag f;
+  f.v[0] = make_uint4(0, 0, 0, 0);
+  f.v[1] = make_uint4(0, 0, 0, 0);
+  return f;
+}
+
+// acc += A(16 x 32-byte K slice) * B(32-byte K slice x 16)
+template <bool BF16>
+__device__ __forceinline__ void mfma_frag(f32x4& acc, const Frag& a, const Frag& b);
+
+template <>
+__device__ __forceinline__ void mfma_frag<true>(f32x4& acc, const Frag& a, const Frag& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a.v[0]),
+                                                __builtin_bit_cast(bf16x8, b.v[0]), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a.v[1]),
+                                                __builtin_bit_cast(bf16x8, b.v[1]), acc, 0, 0, 0);
+}
+
+template <>
+__device__ __forceinline__ void mfma_frag<false>(f32x4& acc, const Frag& a, const Frag& b) {
+  const float* fa0 = reinterpret_cast<const float*>(&a.v[0]);
+  const float* fb0 = reinterpret_cast<const float*>(&b.v[0]);
+  const float* fa1 = reinterpret_cast<const float*>(&a.v[1]);
+  const float* fb1 = reinterpret_cast<const float*>(&b.v[1]);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa0[e], fb0[e], acc, 0, 0, 0);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa1[e], fb1[e], acc, 0, 0, 0);
+}
+
+// Load the 32-byte fragment of row `row` starting at column k0 of a row-major
+// [rows][ld] matrix, zero-filling columns >= K.  `vec_ok` says 16-byte loads
+// are aligned (base and ld*size multiples of 16 bytes).
+template <bool BF16>
+__device__ __forceinline__ Frag load_frag(const void* base, long ld, long row, int k0, int K, bool vec_ok) {
+  typedef typename Dt<BF16>::T T;
+  constexpr int N = 32 / Dt<BF16>::SZ;
+  const T* p = reinterpret_cast<const T*>(base) + row * ld + k0;
+  Frag f;
+  if (vec_ok && k0 + N <= K) {
+    const uint4* q = reinterpret_cast<const uint4*>(p);
+    f.v[0] = q[0];
+    f.v[1] = q[1];
+    return f;
+  }
+  T tmp[N];
+#pragma unroll
+  for (int e = 0; e < N; ++e) tmp[e] = (k0 + e < K) ? p[e] : T(0);
+  __builtin_memcpy(&f, tmp, 32);
+  return f;
+}
+
+// Caller row of tile row rho of M-tile mt (gate-interleaved order); -1 past H.
+__device__ __forceinline__ long tile_row(int mt, int rho, int H) {
+  const int j = 4 * mt + (rho >> 2);
+  return j < H ? (long)(rho & 3) * H + j : -1;
+}
+
+// Logistic function from its definition 1 / (1 + e^{-z}), with the hardware
+// base-2 exponential (v_exp_f32) and reciprocal (v_rcp_f32).  Saturates to
+// exactly 1.0 (e^{-z} underflows to 0) and 0.0 (e^{-z} overflows to +inf).
+__device__ __forceinline__ float sigmoid_f(float z) {
+  const float e = __builtin_amdgcn_exp2f(-1.4426950408889634f * z);
+  return __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// tanh(z) = 2 sigmoid(2z) - 1; exact +-1 at saturation, absolute error ~1e-7 near 0.
+__device__ __forceinline__ float tanh_f(float z) { return 2.0f * sigmoid_f(2.0f * z) - 1.0f; }
+
+__device__ __forceinline__ float to_float(float v) { return v; }
+__device__ __forceinline__ float to_float(uint16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (NaN kept quiet)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <bool BF16>
+__device__ __forceinline__ typename Dt<BF16>::T from_float(float f);
+template <>
+__device__ __forceinline__ float from_float<false>(float f) { return f; }
+template <>
+__device__ __forceinline__ uint16_t from_float<true>(float f) { return f32_to_bf16(f); }
+
+}  // namespace lstm

@@ -1,0 +1,299 @@
+// C-ABI entry points of the stacked-LSTM forward library (host side).
+//
+// lstm_fwd validates its arguments, asks the planner for a schedule, carves
+// the caller's workspace and enqueues the kernels on the caller's stream:
+//   1. the grouped input-projection GEMM of layer 0 over all timesteps (it
+//      also zeroes the error word and the step counters in the workspace);
+//   2. LAYERWISE: per layer, the persistent recurrence, then the next layer's
+//      input GEMM;  WAVEFRONT: one persistent launch that runs every layer.
+// Nothing here synchronises the host.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+
+#include "../../include/lstm_fwd.h"
+#include "lstm_params.h"
+#include "lstm_plan.h"
+
+namespace lstm {
+hipError_t launch_input_gemm(bool bf16, const GemmParams& p, hipStream_t s);
+hipError_t rec_prepare(bool bf16, int ks, int lds_bytes, int* max_blocks_per_cu);
+hipError_t launch_rec(bool bf16, int ks, const RecParams& p, int lds_bytes, hipStream_t s);
+}  // namespace lstm
+
+using namespace lstm;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+constexpr long long kDefaultTimeoutUs = 2000000;  // 2 s per step wait
+
+struct DevCache {
+  bool ready = false;
+  DeviceInfo info;
+  long long clock_khz = 100000;  // wall clock (s_memrealtime) rate
+};
+DevCache g_dev[kMaxDevices];
+std::mutex g_dev_mu;
+
+lstm_status_t device_info(DevCache* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LSTM_ERR_HIP;
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  DevCache& c = g_dev[dev];
+  if (!c.ready) {
+    int cus = 0, lds = 0, clk = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return LSTM_ERR_HIP;
+    if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess) return LSTM_ERR_HIP;
+    if (hipDeviceGetAttribute(&clk, hipDeviceAttributeWallClockRate, dev) != hipSuccess) return LSTM_ERR_HIP;
+    c.info.num_cus = cus;
+    c.info.lds_per_block = lds;
+    c.clock_khz = clk > 0 ? clk : 100000;
+    c.ready = true;
+  }
+  *out = c;
+  return LSTM_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+lstm_status_t validate(const lstm_desc_t* d, const void* x, const void* W, const void* R, const void* b,
+                       const void* y, const void* ws) {
+  if (!d) return LSTM_ERR_INVALID_ARG;
+  if (d->L < 1 || d->I < 1 || d->H < 1 || d->B < 1 || d->T < 1) return LSTM_ERR_INVALID_ARG;
+  if (d->dtype != LSTM_F32 && d->dtype != LSTM_BF16) return LSTM_ERR_INVALID_ARG;
+  if (!x || !W || !R || !b || !y) return LSTM_ERR_INVALID_ARG;
+  if (!ws) return LSTM_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return LSTM_ERR_WORKSPACE;
+  return LSTM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lstm_status_string(lstm_status_t s) {
+  switch (s) {
+    case LSTM_OK: return "LSTM_OK";
+    case LSTM_ERR_INVALID_ARG: return "LSTM_ERR_INVALID_ARG";
+    case LSTM_ERR_UNSUPPORTED: return "LSTM_ERR_UNSUPPORTED";
+    case LSTM_ERR_WORKSPACE: return "LSTM_ERR_WORKSPACE";
+    case LSTM_ERR_HIP: return "LSTM_ERR_HIP";
+    case LSTM_ERR_BARRIER_TIMEOUT: return "LSTM_ERR_BARRIER_TIMEOUT";
+  }
+  return "LSTM_ERR_UNKNOWN";
+}
+
+lstm_status_t lstm_fwd_plan(const lstm_desc_t* d, int32_t force_regime, int32_t num_cus, int32_t lds_per_cu,
+                            lstm_plan_info_t* out) {
+  if (!d || !out) return LSTM_ERR_INVALID_ARG;
+  DeviceInfo info;
+  if (num_cus > 0) {
+    info.num_cus = num_cus;
+    info.lds_per_block = lds_per_cu > 0 ? lds_per_cu : 160 * 1024;
+  } else {
+    DevCache c;
+    lstm_status_t st = device_info(&c);
+    if (st != LSTM_OK) return st;
+    info = c.info;
+  }
+  Plan p;
+  const int rc = make_plan(d->L, d->I, d->H, d->B, d->T, d->dtype, force_regime, info, &p);
+  if (rc) return (lstm_status_t)rc;
+  *out = lstm_plan_info_t();
+  out->regime = p.regime;
+  out->num_launches = p.num_launches;
+  out->grid = p.rec[0].grid;
+  out->block = kRecThreads;
+  out->lds_bytes = p.rec[0].lds_bytes;
+  out->ksplit = p.rec[0].ks;
+  int on_chip = 1;
+  for (int r = 0; r < p.nrec; ++r)
+    for (int k = 0; k < p.rec[r].nlayers; ++k) on_chip &= p.rec[r].layers[k].staged;
+  out->weights_on_chip = on_chip;
+  out->layers_per_launch = p.rec[0].nlayers;
+  for (int k = 0; k < p.rec[0].nlayers && k < 16; ++k) {
+    out->wg_per_layer[k] = p.rec[0].layers[k].wg_count;
+    out->mtiles_per_wg[k] = p.rec[0].layers[k].mt_per_wg;
+  }
+  return LSTM_OK;
+}
+
+size_t lstm_fwd_workspace_size(const lstm_desc_t* d) {
+  if (!d) return 0;
+  // the layout does not depend on the device; any partition fits the same buffers
+  DeviceInfo info;
+  Plan p;
+  if (make_plan(d->L, d->I, d->H, d->B, d->T, d->dtype, LSTM_REGIME_LAYERWISE, info, &p)) return 0;
+  return p.ws_bytes;
+}
+
+lstm_status_t lstm_fwd_validate(const lstm_desc_t* d, const void* x, const void* W, const void* R, const void* b,
+                                const void* y, const void* ws, size_t ws_bytes) {
+  lstm_status_t st = validate(d, x, W, R, b, y, ws);
+  if (st != LSTM_OK) return st;
+  const size_t need = lstm_fwd_workspace_size(d);
+  if (need == 0) return LSTM_ERR_UNSUPPORTED;
+  if (ws_bytes < need) return LSTM_ERR_WORKSPACE;
+  return LSTM_OK;
+}
+
+lstm_status_t lstm_fwd_last_error(const void* ws, hipStream_t stream) {
+  if (!ws) return LSTM_ERR_WORKSPACE;
+  if (hipStreamSynchronize(stream) != hipSuccess) return LSTM_ERR_HIP;
+  int v = 0;
+  if (hipMemcpy(&v, ws, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess) return LSTM_ERR_HIP;
+  return v == 0 ? LSTM_OK : LSTM_ERR_BARRIER_TIMEOUT;
+}
+
+lstm_status_t lstm_fwd_ex(const lstm_desc_t* d, const void* x, const void* h0, const float* c0, const void* W,
+                          const void* R, const void* b, void* y, void* hT, float* cT, void* ws, hipStream_t stream,
+                          const lstm_fwd_opts_t* opts) {
+  lstm_status_t st = validate(d, x, W, R, b, y, ws);
+  if (st != LSTM_OK) return st;
+  DevCache dev;
+  st = device_info(&dev);
+  if (st != LSTM_OK) return st;
+  const int force = opts ? opts->force_regime : LSTM_REGIME_AUTO;
+  Plan p;
+  const int rc = make_plan(d->L, d->I, d->H, d->B, d->T, d->dtype, force, dev.info, &p);
+  if (rc) return (lstm_status_t)rc;
+
+  const int L = d->L, I = d->I, H = d->H, B = d->B, T = d->T;
+  const bool bf16 = p.bf16;
+  const size_t ds = p.dsize;
+  char* wsb = static_cast<char*>(ws);
+  int* err = reinterpret_cast<int*>(wsb + p.err_off);
+  int* flags = reinterpret_cast<int*>(wsb + p.flags_off);
+  float* G = reinterpret_cast<float*>(wsb + p.G_off);
+  char* hist = wsb + p.hist_off;
+  const char* Wb = static_cast<const char*>(W);
+  const char* Rb = static_cast<const char*>(R);
+  const char* bb = static_cast<const char*>(b);
+  auto W_l = [&](int l) -> const void* {
+    return l == 0 ? Wb : Wb + ((size_t)4 * H * I + (size_t)(l - 1) * 4 * H * H) * ds;
+  };
+  auto R_l = [&](int l) -> const void* { return Rb + (size_t)l * 4 * H * H * ds; };
+  auto b_l = [&](int l) -> const void* { return bb + (size_t)l * 4 * H * ds; };
+  auto out_l = [&](int l) -> void* {  // layer l's output sequence [T][B][H]
+    return l == L - 1 ? y : static_cast<void*>(hist + (size_t)l * T * B * H * ds);
+  };
+  auto state = [&](const void* base, int l, size_t esz) -> const void* {
+    return base ? static_cast<const char*>(base) + (size_t)l * B * H * esz : nullptr;
+  };
+
+  long long timeout_us = (opts && opts->wait_timeout_us > 0) ? opts->wait_timeout_us : kDefaultTimeoutUs;
+  if (opts && opts->wait_timeout_us < 0) timeout_us = 0;  // forces every blocked wait to fail (tests)
+  const long long timeout_ticks = timeout_us * dev.clock_khz / 1000;
+
+  int nl = 0;
+  const int maxl = (opts && opts->max_launches > 0) ? opts->max_launches : 0;
+  auto before = [&](int kind) {
+    if (nl < maxl) {
+      if (opts->launch_kind) opts->launch_kind[nl] = kind;
+      if (opts->ev_start && hipEventRecord(opts->ev_start[nl], stream) != hipSuccess) return false;
+    }
+    return true;
+  };
+  auto after = [&]() {
+    if (nl < maxl && opts->ev_stop && hipEventRecord(opts->ev_stop[nl], stream) != hipSuccess) return false;
+    ++nl;
+    return true;
+  };
+
+  auto gemm = [&](int l, const void* U, int K, bool zero) -> lstm_status_t {
+    GemmParams gp;
+    gp.W = W_l(l);
+    gp.U = U;
+    gp.bias = b_l(l);
+    gp.G = G;
+    gp.zero_ptr = zero ? reinterpret_cast<int*>(wsb) : nullptr;
+    gp.zero_count = zero ? (int)p.zero_ints : 0;
+    gp.K = K;
+    gp.H = H;
+    gp.Mt = p.Mt;
+    gp.B = B;
+    gp.N = T * B;
+    gp.vec_ok_w = aligned16(gp.W) && ((size_t)K * ds) % 16 == 0;
+    gp.vec_ok_u = aligned16(U) && ((size_t)K * ds) % 16 == 0;
+    if (!before(LSTM_KERNEL_INPUT_GEMM)) return LSTM_ERR_HIP;
+    if (launch_input_gemm(bf16, gp, stream) != hipSuccess) return LSTM_ERR_HIP;
+    if (!after()) return LSTM_ERR_HIP;
+    return LSTM_OK;
+  };
+
+  auto rec = [&](const LaunchPlan& lp) -> lstm_status_t {
+    RecParams rp;
+    rp.nlayers = lp.nlayers;
+    rp.T = T, rp.B = B, rp.H = H, rp.Mt = p.Mt, rp.ncnt = p.ncnt;
+    rp.ntgm = lp.ntgm, rp.ntgn = lp.ntgn, rp.mw = lp.mw, rp.nw = lp.nw;
+    rp.red_off = lp.red_off;
+    rp.grid = lp.grid;
+    rp.xcd_remap = (lp.grid % 8) == 0 ? 1 : 0;
+    rp.err = err;
+    rp.timeout_ticks = timeout_ticks;
+    for (int k = 0; k < lp.nlayers; ++k) {
+      const LayerPlan& pl = lp.layers[k];
+      const int l = pl.layer;
+      RecLayer& r = rp.layer[k];
+      r.W = pl.hoisted ? nullptr : W_l(l);
+      r.R = R_l(l);
+      r.bias = b_l(l);
+      r.G = pl.hoisted ? G : nullptr;
+      r.U = pl.hoisted ? nullptr : out_l(l - 1);
+      r.Y = out_l(l);
+      r.h0 = state(h0, l, ds);
+      r.c0 = static_cast<const float*>(state(c0, l, sizeof(float)));
+      r.hT = hT ? static_cast<char*>(hT) + (size_t)l * B * H * ds : nullptr;
+      r.cT = cT ? cT + (size_t)l * B * H : nullptr;
+      r.flags = flags + (size_t)l * kFlagsPerLayer;
+      const bool dep_here = !pl.hoisted && k > 0;
+      r.dep_flags = dep_here ? flags + (size_t)(l - 1) * kFlagsPerLayer : nullptr;
+      r.dep_count = dep_here ? lp.layers[k - 1].wg_count : 0;
+      r.Kin = pl.hoisted ? 0 : H;
+      r.wg_begin = pl.wg_begin;
+      r.wg_count = pl.wg_count;
+      r.mt_per_wg = pl.mt_per_wg;
+      r.staged = pl.staged;
+      const size_t row_bytes = (size_t)H * ds;
+      r.vec_ok = (row_bytes % 16 == 0) && aligned16(r.R) && aligned16(r.Y) && (!r.W || aligned16(r.W)) &&
+                 (!r.U || aligned16(r.U)) && (!r.h0 || aligned16(r.h0));
+    }
+    for (int k = lp.nlayers; k < kMaxLayersPerLaunch; ++k) rp.layer[k] = RecLayer();
+    int per_cu = 0;
+    if (rec_prepare(bf16, lp.ks, lp.lds_bytes, &per_cu) != hipSuccess) return LSTM_ERR_HIP;
+    if ((long long)per_cu * dev.info.num_cus < lp.grid) return LSTM_ERR_UNSUPPORTED;  // not co-resident
+    if (!before(LSTM_KERNEL_RECURRENT)) return LSTM_ERR_HIP;
+    if (launch_rec(bf16, lp.ks, rp, lp.lds_bytes, stream) != hipSuccess) return LSTM_ERR_HIP;
+    if (!after()) return LSTM_ERR_HIP;
+    return LSTM_OK;
+  };
+
+  // layer 0 input projection (+ zeroing of the error word and step counters)
+  st = gemm(0, x, I, true);
+  if (st != LSTM_OK) return st;
+  if (p.regime == LSTM_REGIME_WAVEFRONT) {
+    for (int r = 0; r < p.nrec; ++r) {
+      st = rec(p.rec[r]);
+      if (st != LSTM_OK) return st;
+    }
+  } else {
+    for (int l = 0; l < L; ++l) {
+      if (l > 0) {
+        st = gemm(l, out_l(l - 1), H, false);
+        if (st != LSTM_OK) return st;
+      }
+      st = rec(p.rec[l]);
+      if (st != LSTM_OK) return st;
+    }
+  }
+  if (opts && opts->num_launches) *opts->num_launches = nl;
+  return LSTM_OK;
+}
+
+lstm_status_t lstm_fwd(const lstm_desc_t* d, const void* x, const void* h0, const float* c0, const void* W,
+                       const void* R, const void* b, void* y, void* hT, float* cT, void* ws, hipStream_t stream) {
+  return lstm_fwd_ex(d, x, h0, c0, W, R, b, y, hT, cT, ws, stream, nullptr);
+}
+
+}  // extern "C"

@@ -1,0 +1,64 @@
+// Kernel parameter blocks shared by the host planner and the device kernels.
+#pragma once
+
+#include <stdint.h>
+
+namespace lstm {
+
+constexpr int kMaxLayersPerLaunch = 16;  // layers one recurrent launch can run as a wavefront
+constexpr int kFlagsPerLayer = 1024;     // step-counter slots per layer (max workgroups per layer)
+constexpr int kRecThreads = 256;         // 4 waves of 64
+constexpr int kGemmThreads = 256;
+constexpr int kGemmTileM = 128;          // rows (8 M-tiles) per input-GEMM workgroup
+constexpr int kGemmTileN = 128;          // columns (time x batch) per input-GEMM workgroup
+
+// Input projection G = W_l U^T + b_l over all T*B columns (hoisted out of the recurrence).
+// Output layout [T][Mt][B][16] fp32: for step t, M-tile mt, batch b, the 16
+// gate-interleaved rows (unit 4*mt + rho/4, gate rho%4).
+struct GemmParams {
+  const void* W;     // [4H][K] (caller layout, gate blocks)
+  const void* U;     // [T*B][K]
+  const void* bias;  // [4H]
+  float* G;          // [T][Mt][B][16]
+  int* zero_ptr;     // if non-null: workgroup 0 zeroes zero_count ints first (flags, error word)
+  int zero_count;
+  int K, H, Mt, B, N;  // N = T*B
+  int vec_ok_w, vec_ok_u;
+};
+
+// One layer of a recurrent launch.
+struct RecLayer {
+  const void* W;          // fused input weights W_l [4H][Kin], or null when the input is hoisted
+  const void* R;          // R_l [4H][H]
+  const void* bias;       // b_l [4H] (fused input only; hoisted G already holds the bias)
+  const float* G;         // hoisted pre-activations [T][Mt][B][16], or null
+  const void* U;          // fused input sequence [T][B][Kin] (output of the layer below), or null
+  void* Y;                // this layer's output sequence [T][B][H]
+  const void* h0;         // [B][H] or null (zeros)
+  const float* c0;        // [B][H] or null (zeros)
+  void* hT;               // [B][H] or null
+  float* cT;              // [B][H] or null
+  int* flags;             // per-workgroup step counters of this layer [wg_count]
+  const int* dep_flags;   // step counters of the producer of U in this launch, or null
+  int dep_count;          // workgroups of that producer
+  int Kin;                // fused input width (0 when hoisted)
+  int wg_begin, wg_count; // virtual workgroup ids owned by this layer
+  int mt_per_wg;          // M-tiles per workgroup
+  int staged;             // 1: weight rows kept in LDS for the whole sequence
+  int vec_ok;             // 16-byte loads allowed on W/R/U/Y/h0 rows
+};
+
+struct RecParams {
+  RecLayer layer[kMaxLayersPerLaunch];
+  int nlayers;
+  int T, B, H, Mt, ncnt;  // ncnt = ceil(B/16) column tiles
+  int ntgm, ntgn;         // tile groups: ntgm*ntgn = 4/ksplit; group g -> (g%ntgm, g/ntgm)
+  int mw, nw;             // max tiles per wave in M and N (<= 4)
+  int red_off;            // LDS byte offset of the cross-wave reduction area
+  int grid;               // launched workgroups
+  int xcd_remap;          // 1: map blockIdx round-robin over 8 XCDs to contiguous virtual ids
+  int* err;               // device error word (0 ok, 1 step-wait timeout)
+  long long timeout_ticks;  // per-wait limit in wall-clock ticks
+};
+
+}  // namespace lstm

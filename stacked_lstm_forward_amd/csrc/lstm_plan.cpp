@@ -1,0 +1,207 @@
+// Host planner of the stacked-LSTM forward pass (pure C++, no HIP calls).
+//
+// Two schedules:
+//   LAYERWISE  per layer: one input GEMM over all T*B columns, then one
+//              persistent recurrent launch for that layer.  Used when the
+//              layers' weights cannot all stay on chip at once (large H) or L = 1.
+//   WAVEFRONT  one input GEMM for layer 0, then one persistent launch in which
+//              every layer owns its own workgroups and its own weight rows in
+//              LDS; layer l+1 fuses its input product W_{l+1} h^l_t into the
+//              step and starts step t as soon as layer l has published it.
+// The wavefront is the network-level overlap of layers ("Optimizing
+// Performance of Recurrent Neural Networks on GPUs", proposed method and key
+// results on layer overlap); keeping each workgroup's rows in LDS across all
+// steps is the persistent-kernel idea ("Persistent RNNs").  The per-layer
+// workgroup partition plays the role of the pages' hand-tuned kernel choice
+// under concurrency: each concurrently running layer gets a share of the CUs
+// sized to its work instead of the whole GPU.
+#include "lstm_plan.h"
+
+#include <algorithm>
+
+namespace lstm {
+
+namespace {
+
+constexpr int kStatusOk = 0, kInvalid = 1, kUnsupported = 2;
+constexpr int kRegimeAuto = 0, kRegimeLayerwise = 1, kRegimeWavefront = 2;
+constexpr int kFragBytes = 32;  // one lane's fragment
+constexpr int kLdsReserve = 256;  // static LDS of the kernel
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// Choose the K split and the tile groups of a launch whose largest workgroup
+// owns `mmax` M-tiles; fills ks/ntgm/ntgn/mw/nw/red_off/lds_bytes.  `staged_bytes`
+// is the LDS the weight rows need (0 when streamed).  Returns false if nothing fits.
+bool choose_split(int mmax, int ncnt, int staged_bytes, int lds_limit, LaunchPlan* lp) {
+  static const int ks_order[3] = {4, 2, 1};
+  for (int ks : ks_order) {
+    const int ntg = 4 / ks;
+    int best_ntgm = -1, best_cost = 1 << 30;
+    for (int ntgm = 1; ntgm <= ntg; ntgm *= 2) {
+      const int ntgn = ntg / ntgm;
+      const int mw = cdiv(mmax, ntgm), nw = cdiv(ncnt, ntgn);
+      if (mw > 4 || nw > 4) continue;
+      // re-read cost proxy: each tile group re-reads the weights of its M-tiles and
+      // the activations of its column tiles
+      const int cost = ntgn * mmax + ntgm * ncnt;
+      if (cost < best_cost) best_cost = cost, best_ntgm = ntgm;
+    }
+    if (best_ntgm < 0) continue;
+    const int ntgm = best_ntgm, ntgn = ntg / ntgm;
+    const int mw = cdiv(mmax, ntgm), nw = cdiv(ncnt, ntgn);
+    const int red = ks > 1 ? ntg * mw * nw * ks * 64 * 16 : 0;
+    const int red_off = (staged_bytes + 255) & ~255;
+    if (red_off + red + kLdsReserve > lds_limit) continue;
+    lp->ks = ks, lp->ntgm = ntgm, lp->ntgn = ntgn, lp->mw = mw, lp->nw = nw;
+    lp->red_off = red_off;
+    lp->lds_bytes = red_off + red;
+    return true;
+  }
+  return false;
+}
+
+int round_grid(int g) { return (g + 7) & ~7; }
+
+// Single-layer persistent launch (hoisted input).
+bool plan_single(int layer, int Mt, int nch, int ncnt, const DeviceInfo& dev, LaunchPlan* lp) {
+  const int gmax = dev.num_cus;
+  int m = std::max(1, cdiv(Mt, gmax));
+  if (m > 16) return false;
+  const int wgs = cdiv(Mt, m);
+  LayerPlan& L = lp->layers[0];
+  L = LayerPlan();
+  L.layer = layer, L.hoisted = 1, L.Kin = 0, L.nch = nch;
+  L.wg_begin = 0, L.wg_count = wgs, L.mt_per_wg = m;
+  lp->nlayers = 1;
+  const int staged_bytes = m * nch * 64 * kFragBytes;
+  if (choose_split(m, ncnt, staged_bytes, dev.lds_per_block, lp)) {
+    L.staged = 1;
+  } else if (choose_split(m, ncnt, 0, dev.lds_per_block, lp)) {
+    L.staged = 0;
+  } else {
+    return false;
+  }
+  lp->grid = round_grid(wgs);
+  return wgs <= kFlagsPerLayer && lp->grid <= std::max(gmax, 8);
+}
+
+// Wavefront launch over layers [l0, l0+n): layer 0 hoisted, others fused.
+bool plan_wavefront(int l0, int n, int Mt, int nch_h, int nch_in0, int ncnt, const DeviceInfo& dev,
+                    LaunchPlan* lp) {
+  const int gmax = dev.num_cus;
+  int nchl[kMaxLayersPerLaunch];
+  for (int k = 0; k < n; ++k) {
+    const int l = l0 + k;
+    nchl[k] = (l == 0) ? nch_h : nch_in0 + nch_h;  // fused layers: input chunks + recurrent chunks
+  }
+  // smallest per-workgroup budget (chunks x M-tiles) whose partition fits the grid
+  int best_budget = -1;
+  int budgets[kMaxLayersPerLaunch * 16];
+  int nb = 0;
+  for (int k = 0; k < n; ++k)
+    for (int m = 1; m <= 16; ++m) budgets[nb++] = m * nchl[k];
+  std::sort(budgets, budgets + nb);
+  int mt[kMaxLayersPerLaunch];
+  for (int bi = 0; bi < nb; ++bi) {
+    const int wb = budgets[bi];
+    int tot = 0;
+    bool ok = true;
+    for (int k = 0; k < n; ++k) {
+      const int m = std::min(16, std::max(1, wb / nchl[k]));
+      if (m * nchl[k] > wb && m > 1) { ok = false; break; }
+      mt[k] = m;
+      tot += cdiv(Mt, m);
+    }
+    if (ok && tot <= gmax) { best_budget = wb; break; }
+  }
+  if (best_budget < 0) return false;
+  int mmax = 1, staged_max = 0, begin = 0;
+  lp->nlayers = n;
+  for (int k = 0; k < n; ++k) {
+    LayerPlan& L = lp->layers[k];
+    L = LayerPlan();
+    L.layer = l0 + k;
+    L.hoisted = (l0 + k == 0) ? 1 : 0;
+    L.nch = nchl[k];
+    L.mt_per_wg = mt[k];
+    L.wg_count = cdiv(Mt, mt[k]);
+    L.wg_begin = begin;
+    L.staged = 1;
+    begin += L.wg_count;
+    mmax = std::max(mmax, mt[k]);
+    staged_max = std::max(staged_max, mt[k] * nchl[k] * 64 * kFragBytes);
+  }
+  if (!choose_split(mmax, ncnt, staged_max, dev.lds_per_block, lp)) return false;
+  lp->grid = round_grid(begin);
+  for (int k = 0; k < n; ++k)
+    if (lp->layers[k].wg_count > kFlagsPerLayer) return false;
+  return lp->grid <= std::max(gmax, 8);
+}
+
+}  // namespace
+
+int make_plan(const int32_t L, const int32_t I, const int32_t H, const int32_t B, const int32_t T,
+              const int32_t dtype, int force_regime, const DeviceInfo& dev, Plan* out) {
+  if (L < 1 || I < 1 || H < 1 || B < 1 || T < 1) return kInvalid;
+  if (dtype != 0 && dtype != 1) return kInvalid;
+  if (force_regime < kRegimeAuto || force_regime > kRegimeWavefront) return kInvalid;
+  if (dev.num_cus < 1) return kInvalid;
+  Plan& p = *out;
+  p = Plan();
+  p.bf16 = dtype == 1;
+  p.KC = p.bf16 ? 64 : 32;
+  p.dsize = p.bf16 ? 2 : 4;
+  p.Mt = cdiv(H, 4);
+  p.ncnt = cdiv(B, 16);
+  if (p.ncnt > 16) return kUnsupported;                     // B > 256
+  if ((long long)L > 64) return kUnsupported;
+  if ((long long)T * B > (1LL << 31) / 16 || (long long)H * 4 > (1LL << 30)) return kUnsupported;
+
+  const int nch_h = cdiv(H, p.KC);
+  const int nch_hin = cdiv(H, p.KC);  // input width of layers >= 1 is H
+
+  bool wave = false;
+  if (force_regime == kRegimeWavefront || (force_regime == kRegimeAuto && L >= 2)) {
+    // try the wavefront: groups of up to 16 layers per launch
+    int nrec = 0;
+    bool ok = true;
+    for (int l0 = 0; l0 < L; l0 += kMaxLayersPerLaunch) {
+      const int n = std::min(kMaxLayersPerLaunch, L - l0);
+      if (!plan_wavefront(l0, n, p.Mt, nch_h, nch_hin, p.ncnt, dev, &p.rec[nrec])) { ok = false; break; }
+      ++nrec;
+    }
+    if (ok) {
+      wave = true;
+      p.nrec = nrec;
+      p.ngemm = 1;
+    } else if (force_regime == kRegimeWavefront) {
+      return kUnsupported;
+    }
+  }
+  if (!wave) {
+    p.nrec = L;
+    p.ngemm = L;
+    for (int l = 0; l < L; ++l)
+      if (!plan_single(l, p.Mt, nch_h, p.ncnt, dev, &p.rec[l])) return kUnsupported;
+  }
+  p.regime = wave ? kRegimeWavefront : kRegimeLayerwise;
+  p.num_launches = p.nrec + p.ngemm;
+
+  // workspace: [error word | step counters L x kFlagsPerLayer | G (one layer) | layer outputs 0..L-2]
+  size_t off = 0;
+  p.err_off = off;
+  off += 256;
+  p.flags_off = off;
+  off += align256((size_t)L * kFlagsPerLayer * sizeof(int));
+  p.zero_ints = off / sizeof(int);
+  p.G_off = off;
+  off += align256((size_t)T * p.Mt * B * 16 * sizeof(float));
+  p.hist_off = off;
+  off += align256((size_t)(L - 1) * T * B * H * p.dsize);
+  p.ws_bytes = off;
+  return kStatusOk;
+}
+
+}  // namespace lstm

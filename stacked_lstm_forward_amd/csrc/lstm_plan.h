@@ -1,0 +1,53 @@
+// Host planner: decides the schedule, the workgroup partition and the
+// workspace layout of one lstm_fwd call.  Pure host code (no HIP calls).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "lstm_params.h"
+
+namespace lstm {
+
+struct DeviceInfo {
+  int num_cus = 256;        // compute units
+  int lds_per_block = 160 * 1024;
+};
+
+struct LayerPlan {
+  int layer = 0;        // network layer index
+  int hoisted = 1;      // 1: input product from the input GEMM; 0: fused W_l u_t per step
+  int Kin = 0;          // fused input width (0 when hoisted)
+  int nch = 0;          // K chunks per tile row (fused input + recurrent)
+  int wg_begin = 0, wg_count = 0, mt_per_wg = 0;
+  int staged = 0;
+};
+
+struct LaunchPlan {
+  int nlayers = 0;
+  LayerPlan layers[kMaxLayersPerLaunch];
+  int ks = 4, ntgm = 1, ntgn = 1, mw = 1, nw = 1;
+  int lds_bytes = 0, red_off = 0;
+  int grid = 0;
+};
+
+struct Plan {
+  int regime = 0;       // lstm_regime_t
+  int bf16 = 0;
+  int KC = 32;          // K columns per chunk
+  int dsize = 4;
+  int Mt = 0, ncnt = 0;
+  int nrec = 0;         // recurrent launches
+  LaunchPlan rec[64];   // layerwise: one per layer; wavefront: one per group of up to 16 layers
+  int ngemm = 0;        // input-GEMM launches
+  int num_launches = 0;
+  // workspace layout (bytes)
+  size_t err_off = 0, flags_off = 0, G_off = 0, hist_off = 0, ws_bytes = 0;
+  size_t zero_ints = 0; // ints zeroed at the start (error word + all step counters)
+};
+
+// Returns 0 on success, else an lstm_status_t.
+int make_plan(const int32_t L, const int32_t I, const int32_t H, const int32_t B, const int32_t T,
+              const int32_t dtype, int force_regime, const DeviceInfo& dev, Plan* out);
+
+}  // namespace lstm

@@ -1,0 +1,100 @@
+"""Torch plumbing around the C ABI: device copies of host arrays, output and
+workspace allocation, and one call of ``lstm_fwd``.  No LSTM arithmetic here.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+from . import (LSTM_BF16, LSTM_F32, LstmDesc, LstmOpts, check, lstm_fwd, lstm_fwd_ex,
+               lstm_fwd_workspace_size, make_desc)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def to_device_array(a: Optional[np.ndarray], dtype: str, device):
+    """Storage array (float32, or uint16 bf16 bits) -> device tensor (float32 / bfloat16)."""
+    torch = _torch()
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(a.astype(np.float32, copy=False))
+    return t.to(device)
+
+
+@dataclass
+class DeviceProblem:
+    desc: LstmDesc
+    x: object
+    W: object
+    R: object
+    b: object
+    h0: object
+    c0: object
+    y: object
+    hT: object
+    cT: object
+    ws: object
+    ws_bytes: int
+
+    def run(self, stream=None, opts: Optional[LstmOpts] = None) -> None:
+        if opts is None:
+            st = lstm_fwd(self.desc, self.x, self.h0, self.c0, self.W, self.R, self.b, self.y, self.hT, self.cT,
+                          self.ws, stream)
+        else:
+            st = lstm_fwd_ex(self.desc, self.x, self.h0, self.c0, self.W, self.R, self.b, self.y, self.hT,
+                             self.cT, self.ws, stream, opts)
+        check(st, "lstm_fwd")
+
+    def outputs_f32(self):
+        """(y, hT, cT) as float32 numpy arrays (synchronises)."""
+        return (self.y.float().cpu().numpy(), self.hT.float().cpu().numpy(), self.cT.float().cpu().numpy())
+
+
+def workspace(desc: LstmDesc, device):
+    """A 256-byte aligned uint8 workspace tensor of lstm_fwd_workspace_size(desc) bytes."""
+    torch = _torch()
+    n = lstm_fwd_workspace_size(desc)
+    if n == 0:
+        raise ValueError("unsupported problem: lstm_fwd_workspace_size returned 0")
+    raw = torch.empty(n + 256, dtype=torch.uint8, device=device)
+    off = (-raw.data_ptr()) % 256
+    return raw[off:off + n], n
+
+
+def prepare(inp, device="cuda:0") -> DeviceProblem:
+    """Copy an ``lstm_inputs.Inputs`` to the device and allocate outputs and workspace."""
+    torch = _torch()
+    c = inp.cfg
+    desc = make_desc(c.L, c.I, c.H, c.B, c.T, c.dtype)
+    pk = inp.packed()
+    tdt = torch.bfloat16 if c.dtype == "bf16" else torch.float32
+    x = to_device_array(pk["x"], c.dtype, device)
+    W = to_device_array(pk["W"], c.dtype, device)
+    R = to_device_array(pk["R"], c.dtype, device)
+    b = to_device_array(pk["b"], c.dtype, device)
+    h0 = to_device_array(pk["h0"], c.dtype, device)
+    c0 = None if pk["c0"] is None else torch.from_numpy(pk["c0"]).to(device)
+    y = torch.empty((c.T, c.B, c.H), dtype=tdt, device=device)
+    hT = torch.empty((c.L, c.B, c.H), dtype=tdt, device=device)
+    cT = torch.empty((c.L, c.B, c.H), dtype=torch.float32, device=device)
+    ws, n = workspace(desc, device)
+    return DeviceProblem(desc, x, W, R, b, h0, c0, y, hT, cT, ws, n)
+
+
+def forward(inp, device="cuda:0", opts: Optional[LstmOpts] = None):
+    """Run the HIP forward pass on ``inp``; returns float32 numpy (y, hT, cT)."""
+    prob = prepare(inp, device)
+    prob.run(opts=opts)
+    return prob.outputs_f32()
+
+
+__all__ = ["DeviceProblem", "prepare", "forward", "workspace", "to_device_array", "LSTM_F32", "LSTM_BF16"]

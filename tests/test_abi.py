@@ -1,0 +1,122 @@
+"""CPU tests of the C-ABI library: it loads, exports every declared entry
+point, and its host-only logic (validation, workspace size, planner) behaves.
+No compute call is made here (there may be no GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import lstm_inputs as li
+import stacked_lstm_forward_amd as sl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = []
+    inc = os.path.join(ROOT, "include")
+    for fn in sorted(os.listdir(inc)):
+        if not fn.endswith(".h"):
+            continue
+        text = open(os.path.join(inc, fn)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(", text, re.M):
+            names.append(m.group(1))
+    return names
+
+
+def test_library_loads_and_exports_all_declared_symbols():
+    lib = sl.load_library()
+    names = declared_functions()
+    assert set(names) == set(sl.EXPORTED), names
+    for n in names:
+        assert hasattr(lib, n), n
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+
+
+def test_status_strings():
+    assert sl.lstm_status_string(sl.LSTM_OK) == "LSTM_OK"
+    assert sl.lstm_status_string(sl.LSTM_ERR_BARRIER_TIMEOUT) == "LSTM_ERR_BARRIER_TIMEOUT"
+    assert sl.lstm_status_string(99) == "LSTM_ERR_UNKNOWN"
+
+
+FAKE = 1 << 20  # a non-null, 256-aligned fake address; validation never dereferences it
+
+
+def test_validate_error_paths():
+    d = sl.make_desc(2, 8, 8, 3, 4, "f32")
+    need = sl.lstm_fwd_workspace_size(d)
+    assert need > 0
+    v = sl.lstm_fwd_validate
+    assert v(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need) == sl.LSTM_OK
+    assert v(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need) == sl.LSTM_ERR_INVALID_ARG
+    for k in range(5):  # each required tensor
+        args = [FAKE] * 5
+        args[k] = None
+        assert v(d, *args, FAKE, need) == sl.LSTM_ERR_INVALID_ARG
+    assert v(d, FAKE, FAKE, FAKE, FAKE, FAKE, None, need) == sl.LSTM_ERR_WORKSPACE
+    assert v(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 16, need) == sl.LSTM_ERR_WORKSPACE   # misaligned
+    assert v(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1) == sl.LSTM_ERR_WORKSPACE
+    for field in ("L", "I", "H", "B", "T"):
+        bad = sl.make_desc(2, 8, 8, 3, 4, "f32")
+        setattr(bad, field, 0)
+        assert v(bad, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need) == sl.LSTM_ERR_INVALID_ARG
+        setattr(bad, field, -3)
+        assert v(bad, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need) == sl.LSTM_ERR_INVALID_ARG
+    bad = sl.make_desc(2, 8, 8, 3, 4, 7)
+    assert v(bad, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need) == sl.LSTM_ERR_INVALID_ARG
+    assert sl.lstm_fwd_workspace_size(bad) == 0
+
+
+def test_unsupported_batch():
+    d = sl.make_desc(1, 8, 8, 257, 4, "f32")
+    assert sl.lstm_fwd_workspace_size(d) == 0
+    assert sl.lstm_fwd_validate(d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30) == sl.LSTM_ERR_UNSUPPORTED
+
+
+def test_workspace_size_formula():
+    for name, c in li.CONFIGS.items():
+        d = sl.make_desc(c.L, c.I, c.H, c.B, c.T, c.dtype)
+        n = sl.lstm_fwd_workspace_size(d)
+        ds = 2 if c.dtype == "bf16" else 4
+        mt = (c.H + 3) // 4
+        expect = 256 + c.L * 1024 * 4 + c.T * mt * c.B * 16 * 4 + (c.L - 1) * c.T * c.B * c.H * ds
+        assert expect <= n <= expect + 4 * 256, (name, n, expect)
+
+
+EXPECTED_REGIME = {"c1": 1, "c2": 2, "c3": 2, "c4": 1, "c5": 1}
+
+
+@pytest.mark.parametrize("name", sorted(li.CONFIGS))
+def test_planner_on_mi355x_shape(name):
+    c = li.CONFIGS[name]
+    d = sl.make_desc(c.L, c.I, c.H, c.B, c.T, c.dtype)
+    info = sl.lstm_fwd_plan(d, 0, 256, 160 * 1024)
+    assert info.regime == EXPECTED_REGIME[name]
+    assert info.grid <= 256 and info.grid % 8 == 0
+    assert info.lds_bytes + 256 <= 160 * 1024
+    mt = (c.H + 3) // 4
+    for k in range(info.layers_per_launch):
+        assert info.wg_per_layer[k] * info.mtiles_per_wg[k] >= mt
+    if name in ("c2", "c3", "c5", "c1"):
+        assert info.weights_on_chip
+    if name == "c4":
+        assert not info.weights_on_chip  # 128 MiB per layer of R cannot stay in LDS
+    if info.regime == 2:
+        assert info.layers_per_launch == c.L
+        assert info.num_launches == 2
+    else:
+        assert info.num_launches == 2 * c.L
+
+
+def test_planner_forced_regimes_and_small_devices():
+    d = sl.make_desc(3, 5, 7, 3, 4, "bf16")
+    for regime in (1, 2):
+        info = sl.lstm_fwd_plan(d, regime, 256, 160 * 1024)
+        assert info.regime == regime
+    # a tiny device: everything still gets a partition with at least one M-tile per workgroup
+    info = sl.lstm_fwd_plan(sl.make_desc(4, 64, 64, 16, 4, "f32"), 1, 8, 64 * 1024)
+    assert info.grid <= 8
+    with pytest.raises(sl.LstmError):
+        sl.lstm_fwd_plan(sl.make_desc(1, 4, 4, 4, 4, "f32"), 9, 256, 160 * 1024)
