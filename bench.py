@@ -82,6 +82,10 @@ def main() -> int:
     ap.add_argument("--regime", type=int, default=0, help="0 auto, 1 layerwise, 2 wavefront")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a device-to-device copy of this many MiB (calibrates HBM traffic counters)")
+    ap.add_argument("--plain-launch", action="store_true",
+                    help="ordinary (not cooperative) launch of the persistent kernel, for profilers")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -98,6 +102,15 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a HIP device", file=sys.stderr)
         return 1
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n}), flush=True)
+        return 0
     sl.load_library()
     cfg = li.CONFIGS[args.config]
     log(f"workload {cfg.name}: {WORKLOAD_TEXT[cfg.name]}; generating inputs")
@@ -124,6 +137,7 @@ def main() -> int:
         keep += [st_arr, sp_arr]
         o = sl.LstmOpts()
         o.force_regime = args.regime
+        o.plain_launch = 1 if args.plain_launch else 0
         o.max_launches = maxl
         o.ev_start = ctypes.cast(st_arr, ctypes.POINTER(ctypes.c_void_p))
         o.ev_stop = ctypes.cast(sp_arr, ctypes.POINTER(ctypes.c_void_p))
@@ -132,6 +146,7 @@ def main() -> int:
         opts_list.append(o)
     plain = sl.LstmOpts()
     plain.force_regime = args.regime
+    plain.plain_launch = 1 if args.plain_launch else 0
 
     for _ in range(args.warmup):
         prob.run(stream, plain)

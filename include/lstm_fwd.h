@@ -110,6 +110,18 @@ typedef struct {
   int64_t wait_timeout_us;    /* device step-wait limit in microseconds; 0 selects the default (2 s);
                                  negative makes every wait that is not already satisfied fail at once
                                  (exercises the timeout path without waiting)                       */
+  int64_t *trace;             /* optional device buffer: per-step phase timestamps (wall-clock ticks)
+                                 of the first recurrent launch, for workgroups v = 0, s, 2s, ...
+                                 (s = trace_stride): trace[((v/s)*T + t)*8 + k], k = 0 step start,
+                                 1 dependencies met, 2 products done, 3 partial sums combined,
+                                 4 gates/stores issued, 5 step published; trace_wgs*T*8 entries    */
+  int32_t trace_wgs;          /* number of traced workgroups (0: no trace)                        */
+  int32_t trace_stride;       /* virtual workgroup stride between traced workgroups (>= 1)         */
+  int32_t plain_launch;       /* 1: launch the persistent kernel with an ordinary launch instead of a
+                                 cooperative one (for profilers that do not handle cooperative
+                                 launches).  Co-residency is still checked against the occupancy
+                                 limit; a grid that is not co-resident ends with
+                                 LSTM_ERR_BARRIER_TIMEOUT rather than a hang.                      */
 } lstm_fwd_opts_t;
 
 /* lstm_fwd with options (opts may be NULL, which equals lstm_fwd). */
@@ -149,6 +161,11 @@ typedef struct {
   int32_t layers_per_launch; /* layers one recurrent launch runs concurrently                  */
   int32_t wg_per_layer[16];  /* workgroups given to each layer of the first recurrent launch   */
   int32_t mtiles_per_wg[16]; /* 16-row tiles (4 units x 4 gates) per workgroup, per layer      */
+  int32_t tile_groups_m;     /* waves of a K-group that split the M-tiles (x tile_groups_n = 4/ksplit) */
+  int32_t tile_groups_n;     /* ... that split the 16-column batch tiles                      */
+  int32_t wave_tiles_m;      /* most M-tiles one wave computes                                 */
+  int32_t wave_tiles_n;      /* most column tiles one wave computes                            */
+  int32_t weights_streamed;  /* 1 if the first recurrent launch reads weights from HBM per step */
 } lstm_plan_info_t;
 
 /*

@@ -44,14 +44,18 @@ class LstmOpts(ctypes.Structure):
     _fields_ = [("force_regime", ctypes.c_int32), ("max_launches", ctypes.c_int32),
                 ("ev_start", ctypes.POINTER(ctypes.c_void_p)), ("ev_stop", ctypes.POINTER(ctypes.c_void_p)),
                 ("launch_kind", ctypes.POINTER(ctypes.c_int32)), ("num_launches", ctypes.POINTER(ctypes.c_int32)),
-                ("wait_timeout_us", ctypes.c_int64)]
+                ("wait_timeout_us", ctypes.c_int64), ("trace", ctypes.c_void_p),
+                ("trace_wgs", ctypes.c_int32), ("trace_stride", ctypes.c_int32), ("plain_launch", ctypes.c_int32)]
 
 
 class PlanInfo(ctypes.Structure):
     _fields_ = [("regime", ctypes.c_int32), ("num_launches", ctypes.c_int32), ("grid", ctypes.c_int32),
                 ("block", ctypes.c_int32), ("lds_bytes", ctypes.c_int32), ("ksplit", ctypes.c_int32),
                 ("weights_on_chip", ctypes.c_int32), ("layers_per_launch", ctypes.c_int32),
-                ("wg_per_layer", ctypes.c_int32 * 16), ("mtiles_per_wg", ctypes.c_int32 * 16)]
+                ("wg_per_layer", ctypes.c_int32 * 16), ("mtiles_per_wg", ctypes.c_int32 * 16),
+                ("tile_groups_m", ctypes.c_int32), ("tile_groups_n", ctypes.c_int32),
+                ("wave_tiles_m", ctypes.c_int32), ("wave_tiles_n", ctypes.c_int32),
+                ("weights_streamed", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
         n = self.layers_per_launch
@@ -59,7 +63,10 @@ class PlanInfo(ctypes.Structure):
                 "num_launches": self.num_launches, "grid": self.grid, "block": self.block,
                 "lds_bytes": self.lds_bytes, "ksplit": self.ksplit, "weights_on_chip": bool(self.weights_on_chip),
                 "layers_per_launch": n, "wg_per_layer": list(self.wg_per_layer[:n]),
-                "mtiles_per_wg": list(self.mtiles_per_wg[:n])}
+                "mtiles_per_wg": list(self.mtiles_per_wg[:n]),
+                "tile_groups": [self.tile_groups_m, self.tile_groups_n],
+                "wave_tiles": [self.wave_tiles_m, self.wave_tiles_n],
+                "weights_streamed": bool(self.weights_streamed)}
 
 
 class LstmError(RuntimeError):

@@ -13,8 +13,19 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIBDIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIBDIR, "liblstm_fwd.so")
-SOURCES = ["lstm_kernels.hip", "lstm_fwd.cpp", "lstm_plan.cpp"]
 ARCH = "gfx950"
+# (source, extra defines): the recurrent kernel is instantiated once per
+# (dtype, weight source) so the four variants compile in parallel
+UNITS = [
+    ("lstm_kernels.hip", []),
+    ("lstm_rec_inst.hip", ["-DLSTM_INST_BF16=0", "-DLSTM_INST_STREAM=0"]),
+    ("lstm_rec_inst.hip", ["-DLSTM_INST_BF16=0", "-DLSTM_INST_STREAM=1"]),
+    ("lstm_rec_inst.hip", ["-DLSTM_INST_BF16=1", "-DLSTM_INST_STREAM=0"]),
+    ("lstm_rec_inst.hip", ["-DLSTM_INST_BF16=1", "-DLSTM_INST_STREAM=1"]),
+    ("lstm_fwd.cpp", []),
+    ("lstm_plan.cpp", []),
+]
+BUILD_DIR = os.path.join(HERE, "_build")
 
 
 def hipcc() -> str:
@@ -24,19 +35,43 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+def _flags() -> list:
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+            # keep hipcc from forming packed fp32 instructions (v_pk_*_f32)
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-I", os.path.join(os.path.dirname(HERE), "include")]
+
+
 def build(verbose: bool = False) -> str:
+    from concurrent.futures import ThreadPoolExecutor
+
     os.makedirs(LIBDIR, exist_ok=True)
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    cc = hipcc()
+    jobs = []
+    for i, (src, defs) in enumerate(UNITS):
+        obj = os.path.join(BUILD_DIR, f"{i:02d}_{os.path.splitext(src)[0]}.o")
+        jobs.append((obj, [cc, *_flags(), *defs, "-c", os.path.join(CSRC, src), "-o", obj]))
+
+    def run(job):
+        obj, cmd = job
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed ({r.returncode}): {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+        return obj
+
+    workers = max(1, min(len(jobs), os.cpu_count() or 1, 8))
+    with ThreadPoolExecutor(workers) as ex:
+        objs = list(ex.map(run, jobs))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-           # keep hipcc from forming packed fp32 instructions (v_pk_*_f32)
-           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-I", os.path.join(os.path.dirname(HERE), "include"),
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+    link = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
+        print(" ".join(link), flush=True)
+    r = subprocess.run(link, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{r.stdout}\n{r.stderr}")
+        raise RuntimeError(f"link failed ({r.returncode}):\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
     return LIB
 

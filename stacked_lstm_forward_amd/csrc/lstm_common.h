@@ -79,14 +79,23 @@ __device__ __forceinline__ void mfma_frag<false>(f32x4& acc, const Frag& a, cons
   for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa1[e], fb1[e], acc, 0, 0, 0);
 }
 
-// Load the 32-byte fragment of row `row` starting at column k0 of a row-major
-// [rows][ld] matrix, zero-filling columns >= K.  `vec_ok` says 16-byte loads
-// are aligned (base and ld*size multiples of 16 bytes).
+// 32 bytes at p (16-byte aligned), two unconditional 16-byte loads
+__device__ __forceinline__ Frag load_frag_vec(const void* p) {
+  const uint4* q = reinterpret_cast<const uint4*>(p);
+  Frag f;
+  f.v[0] = q[0];
+  f.v[1] = q[1];
+  return f;
+}
+
+// Load 32 bytes (8 fp32 or 16 bf16) starting at element off + k0 of a row of
+// length K, zero-filling columns >= K.  `vec_ok` says 16-byte loads are
+// aligned there (every row start is a multiple of 16 bytes).
 template <bool BF16>
-__device__ __forceinline__ Frag load_frag(const void* base, long ld, long row, int k0, int K, bool vec_ok) {
+__device__ __forceinline__ Frag load_frag_off(const void* base, long off, int k0, int K, bool vec_ok) {
   typedef typename Dt<BF16>::T T;
   constexpr int N = 32 / Dt<BF16>::SZ;
-  const T* p = reinterpret_cast<const T*>(base) + row * ld + k0;
+  const T* p = reinterpret_cast<const T*>(base) + off + k0;
   Frag f;
   if (vec_ok && k0 + N <= K) {
     const uint4* q = reinterpret_cast<const uint4*>(p);
@@ -99,6 +108,12 @@ __device__ __forceinline__ Frag load_frag(const void* base, long ld, long row, i
   for (int e = 0; e < N; ++e) tmp[e] = (k0 + e < K) ? p[e] : T(0);
   __builtin_memcpy(&f, tmp, 32);
   return f;
+}
+
+// Same for row `row` of a row-major [rows][ld] matrix.
+template <bool BF16>
+__device__ __forceinline__ Frag load_frag(const void* base, long ld, long row, int k0, int K, bool vec_ok) {
+  return load_frag_off<BF16>(base, row * ld, k0, K, vec_ok);
 }
 
 // Caller row of tile row rho of M-tile mt (gate-interleaved order); -1 past H.

@@ -11,14 +11,14 @@
 
 #include <mutex>
 
-#include "../../include/lstm_fwd.h"
+#include "lstm_fwd.h"  // include/ is on the include path
 #include "lstm_params.h"
 #include "lstm_plan.h"
 
 namespace lstm {
 hipError_t launch_input_gemm(bool bf16, const GemmParams& p, hipStream_t s);
-hipError_t rec_prepare(bool bf16, int ks, int lds_bytes, int* max_blocks_per_cu);
-hipError_t launch_rec(bool bf16, int ks, const RecParams& p, int lds_bytes, hipStream_t s);
+hipError_t rec_prepare(bool bf16, bool stream, bool vec, int mw, int nw, int lds_bytes, int* max_blocks_per_cu);
+hipError_t launch_rec(bool bf16, bool stream, bool vec, const RecParams& p, int lds_bytes, bool plain, hipStream_t s);
 }  // namespace lstm
 
 using namespace lstm;
@@ -116,6 +116,11 @@ lstm_status_t lstm_fwd_plan(const lstm_desc_t* d, int32_t force_regime, int32_t 
     out->wg_per_layer[k] = p.rec[0].layers[k].wg_count;
     out->mtiles_per_wg[k] = p.rec[0].layers[k].mt_per_wg;
   }
+  out->tile_groups_m = p.rec[0].ntgm;
+  out->tile_groups_n = p.rec[0].ntgn;
+  out->wave_tiles_m = p.rec[0].mw;
+  out->wave_tiles_n = p.rec[0].nw;
+  out->weights_streamed = p.rec[0].stream;
   return LSTM_OK;
 }
 
@@ -167,6 +172,7 @@ lstm_status_t lstm_fwd_ex(const lstm_desc_t* d, const void* x, const void* h0, c
   int* flags = reinterpret_cast<int*>(wsb + p.flags_off);
   float* G = reinterpret_cast<float*>(wsb + p.G_off);
   char* hist = wsb + p.hist_off;
+  const size_t slot = p.slot_elems;  // elements between two steps of an exchange buffer
   const char* Wb = static_cast<const char*>(W);
   const char* Rb = static_cast<const char*>(R);
   const char* bb = static_cast<const char*>(b);
@@ -175,8 +181,8 @@ lstm_status_t lstm_fwd_ex(const lstm_desc_t* d, const void* x, const void* h0, c
   };
   auto R_l = [&](int l) -> const void* { return Rb + (size_t)l * 4 * H * H * ds; };
   auto b_l = [&](int l) -> const void* { return bb + (size_t)l * 4 * H * ds; };
-  auto out_l = [&](int l) -> void* {  // layer l's output sequence [T][B][H]
-    return l == L - 1 ? y : static_cast<void*>(hist + (size_t)l * T * B * H * ds);
+  auto xbuf = [&](int l) -> void* {  // layer l's exchange buffer: T slots of [B][H]
+    return static_cast<void*>(hist + (size_t)l * T * slot * ds);
   };
   auto state = [&](const void* base, int l, size_t esz) -> const void* {
     return base ? static_cast<const char*>(base) + (size_t)l * B * H * esz : nullptr;
@@ -201,10 +207,11 @@ lstm_status_t lstm_fwd_ex(const lstm_desc_t* d, const void* x, const void* h0, c
     return true;
   };
 
-  auto gemm = [&](int l, const void* U, int K, bool zero) -> lstm_status_t {
+  auto gemm = [&](int l, const void* U, long long u_slot, int K, bool zero) -> lstm_status_t {
     GemmParams gp;
     gp.W = W_l(l);
     gp.U = U;
+    gp.u_slot = u_slot;
     gp.bias = b_l(l);
     gp.G = G;
     gp.zero_ptr = zero ? reinterpret_cast<int*>(wsb) : nullptr;
@@ -215,23 +222,31 @@ lstm_status_t lstm_fwd_ex(const lstm_desc_t* d, const void* x, const void* h0, c
     gp.B = B;
     gp.N = T * B;
     gp.vec_ok_w = aligned16(gp.W) && ((size_t)K * ds) % 16 == 0;
-    gp.vec_ok_u = aligned16(U) && ((size_t)K * ds) % 16 == 0;
+    gp.vec_ok_u = aligned16(U) && ((size_t)K * ds) % 16 == 0 && ((size_t)u_slot * ds) % 16 == 0;
     if (!before(LSTM_KERNEL_INPUT_GEMM)) return LSTM_ERR_HIP;
     if (launch_input_gemm(bf16, gp, stream) != hipSuccess) return LSTM_ERR_HIP;
     if (!after()) return LSTM_ERR_HIP;
     return LSTM_OK;
   };
 
+  bool traced = false;  // only the first recurrent launch is traced
   auto rec = [&](const LaunchPlan& lp) -> lstm_status_t {
     RecParams rp;
     rp.nlayers = lp.nlayers;
+    rp.slot = (long long)slot;
     rp.T = T, rp.B = B, rp.H = H, rp.Mt = p.Mt, rp.ncnt = p.ncnt;
+    rp.ks = lp.ks;
     rp.ntgm = lp.ntgm, rp.ntgn = lp.ntgn, rp.mw = lp.mw, rp.nw = lp.nw;
     rp.red_off = lp.red_off;
     rp.grid = lp.grid;
     rp.xcd_remap = (lp.grid % 8) == 0 ? 1 : 0;
     rp.err = err;
     rp.timeout_ticks = timeout_ticks;
+    const bool tr = opts && opts->trace && opts->trace_wgs > 0 && !traced;
+    rp.trace = tr ? reinterpret_cast<long long*>(opts->trace) : nullptr;
+    rp.trace_wgs = tr ? opts->trace_wgs : 0;
+    rp.trace_stride = (tr && opts->trace_stride > 0) ? opts->trace_stride : 1;
+    traced = traced || tr;
     for (int k = 0; k < lp.nlayers; ++k) {
       const LayerPlan& pl = lp.layers[k];
       const int l = pl.layer;
@@ -240,15 +255,16 @@ lstm_status_t lstm_fwd_ex(const lstm_desc_t* d, const void* x, const void* h0, c
       r.R = R_l(l);
       r.bias = b_l(l);
       r.G = pl.hoisted ? G : nullptr;
-      r.U = pl.hoisted ? nullptr : out_l(l - 1);
-      r.Y = out_l(l);
+      r.U = pl.hoisted ? nullptr : xbuf(l - 1);
+      r.X = xbuf(l);
+      r.Yout = (l == L - 1) ? y : nullptr;
       r.h0 = state(h0, l, ds);
       r.c0 = static_cast<const float*>(state(c0, l, sizeof(float)));
       r.hT = hT ? static_cast<char*>(hT) + (size_t)l * B * H * ds : nullptr;
       r.cT = cT ? cT + (size_t)l * B * H : nullptr;
-      r.flags = flags + (size_t)l * kFlagsPerLayer;
+      r.flags = flags + (size_t)l * kFlagsPerLayer * kFlagStride;
       const bool dep_here = !pl.hoisted && k > 0;
-      r.dep_flags = dep_here ? flags + (size_t)(l - 1) * kFlagsPerLayer : nullptr;
+      r.dep_flags = dep_here ? flags + (size_t)(l - 1) * kFlagsPerLayer * kFlagStride : nullptr;
       r.dep_count = dep_here ? lp.layers[k - 1].wg_count : 0;
       r.Kin = pl.hoisted ? 0 : H;
       r.wg_begin = pl.wg_begin;
@@ -256,21 +272,25 @@ lstm_status_t lstm_fwd_ex(const lstm_desc_t* d, const void* x, const void* h0, c
       r.mt_per_wg = pl.mt_per_wg;
       r.staged = pl.staged;
       const size_t row_bytes = (size_t)H * ds;
-      r.vec_ok = (row_bytes % 16 == 0) && aligned16(r.R) && aligned16(r.Y) && (!r.W || aligned16(r.W)) &&
+      r.vec_ok = (row_bytes % 16 == 0) && aligned16(r.R) && aligned16(r.X) && (!r.W || aligned16(r.W)) &&
                  (!r.U || aligned16(r.U)) && (!r.h0 || aligned16(r.h0));
     }
     for (int k = lp.nlayers; k < kMaxLayersPerLaunch; ++k) rp.layer[k] = RecLayer();
+    // aligned fast path: whole chunks and 16-byte aligned rows in every layer of the launch
+    bool vec = (H % p.KC) == 0;
+    for (int k = 0; k < lp.nlayers; ++k) vec = vec && rp.layer[k].vec_ok;
     int per_cu = 0;
-    if (rec_prepare(bf16, lp.ks, lp.lds_bytes, &per_cu) != hipSuccess) return LSTM_ERR_HIP;
+    if (rec_prepare(bf16, lp.stream, vec, lp.mw, lp.nw, lp.lds_bytes, &per_cu) != hipSuccess) return LSTM_ERR_HIP;
     if ((long long)per_cu * dev.info.num_cus < lp.grid) return LSTM_ERR_UNSUPPORTED;  // not co-resident
     if (!before(LSTM_KERNEL_RECURRENT)) return LSTM_ERR_HIP;
-    if (launch_rec(bf16, lp.ks, rp, lp.lds_bytes, stream) != hipSuccess) return LSTM_ERR_HIP;
+    const bool plain = opts && opts->plain_launch;
+    if (launch_rec(bf16, lp.stream, vec, rp, lp.lds_bytes, plain, stream) != hipSuccess) return LSTM_ERR_HIP;
     if (!after()) return LSTM_ERR_HIP;
     return LSTM_OK;
   };
 
   // layer 0 input projection (+ zeroing of the error word and step counters)
-  st = gemm(0, x, I, true);
+  st = gemm(0, x, (long long)B * I, I, true);
   if (st != LSTM_OK) return st;
   if (p.regime == LSTM_REGIME_WAVEFRONT) {
     for (int r = 0; r < p.nrec; ++r) {
@@ -280,7 +300,7 @@ lstm_status_t lstm_fwd_ex(const lstm_desc_t* d, const void* x, const void* h0, c
   } else {
     for (int l = 0; l < L; ++l) {
       if (l > 0) {
-        st = gemm(l, out_l(l - 1), H, false);
+        st = gemm(l, xbuf(l - 1), (long long)slot, H, false);
         if (st != LSTM_OK) return st;
       }
       st = rec(p.rec[l]);

@@ -7,20 +7,23 @@ namespace lstm {
 
 constexpr int kMaxLayersPerLaunch = 16;  // layers one recurrent launch can run as a wavefront
 constexpr int kFlagsPerLayer = 1024;     // step-counter slots per layer (max workgroups per layer)
+constexpr int kFlagStride = 32;          // ints between two step counters: one 128-byte line each
 constexpr int kRecThreads = 256;         // 4 waves of 64
 constexpr int kGemmThreads = 256;
-constexpr int kGemmTileM = 128;          // rows (8 M-tiles) per input-GEMM workgroup
+constexpr int kGemmTileM = 256;          // rows (16 M-tiles) per input-GEMM workgroup
 constexpr int kGemmTileN = 128;          // columns (time x batch) per input-GEMM workgroup
+constexpr int kSlotAlign = 256;          // bytes: exchange slots never share a cache line
 
 // Input projection G = W_l U^T + b_l over all T*B columns (hoisted out of the recurrence).
 // Output layout [T][Mt][B][16] fp32: for step t, M-tile mt, batch b, the 16
 // gate-interleaved rows (unit 4*mt + rho/4, gate rho%4).
 struct GemmParams {
   const void* W;     // [4H][K] (caller layout, gate blocks)
-  const void* U;     // [T*B][K]
+  const void* U;     // input sequence: step t, batch b at U + t*u_slot + b*K (elements)
   const void* bias;  // [4H]
   float* G;          // [T][Mt][B][16]
   int* zero_ptr;     // if non-null: workgroup 0 zeroes zero_count ints first (flags, error word)
+  long long u_slot;  // elements between two steps of U
   int zero_count;
   int K, H, Mt, B, N;  // N = T*B
   int vec_ok_w, vec_ok_u;
@@ -32,33 +35,38 @@ struct RecLayer {
   const void* R;          // R_l [4H][H]
   const void* bias;       // b_l [4H] (fused input only; hoisted G already holds the bias)
   const float* G;         // hoisted pre-activations [T][Mt][B][16], or null
-  const void* U;          // fused input sequence [T][B][Kin] (output of the layer below), or null
-  void* Y;                // this layer's output sequence [T][B][H]
+  const void* U;          // exchange buffer of the layer below ([T] slots of [B][Kin]), or null
+  void* X;                // this layer's exchange buffer: [T] slots of [B][H]
+  void* Yout;             // caller's y [T][B][H] (top layer), or null
   const void* h0;         // [B][H] or null (zeros)
   const float* c0;        // [B][H] or null (zeros)
   void* hT;               // [B][H] or null
   float* cT;              // [B][H] or null
-  int* flags;             // per-workgroup step counters of this layer [wg_count]
+  int* flags;             // per-workgroup step counters of this layer, kFlagStride apart
   const int* dep_flags;   // step counters of the producer of U in this launch, or null
   int dep_count;          // workgroups of that producer
   int Kin;                // fused input width (0 when hoisted)
   int wg_begin, wg_count; // virtual workgroup ids owned by this layer
   int mt_per_wg;          // M-tiles per workgroup
   int staged;             // 1: weight rows kept in LDS for the whole sequence
-  int vec_ok;             // 16-byte loads allowed on W/R/U/Y/h0 rows
+  int vec_ok;             // 16-byte loads allowed on W/R/U/X/h0 rows
 };
 
 struct RecParams {
   RecLayer layer[kMaxLayersPerLaunch];
+  long long slot;         // elements between two steps of an exchange buffer
   int nlayers;
   int T, B, H, Mt, ncnt;  // ncnt = ceil(B/16) column tiles
-  int ntgm, ntgn;         // tile groups: ntgm*ntgn = 4/ksplit; group g -> (g%ntgm, g/ntgm)
-  int mw, nw;             // max tiles per wave in M and N (<= 4)
+  int ks;                 // waves splitting the K chunks of one tile (1, 2 or 4)
+  int ntgm, ntgn;         // tile groups: ntgm*ntgn = 4/ks; group g -> (g%ntgm, g/ntgm)
+  int mw, nw;             // tiles per wave in M and N (<= the kernel's MW, NW)
   int red_off;            // LDS byte offset of the cross-wave reduction area
   int grid;               // launched workgroups
   int xcd_remap;          // 1: map blockIdx round-robin over 8 XCDs to contiguous virtual ids
   int* err;               // device error word (0 ok, 1 step-wait timeout)
   long long timeout_ticks;  // per-wait limit in wall-clock ticks
+  long long* trace;       // optional per-step phase timestamps (see lstm_fwd_opts_t), or null
+  int trace_wgs, trace_stride;
 };
 
 }  // namespace lstm

@@ -36,28 +36,35 @@ int cdiv(int a, int b) { return (a + b - 1) / b; }
 // is the LDS the weight rows need (0 when streamed).  Returns false if nothing fits.
 bool choose_split(int mmax, int ncnt, int staged_bytes, int lds_limit, LaunchPlan* lp) {
   static const int ks_order[3] = {4, 2, 1};
-  for (int ks : ks_order) {
-    const int ntg = 4 / ks;
-    int best_ntgm = -1, best_cost = 1 << 30;
-    for (int ntgm = 1; ntgm <= ntg; ntgm *= 2) {
-      const int ntgn = ntg / ntgm;
+  // first pass: at most 8 tiles per wave (more does not fit in registers without spilling)
+  for (int pass = 0; pass < 2; ++pass) {
+    const int tile_cap = pass == 0 ? 8 : 16;
+    for (int ks : ks_order) {
+      const int ntg = 4 / ks;
+      int best_ntgm = -1, best_cost = 1 << 30;
+      for (int ntgm = 1; ntgm <= ntg; ntgm *= 2) {
+        const int ntgn = ntg / ntgm;
+        const int mw = cdiv(mmax, ntgm), nw = cdiv(ncnt, ntgn);
+        if (mw > 4 || nw > 4 || mw * nw > tile_cap) continue;
+        // re-read cost: tile groups that share column tiles each read those
+        // activations from global memory (x ntgm); tile groups that share M-tiles
+        // each read those weight rows, from LDS when staged (cheap) or from
+        // global memory when streamed (x ntgn)
+        const int w_act = 4, w_wgt = staged_bytes > 0 ? 1 : 4;
+        const int cost = w_act * ntgm * ncnt + w_wgt * ntgn * mmax;
+        if (cost < best_cost) best_cost = cost, best_ntgm = ntgm;
+      }
+      if (best_ntgm < 0) continue;
+      const int ntgm = best_ntgm, ntgn = ntg / ntgm;
       const int mw = cdiv(mmax, ntgm), nw = cdiv(ncnt, ntgn);
-      if (mw > 4 || nw > 4) continue;
-      // re-read cost proxy: each tile group re-reads the weights of its M-tiles and
-      // the activations of its column tiles
-      const int cost = ntgn * mmax + ntgm * ncnt;
-      if (cost < best_cost) best_cost = cost, best_ntgm = ntgm;
+      const int red = ks > 1 ? ntg * mw * nw * ks * 64 * 16 : 0;
+      const int red_off = (staged_bytes + 255) & ~255;
+      if (red_off + red + kLdsReserve > lds_limit) continue;
+      lp->ks = ks, lp->ntgm = ntgm, lp->ntgn = ntgn, lp->mw = mw, lp->nw = nw;
+      lp->red_off = red_off;
+      lp->lds_bytes = red_off + red;
+      return true;
     }
-    if (best_ntgm < 0) continue;
-    const int ntgm = best_ntgm, ntgn = ntg / ntgm;
-    const int mw = cdiv(mmax, ntgm), nw = cdiv(ncnt, ntgn);
-    const int red = ks > 1 ? ntg * mw * nw * ks * 64 * 16 : 0;
-    const int red_off = (staged_bytes + 255) & ~255;
-    if (red_off + red + kLdsReserve > lds_limit) continue;
-    lp->ks = ks, lp->ntgm = ntgm, lp->ntgn = ntgn, lp->mw = mw, lp->nw = nw;
-    lp->red_off = red_off;
-    lp->lds_bytes = red_off + red;
-    return true;
   }
   return false;
 }
@@ -78,8 +85,10 @@ bool plan_single(int layer, int Mt, int nch, int ncnt, const DeviceInfo& dev, La
   const int staged_bytes = m * nch * 64 * kFragBytes;
   if (choose_split(m, ncnt, staged_bytes, dev.lds_per_block, lp)) {
     L.staged = 1;
+    lp->stream = 0;
   } else if (choose_split(m, ncnt, 0, dev.lds_per_block, lp)) {
     L.staged = 0;
+    lp->stream = 1;
   } else {
     return false;
   }
@@ -134,6 +143,7 @@ bool plan_wavefront(int l0, int n, int Mt, int nch_h, int nch_in0, int ncnt, con
     staged_max = std::max(staged_max, mt[k] * nchl[k] * 64 * kFragBytes);
   }
   if (!choose_split(mmax, ncnt, staged_max, dev.lds_per_block, lp)) return false;
+  lp->stream = 0;
   lp->grid = round_grid(begin);
   for (int k = 0; k < n; ++k)
     if (lp->layers[k].wg_count > kFlagsPerLayer) return false;
@@ -189,17 +199,20 @@ int make_plan(const int32_t L, const int32_t I, const int32_t H, const int32_t B
   p.regime = wave ? kRegimeWavefront : kRegimeLayerwise;
   p.num_launches = p.nrec + p.ngemm;
 
-  // workspace: [error word | step counters L x kFlagsPerLayer | G (one layer) | layer outputs 0..L-2]
+  // workspace: [error word | step counters L x kFlagsPerLayer, one 128-byte line each |
+  //             G (one layer) | exchange buffers of all L layers, T slots each]
   size_t off = 0;
   p.err_off = off;
   off += 256;
   p.flags_off = off;
-  off += align256((size_t)L * kFlagsPerLayer * sizeof(int));
+  off += align256((size_t)L * kFlagsPerLayer * kFlagStride * sizeof(int));
   p.zero_ints = off / sizeof(int);
   p.G_off = off;
   off += align256((size_t)T * p.Mt * B * 16 * sizeof(float));
   p.hist_off = off;
-  off += align256((size_t)(L - 1) * T * B * H * p.dsize);
+  const size_t slot_bytes = ((size_t)B * H * p.dsize + kSlotAlign - 1) / kSlotAlign * kSlotAlign;
+  p.slot_elems = slot_bytes / p.dsize;
+  off += (size_t)L * T * slot_bytes;
   p.ws_bytes = off;
   return kStatusOk;
 }

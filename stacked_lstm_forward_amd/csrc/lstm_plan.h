@@ -26,6 +26,7 @@ struct LayerPlan {
 struct LaunchPlan {
   int nlayers = 0;
   LayerPlan layers[kMaxLayersPerLaunch];
+  int stream = 0;       // 1: weight rows streamed from global memory every step
   int ks = 4, ntgm = 1, ntgn = 1, mw = 1, nw = 1;
   int lds_bytes = 0, red_off = 0;
   int grid = 0;
@@ -43,6 +44,7 @@ struct Plan {
   int num_launches = 0;
   // workspace layout (bytes)
   size_t err_off = 0, flags_off = 0, G_off = 0, hist_off = 0, ws_bytes = 0;
+  size_t slot_elems = 0;  // elements between two steps of an exchange buffer
   size_t zero_ints = 0; // ints zeroed at the start (error word + all step counters)
 };
 

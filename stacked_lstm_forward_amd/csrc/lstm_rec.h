@@ -1,0 +1,393 @@
+// Persistent recurrent kernel of the stacked-LSTM forward pass (template
+// definitions; instantiated by lstm_rec_inst.hip once per dtype / weight source).
+#pragma once
+
+#include "lstm_common.h"
+#include "lstm_params.h"
+
+namespace lstm {
+
+// ----------------------------------------------------------------------------
+// Step ordering
+// ----------------------------------------------------------------------------
+// Protocol between workgroups (no cache-wide fences):
+//  * a layer's h_t is written to slot t of its exchange buffer with agent-scope
+//    atomic stores, which write through to the device-wide coherence point;
+//    every slot is written once per launch and starts on its own 256-byte
+//    boundary, so no cache can hold a copy of it from before it was written
+//    (kernel start drops stale lines from previous launches);
+//  * the writer waits for those stores to complete (s_waitcnt 0), then one
+//    thread bumps the workgroup's step counter (agent-scope atomic store);
+//  * a reader polls the counters it depends on (one 128-byte line each, all
+//    polled with one batch of loads), then reads the slot with ordinary loads.
+// Every wait is bounded: past `timeout` wall-clock ticks the error word is set
+// and all workgroups leave the kernel.
+
+// Executed by one whole wave: true once every counter of flags[0..count) is
+// >= target.  False if another workgroup reported an error or the wait timed out.
+// The loads of one poll are unconditional (indices clamped) so they are all in
+// flight together.
+__device__ bool wait_counts(const int* flags, int count, int target, int* err, long long timeout) {
+  const int lane = threadIdx.x & 63;
+  const long long start = wall_clock64();
+  while (true) {
+    int ok = 1;
+    for (int base = 0; base < count; base += 256) {
+      int v[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int i = min(base + lane + 64 * k, count - 1);
+        v[k] = __hip_atomic_load(flags + (long)i * kFlagStride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) ok &= (v[k] >= target) ? 1 : 0;
+    }
+    if (__all(ok)) return true;
+    if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return false;
+    if (wall_clock64() - start > timeout) {
+      if (lane == 0) __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store_coherent(typename Dt<BF16>::T* p, typename Dt<BF16>::T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ----------------------------------------------------------------------------
+// Persistent recurrence (optionally several layers as a wavefront)
+// ----------------------------------------------------------------------------
+// Waves: wave w -> K-group w % ks, tile group w / ks.  The ks waves of a tile
+// group split the K chunks of the same output tiles and combine them through
+// LDS; tile group g covers M-tiles g%ntgm (+ntgm ...) and column tiles
+// g/ntgm (+ntgn ...).  MW x NW is the most tiles one wave holds; STREAM means
+// the weight rows are read from global memory every step instead of LDS.
+//
+// VEC (the fast path): every K range is a whole number of chunks and every row
+// starts on a 16-byte boundary, so each fragment is two unconditional 16-byte
+// loads; rows past the end are clamped to a valid row (their products are
+// never used).  With no branch around a load, the compiler's wait counting
+// stays exact and a wave keeps PD chunks of loads in flight ahead of its
+// MFMAs.  !VEC handles ragged sizes with per-element loads (slow, correct).
+template <int MW, int NW, bool STREAM>
+struct RecShape {
+  static constexpr int kRegsPerChunk = 8 * NW + (STREAM ? 8 * MW : 0);
+  static constexpr int PD = (128 / kRegsPerChunk) < 2 ? 2 : ((128 / kRegsPerChunk) > 8 ? 8 : 128 / kRegsPerChunk);
+};
+
+template <bool BF16, int MW, int NW, bool STREAM, bool VEC>
+__global__ void __launch_bounds__(kRecThreads) lstm_rec_kernel(const RecParams P) {
+  typedef typename Dt<BF16>::T T;
+  constexpr int KC = Dt<BF16>::KC;
+  constexpr int FQ = KC / 4;
+  constexpr int PD = RecShape<MW, NW, STREAM>::PD;
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int s_ok;
+
+  // The layer table is read in place from the kernel-argument segment with a
+  // wave-uniform index (scalar loads); copying one entry out of the by-value
+  // array with a runtime index would spill.
+  typedef const __attribute__((address_space(4))) RecParams KP;
+  KP* pp = (KP*)(__builtin_amdgcn_kernarg_segment_ptr());
+  const int bid = blockIdx.x;
+  const int v = P.xcd_remap ? ((bid & 7) * (P.grid >> 3) + (bid >> 3)) : bid;
+  int li = -1;
+  for (int i = 0; i < P.nlayers; ++i)
+    if (v >= pp->layer[i].wg_begin && v < pp->layer[i].wg_begin + pp->layer[i].wg_count) li = i;
+  if (li < 0) return;
+  li = __builtin_amdgcn_readfirstlane(li);
+#define LY(f) (pp->layer[li].f)
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave index as a provably wave-uniform value: everything derived from it
+  // (K-group, tile group, chunk counts, tile validity) lives in scalar
+  // registers and its branches are scalar, so no load sits behind a divergent branch
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ks = P.ks;
+  const int kg = wave % ks, tg = wave / ks;
+  const int gm = tg % P.ntgm, gn = tg / P.ntgm;
+  const int wl = v - LY(wg_begin);
+  const int mt0 = wl * LY(mt_per_wg);
+  const int mcnt = min(LY(mt_per_wg), P.Mt - mt0);
+  const int H = P.H, B = P.B, T_ = P.T, Kin = LY(Kin);
+  const long slot = P.slot;
+  const int nch_u = (Kin + KC - 1) / KC;
+  const int nch_h = (H + KC - 1) / KC;
+  const int nch = nch_u + nch_h;
+  const bool vec = LY(vec_ok);
+  const int q = lane >> 4;
+  Frag* As = reinterpret_cast<Frag*>(smem);
+
+  // ---- keep this workgroup's weight rows on chip for the whole sequence
+  if (!STREAM && LY(staged)) {
+    const int total = mcnt * nch * 64;
+    for (int f = tid; f < total; f += kRecThreads) {
+      const int ln = f & 63;
+      const int c = (f >> 6) % nch;
+      const int m = (f >> 6) / nch;
+      const long row = tile_row(mt0 + m, ln & 15, H);
+      const int qq = ln >> 4;
+      Frag fr = zero_frag();
+      if (row >= 0) {
+        if (c < nch_u)
+          fr = load_frag<BF16>(LY(W), Kin, row, c * KC + qq * FQ, Kin, vec);
+        else
+          fr = load_frag<BF16>(LY(R), H, row, (c - nch_u) * KC + qq * FQ, H, vec);
+      }
+      As[f] = fr;
+    }
+    __syncthreads();
+  }
+
+  // ---- per-wave tile bookkeeping
+  bool mval[MW], nval[NW];
+  int mloc[MW];
+  long arow[MW];  // caller weight row this lane loads for M-tile i (streamed weights; clamped)
+  int unit[MW], bcol[NW];
+  long boff[NW];  // element offset of this lane's activation row (clamped to a valid row)
+#pragma unroll
+  for (int i = 0; i < MW; ++i) {
+    mloc[i] = gm + i * P.ntgm;
+    mval[i] = i < P.mw && mloc[i] < mcnt;
+    const long r = mval[i] ? tile_row(mt0 + mloc[i], lane & 15, H) : -1;
+    arow[i] = VEC ? (r >= 0 ? r : 0) : r;
+    unit[i] = 4 * (mt0 + mloc[i]) + q;
+  }
+#pragma unroll
+  for (int j = 0; j < NW; ++j) {
+    const int nloc = gn + j * P.ntgn;
+    nval[j] = j < P.nw && nloc < P.ncnt;
+    bcol[j] = 16 * nloc + (lane & 15);
+    boff[j] = (long)min(bcol[j], B - 1) * H;  // every activation row has H elements (I_l = H for l >= 1)
+  }
+  auto fin = [&](int i, int j) { return ((i * P.nw + j) % ks) == kg; };
+  auto live = [&](int i, int j) { return mval[i] && nval[j] && fin(i, j) && unit[i] < H && bcol[j] < B; };
+
+  // cell state (fp32, registers) and bias of fused-input layers
+  float creg[MW][NW];
+  f32x4 breg[MW];
+  const T* bias = reinterpret_cast<const T*>(LY(bias));
+#pragma unroll
+  for (int i = 0; i < MW; ++i) {
+    breg[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (Kin && mval[i] && unit[i] < H) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) breg[i][k] = to_float(bias[k * H + unit[i]]);
+    }
+#pragma unroll
+    for (int j = 0; j < NW; ++j) {
+      creg[i][j] = 0.f;
+      if (LY(c0) && live(i, j)) creg[i][j] = LY(c0)[(long)bcol[j] * H + unit[i]];
+    }
+  }
+
+  // optional phase trace of this workgroup (thread 0 writes wall-clock stamps)
+  long long* trc = nullptr;
+  if (P.trace && v % P.trace_stride == 0 && v / P.trace_stride < P.trace_wgs)
+    trc = P.trace + (long)(v / P.trace_stride) * T_ * 8;
+  auto stamp = [&](int t, int k) {
+    if (trc && tid == 0) trc[t * 8 + k] = wall_clock64();
+  };
+
+  const T* Wp = reinterpret_cast<const T*>(LY(W));
+  const T* Rp = reinterpret_cast<const T*>(LY(R));
+  T* Xp = reinterpret_cast<T*>(LY(X));
+  const T* Up = reinterpret_cast<const T*>(LY(U));
+  const float* Gp = LY(G);
+  // G offsets of this lane's tiles (clamped so every load is valid)
+  long goff[MW][NW];
+#pragma unroll
+  for (int i = 0; i < MW; ++i)
+#pragma unroll
+    for (int j = 0; j < NW; ++j)
+      goff[i][j] = ((long)min(mt0 + mloc[i], P.Mt - 1) * B + min(bcol[j], B - 1)) * 16 + 4 * q;
+
+  for (int t = 0; t < T_; ++t) {
+    stamp(t, 0);
+    // ---- hoisted pre-activations of this wave's tiles (do not depend on the wait)
+    f32x4 gq[MW][NW];
+    if (Gp) {
+      const float* gt = Gp + (long)t * P.Mt * B * 16;
+#pragma unroll
+      for (int i = 0; i < MW; ++i)
+#pragma unroll
+        for (int j = 0; j < NW; ++j) gq[i][j] = *reinterpret_cast<const f32x4*>(gt + goff[i][j]);
+    }
+
+    // ---- wait for h^l_{t-1} (own layer) and h^{l-1}_t (producer in this launch)
+    const bool need_own = t > 0;
+    const bool need_dep = LY(dep_flags) != nullptr;
+    if (need_own || need_dep) {
+      if (wave == 0) {
+        bool ok = true;
+        if (need_own) ok = wait_counts(LY(flags), LY(wg_count), t, P.err, P.timeout_ticks);
+        if (ok && need_dep) ok = wait_counts(LY(dep_flags), LY(dep_count), t + 1, P.err, P.timeout_ticks);
+        if (lane == 0) s_ok = ok ? 1 : 0;
+      }
+      __syncthreads();
+      if (!s_ok) return;
+    }
+    stamp(t, 1);
+
+    // ---- grouped products: [W_l | R_l] (rows of this workgroup) x [u_t ; h_{t-1}]
+    f32x4 acc[MW][NW];
+#pragma unroll
+    for (int i = 0; i < MW; ++i)
+#pragma unroll
+      for (int j = 0; j < NW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const T* hsrc = t > 0 ? Xp + (long)(t - 1) * slot : reinterpret_cast<const T*>(LY(h0));
+    const T* usrc = Kin ? Up + (long)t * slot : nullptr;
+    const int c_end = hsrc ? nch : nch_u;
+    const int n_my = c_end > kg ? (c_end - kg + ks - 1) / ks : 0;
+
+    Frag rb[PD][NW];
+    Frag ra[STREAM ? PD : 1][MW];
+    auto issue = [&](Frag (&b)[NW], Frag (&a)[MW], int ci) {
+      const int c = kg + ci * ks;
+      const bool is_u = c < nch_u;
+      const int Kseg = is_u ? Kin : H;
+      const int kk = (is_u ? c : c - nch_u) * KC + q * FQ;
+      const T* bsrc = is_u ? usrc : hsrc;
+      const T* asrc = is_u ? Wp : Rp;
+      if (VEC) {
+#pragma unroll
+        for (int j = 0; j < NW; ++j) b[j] = load_frag_vec(bsrc + boff[j] + kk);
+        if (STREAM) {
+#pragma unroll
+          for (int i = 0; i < MW; ++i) a[i] = load_frag_vec(asrc + arow[i] * Kseg + kk);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NW; ++j)
+          if (nval[j]) b[j] = bcol[j] < B ? load_frag_off<BF16>(bsrc, (long)bcol[j] * Kseg, kk, Kseg, false) : zero_frag();
+        if (STREAM) {
+#pragma unroll
+          for (int i = 0; i < MW; ++i)
+            if (mval[i]) a[i] = arow[i] >= 0 ? load_frag<BF16>(asrc, Kseg, arow[i], kk, Kseg, false) : zero_frag();
+        }
+      }
+    };
+    // Weight fragments from LDS are read one chunk ahead (acur holds chunk ci's
+    // when compute(s, ci) starts), so their latency hides behind the MFMAs.
+    Frag acur[MW];
+    auto lds_a = [&](int ci) {
+      const int c = kg + min(ci, n_my - 1) * ks;
+#pragma unroll
+      for (int i = 0; i < MW; ++i)
+        if (mval[i]) acur[i] = As[(mloc[i] * nch + c) * 64 + lane];
+    };
+    auto compute = [&](int s, int ci) {
+      Frag a[MW];
+#pragma unroll
+      for (int i = 0; i < MW; ++i) {
+        if (STREAM)
+          a[i] = ra[STREAM ? s : 0][i];
+        else
+          a[i] = acur[i];
+      }
+      if (!STREAM) lds_a(ci + 1);
+#pragma unroll
+      for (int i = 0; i < MW; ++i)
+#pragma unroll
+        for (int j = 0; j < NW; ++j)
+          if (mval[i] && nval[j]) mfma_frag<BF16>(acc[i][j], a[i], rb[s][j]);
+    };
+    if (n_my > 0 && n_my <= PD) {
+      // burst: every chunk of this wave in flight at once
+#pragma unroll
+      for (int s = 0; s < PD; ++s) issue(rb[s], ra[STREAM ? s : 0], min(s, n_my - 1));
+      if (!STREAM) lds_a(0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int s = 0; s < PD; ++s)
+        if (s < n_my) compute(s, s);
+    } else if (n_my > PD) {
+      // ring: every issue is unconditional (chunk index clamped to the last one)
+      // and the loop runs to a multiple of PD, so the load stream has no
+      // branches; only the MFMAs of the padded tail are skipped.  The scheduling
+      // barriers keep each refill where it is written instead of next to its use.
+      const int n_pad = (n_my + PD - 1) / PD * PD;
+#pragma unroll
+      for (int s = 0; s < PD; ++s) issue(rb[s], ra[STREAM ? s : 0], s);
+      if (!STREAM) lds_a(0);
+      __builtin_amdgcn_sched_barrier(0);
+      for (int i0 = 0; i0 < n_pad; i0 += PD) {
+#pragma unroll
+        for (int s = 0; s < PD; ++s) {
+          const int ci = i0 + s;
+          if (ci < n_my) compute(s, ci);
+          issue(rb[s], ra[STREAM ? s : 0], min(ci + PD, n_my - 1));
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+    stamp(t, 2);
+
+    // ---- combine the K-split partial sums
+    if (ks > 1) {
+      f32x4* red = reinterpret_cast<f32x4*>(smem + P.red_off);
+      const int tpg = P.mw * P.nw;
+#pragma unroll
+      for (int i = 0; i < MW; ++i)
+#pragma unroll
+        for (int j = 0; j < NW; ++j) {
+          if (!(mval[i] && nval[j]) || fin(i, j)) continue;
+          const int e = i * P.nw + j;
+          red[((tg * tpg + e) * ks + kg) * 64 + lane] = acc[i][j];
+        }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < MW; ++i)
+#pragma unroll
+        for (int j = 0; j < NW; ++j) {
+          if (!(mval[i] && nval[j]) || !fin(i, j)) continue;
+          const int e = i * P.nw + j;
+          for (int k2 = 0; k2 < ks; ++k2)
+            if (k2 != kg) acc[i][j] += red[((tg * tpg + e) * ks + k2) * 64 + lane];
+        }
+    }
+    stamp(t, 3);
+
+    // ---- gates, cell update, outputs
+    T* xout = Xp + (long)t * slot;
+    T* yout = LY(Yout) ? reinterpret_cast<T*>(LY(Yout)) + (long)t * B * H : nullptr;
+    const bool last = (t == T_ - 1);
+#pragma unroll
+    for (int i = 0; i < MW; ++i)
+#pragma unroll
+      for (int j = 0; j < NW; ++j) {
+        if (!live(i, j)) continue;
+        const f32x4 p = acc[i][j] + (Gp ? gq[i][j] : breg[i]);
+        const float ig = sigmoid_f(p[0]);
+        const float fg = sigmoid_f(p[1]);
+        const float gg = tanh_f(p[2]);
+        const float og = sigmoid_f(p[3]);
+        const float cn = fg * creg[i][j] + ig * gg;
+        creg[i][j] = cn;
+        const T hv = from_float<BF16>(og * tanh_f(cn));
+        const long o = (long)bcol[j] * H + unit[i];
+        store_coherent<BF16>(xout + o, hv);
+        if (yout) yout[o] = hv;
+        if (last) {
+          if (LY(hT)) reinterpret_cast<T*>(LY(hT))[o] = hv;
+          if (LY(cT)) LY(cT)[o] = cn;
+        }
+      }
+    stamp(t, 4);
+
+    // ---- publish step t: stores complete, then the step counter
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0)
+      __hip_atomic_store(LY(flags) + (long)wl * kFlagStride, t + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    stamp(t, 5);
+  }
+#undef LY
+}
+
+}  // namespace lstm
