@@ -114,7 +114,9 @@ typedef struct {
                                  of the first recurrent launch, for workgroups v = 0, s, 2s, ...
                                  (s = trace_stride): trace[((v/s)*T + t)*8 + k], k = 0 step start,
                                  1 dependencies met, 2 products done, 3 partial sums combined,
-                                 4 gates/stores issued, 5 step published; trace_wgs*T*8 entries    */
+                                 4 gates/stores issued, 5 step published (100 MHz wall clock);
+                                 6 and 7: shader-clock counter at 0 and at 2, so (7-6)/(2-0)
+                                 gives the core clock; trace_wgs*T*8 entries                       */
   int32_t trace_wgs;          /* number of traced workgroups (0: no trace)                        */
   int32_t trace_stride;       /* virtual workgroup stride between traced workgroups (>= 1)         */
   int32_t plain_launch;       /* 1: launch the persistent kernel with an ordinary launch instead of a

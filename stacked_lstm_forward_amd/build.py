@@ -15,16 +15,11 @@ LIBDIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIBDIR, "liblstm_fwd.so")
 ARCH = "gfx950"
 # (source, extra defines): the recurrent kernel is instantiated once per
-# (dtype, weight source) so the four variants compile in parallel
-UNITS = [
-    ("lstm_kernels.hip", []),
-    ("lstm_rec_inst.hip", ["-DLSTM_INST_BF16=0", "-DLSTM_INST_STREAM=0"]),
-    ("lstm_rec_inst.hip", ["-DLSTM_INST_BF16=0", "-DLSTM_INST_STREAM=1"]),
-    ("lstm_rec_inst.hip", ["-DLSTM_INST_BF16=1", "-DLSTM_INST_STREAM=0"]),
-    ("lstm_rec_inst.hip", ["-DLSTM_INST_BF16=1", "-DLSTM_INST_STREAM=1"]),
-    ("lstm_fwd.cpp", []),
-    ("lstm_plan.cpp", []),
-]
+# (dtype, weight source, waves per workgroup) so the variants compile in parallel
+UNITS = [("lstm_kernels.hip", [])] + [
+    ("lstm_rec_inst.hip", [f"-DLSTM_INST_BF16={bf}", f"-DLSTM_INST_STREAM={st}", f"-DLSTM_INST_NWV={nwv}"])
+    for bf in (0, 1) for st in (0, 1) for nwv in (4, 8)
+] + [("lstm_fwd.cpp", []), ("lstm_plan.cpp", [])]
 BUILD_DIR = os.path.join(HERE, "_build")
 
 

@@ -17,8 +17,9 @@
 
 namespace lstm {
 hipError_t launch_input_gemm(bool bf16, const GemmParams& p, hipStream_t s);
-hipError_t rec_prepare(bool bf16, bool stream, bool vec, int mw, int nw, int lds_bytes, int* max_blocks_per_cu);
-hipError_t launch_rec(bool bf16, bool stream, bool vec, const RecParams& p, int lds_bytes, bool plain, hipStream_t s);
+hipError_t rec_prepare(bool bf16, bool stream, bool vec, int nwv, int mw, int nw, int lds_bytes, int* max_blocks_per_cu);
+hipError_t launch_rec(bool bf16, bool stream, bool vec, int nwv, const RecParams& p, int lds_bytes, bool plain,
+                      hipStream_t s);
 }  // namespace lstm
 
 using namespace lstm;
@@ -104,7 +105,7 @@ lstm_status_t lstm_fwd_plan(const lstm_desc_t* d, int32_t force_regime, int32_t 
   out->regime = p.regime;
   out->num_launches = p.num_launches;
   out->grid = p.rec[0].grid;
-  out->block = kRecThreads;
+  out->block = 64 * p.rec[0].nwaves;
   out->lds_bytes = p.rec[0].lds_bytes;
   out->ksplit = p.rec[0].ks;
   int on_chip = 1;
@@ -280,11 +281,12 @@ lstm_status_t lstm_fwd_ex(const lstm_desc_t* d, const void* x, const void* h0, c
     bool vec = (H % p.KC) == 0;
     for (int k = 0; k < lp.nlayers; ++k) vec = vec && rp.layer[k].vec_ok;
     int per_cu = 0;
-    if (rec_prepare(bf16, lp.stream, vec, lp.mw, lp.nw, lp.lds_bytes, &per_cu) != hipSuccess) return LSTM_ERR_HIP;
+    if (rec_prepare(bf16, lp.stream, vec, lp.nwaves, lp.mw, lp.nw, lp.lds_bytes, &per_cu) != hipSuccess)
+      return LSTM_ERR_HIP;
     if ((long long)per_cu * dev.info.num_cus < lp.grid) return LSTM_ERR_UNSUPPORTED;  // not co-resident
     if (!before(LSTM_KERNEL_RECURRENT)) return LSTM_ERR_HIP;
     const bool plain = opts && opts->plain_launch;
-    if (launch_rec(bf16, lp.stream, vec, rp, lp.lds_bytes, plain, stream) != hipSuccess) return LSTM_ERR_HIP;
+    if (launch_rec(bf16, lp.stream, vec, lp.nwaves, rp, lp.lds_bytes, plain, stream) != hipSuccess) return LSTM_ERR_HIP;
     if (!after()) return LSTM_ERR_HIP;
     return LSTM_OK;
   };

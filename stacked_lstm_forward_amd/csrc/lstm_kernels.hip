@@ -170,15 +170,19 @@ __global__ void __launch_bounds__(kGemmThreads) lstm_input_gemm(const GemmParams
 // touches them).  The recurrent kernel's instantiations live in
 // lstm_rec_inst.hip, compiled once per (dtype, weight source).
 // ----------------------------------------------------------------------------
-const void* rec_kernel_ptr_f32_lds(int mw, int nw, bool vec);
-const void* rec_kernel_ptr_f32_stream(int mw, int nw, bool vec);
-const void* rec_kernel_ptr_bf16_lds(int mw, int nw, bool vec);
-const void* rec_kernel_ptr_bf16_stream(int mw, int nw, bool vec);
+#define LSTM_DECL(d, s, w) const void* rec_kernel_ptr_##d##_##s##_w##w(int mw, int nw, bool vec);
+LSTM_DECL(f32, lds, 4) LSTM_DECL(f32, stream, 4) LSTM_DECL(bf16, lds, 4) LSTM_DECL(bf16, stream, 4)
+LSTM_DECL(f32, lds, 8) LSTM_DECL(f32, stream, 8) LSTM_DECL(bf16, lds, 8) LSTM_DECL(bf16, stream, 8)
+#undef LSTM_DECL
 
 namespace {
-const void* rec_kernel_fn(bool bf16, bool stream, bool vec, int mw, int nw) {
-  if (bf16) return stream ? rec_kernel_ptr_bf16_stream(mw, nw, vec) : rec_kernel_ptr_bf16_lds(mw, nw, vec);
-  return stream ? rec_kernel_ptr_f32_stream(mw, nw, vec) : rec_kernel_ptr_f32_lds(mw, nw, vec);
+const void* rec_kernel_fn(bool bf16, bool stream, bool vec, int nwv, int mw, int nw) {
+  if (nwv == 8) {
+    if (bf16) return stream ? rec_kernel_ptr_bf16_stream_w8(mw, nw, vec) : rec_kernel_ptr_bf16_lds_w8(mw, nw, vec);
+    return stream ? rec_kernel_ptr_f32_stream_w8(mw, nw, vec) : rec_kernel_ptr_f32_lds_w8(mw, nw, vec);
+  }
+  if (bf16) return stream ? rec_kernel_ptr_bf16_stream_w4(mw, nw, vec) : rec_kernel_ptr_bf16_lds_w4(mw, nw, vec);
+  return stream ? rec_kernel_ptr_f32_stream_w4(mw, nw, vec) : rec_kernel_ptr_f32_lds_w4(mw, nw, vec);
 }
 }  // namespace
 
@@ -200,20 +204,21 @@ hipError_t launch_input_gemm(bool bf16, const GemmParams& p, hipStream_t s) {
   return hipLaunchKernel(fn, grid, dim3(kGemmThreads), args, lds, s);
 }
 
-hipError_t rec_prepare(bool bf16, bool stream, bool vec, int mw, int nw, int lds_bytes, int* max_blocks_per_cu) {
-  const void* fn = rec_kernel_fn(bf16, stream, vec, mw, nw);
+hipError_t rec_prepare(bool bf16, bool stream, bool vec, int nwv, int mw, int nw, int lds_bytes, int* max_blocks_per_cu) {
+  const void* fn = rec_kernel_fn(bf16, stream, vec, nwv, mw, nw);
   if (!fn) return hipErrorInvalidValue;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
   if (e != hipSuccess) return e;
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(max_blocks_per_cu, fn, kRecThreads, lds_bytes);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(max_blocks_per_cu, fn, 64 * nwv, lds_bytes);
 }
 
-hipError_t launch_rec(bool bf16, bool stream, bool vec, const RecParams& p, int lds_bytes, bool plain, hipStream_t s) {
-  const void* fn = rec_kernel_fn(bf16, stream, vec, p.mw, p.nw);
+hipError_t launch_rec(bool bf16, bool stream, bool vec, int nwv, const RecParams& p, int lds_bytes, bool plain,
+                      hipStream_t s) {
+  const void* fn = rec_kernel_fn(bf16, stream, vec, nwv, p.mw, p.nw);
   if (!fn) return hipErrorInvalidValue;
   void* args[] = {const_cast<RecParams*>(&p)};
-  if (plain) return hipLaunchKernel(fn, dim3(p.grid), dim3(kRecThreads), args, (unsigned)lds_bytes, s);
-  return hipLaunchCooperativeKernel(fn, dim3(p.grid), dim3(kRecThreads), args, (unsigned)lds_bytes, s);
+  if (plain) return hipLaunchKernel(fn, dim3(p.grid), dim3(64 * nwv), args, (unsigned)lds_bytes, s);
+  return hipLaunchCooperativeKernel(fn, dim3(p.grid), dim3(64 * nwv), args, (unsigned)lds_bytes, s);
 }
 
 }  // namespace lstm

@@ -8,7 +8,6 @@ namespace lstm {
 constexpr int kMaxLayersPerLaunch = 16;  // layers one recurrent launch can run as a wavefront
 constexpr int kFlagsPerLayer = 1024;     // step-counter slots per layer (max workgroups per layer)
 constexpr int kFlagStride = 32;          // ints between two step counters: one 128-byte line each
-constexpr int kRecThreads = 256;         // 4 waves of 64
 constexpr int kGemmThreads = 256;
 constexpr int kGemmTileM = 256;          // rows (16 M-tiles) per input-GEMM workgroup
 constexpr int kGemmTileN = 128;          // columns (time x batch) per input-GEMM workgroup
@@ -57,8 +56,8 @@ struct RecParams {
   long long slot;         // elements between two steps of an exchange buffer
   int nlayers;
   int T, B, H, Mt, ncnt;  // ncnt = ceil(B/16) column tiles
-  int ks;                 // waves splitting the K chunks of one tile (1, 2 or 4)
-  int ntgm, ntgn;         // tile groups: ntgm*ntgn = 4/ks; group g -> (g%ntgm, g/ntgm)
+  int ks;                 // waves splitting the K chunks of one tile (1, 2, 4 or 8)
+  int ntgm, ntgn;         // tile groups: ntgm*ntgn = waves/ks; group g -> (g%ntgm, g/ntgm)
   int mw, nw;             // tiles per wave in M and N (<= the kernel's MW, NW)
   int red_off;            // LDS byte offset of the cross-wave reduction area
   int grid;               // launched workgroups

@@ -34,18 +34,23 @@ int cdiv(int a, int b) { return (a + b - 1) / b; }
 // Choose the K split and the tile groups of a launch whose largest workgroup
 // owns `mmax` M-tiles; fills ks/ntgm/ntgn/mw/nw/red_off/lds_bytes.  `staged_bytes`
 // is the LDS the weight rows need (0 when streamed).  Returns false if nothing fits.
-bool choose_split(int mmax, int ncnt, int staged_bytes, int lds_limit, LaunchPlan* lp) {
-  static const int ks_order[3] = {4, 2, 1};
-  // first pass: at most 8 tiles per wave (more does not fit in registers without spilling)
-  for (int pass = 0; pass < 2; ++pass) {
-    const int tile_cap = pass == 0 ? 8 : 16;
+bool choose_split(int mmax, int ncnt, int staged_bytes, int lds_limit, int nwaves, LaunchPlan* lp) {
+  static const int ks_order[4] = {8, 4, 2, 1};
+  // prefer at most 4 tiles per wave, fall back to 8, then 16; with two waves
+  // per SIMD a wave has 256 registers and larger tile sets spill, so 8-wave
+  // workgroups take 4 at most
+  const int npass = nwaves == 8 ? 1 : 3;
+  for (int pass = 0; pass < npass; ++pass) {
+    const int tile_cap = pass == 0 ? 4 : (pass == 1 ? 8 : 16);
     for (int ks : ks_order) {
-      const int ntg = 4 / ks;
+      if (ks > nwaves) continue;
+      const int ntg = nwaves / ks;
       int best_ntgm = -1, best_cost = 1 << 30;
       for (int ntgm = 1; ntgm <= ntg; ntgm *= 2) {
         const int ntgn = ntg / ntgm;
         const int mw = cdiv(mmax, ntgm), nw = cdiv(ncnt, ntgn);
         if (mw > 4 || nw > 4 || mw * nw > tile_cap) continue;
+        if (ntgm > mmax || ntgn > ncnt) continue;  // a tile group with nothing to do
         // re-read cost: tile groups that share column tiles each read those
         // activations from global memory (x ntgm); tile groups that share M-tiles
         // each read those weight rows, from LDS when staged (cheap) or from
@@ -57,9 +62,11 @@ bool choose_split(int mmax, int ncnt, int staged_bytes, int lds_limit, LaunchPla
       if (best_ntgm < 0) continue;
       const int ntgm = best_ntgm, ntgn = ntg / ntgm;
       const int mw = cdiv(mmax, ntgm), nw = cdiv(ncnt, ntgn);
-      const int red = ks > 1 ? ntg * mw * nw * ks * 64 * 16 : 0;
+      // one 1 KiB partial per (tile, non-finalising K-group)
+      const int red = ks > 1 ? ntg * mw * nw * (ks - 1) * 64 * 16 : 0;
       const int red_off = (staged_bytes + 255) & ~255;
       if (red_off + red + kLdsReserve > lds_limit) continue;
+      lp->nwaves = nwaves;
       lp->ks = ks, lp->ntgm = ntgm, lp->ntgn = ntgn, lp->mw = mw, lp->nw = nw;
       lp->red_off = red_off;
       lp->lds_bytes = red_off + red;
@@ -83,10 +90,11 @@ bool plan_single(int layer, int Mt, int nch, int ncnt, const DeviceInfo& dev, La
   L.wg_begin = 0, L.wg_count = wgs, L.mt_per_wg = m;
   lp->nlayers = 1;
   const int staged_bytes = m * nch * 64 * kFragBytes;
-  if (choose_split(m, ncnt, staged_bytes, dev.lds_per_block, lp)) {
+  // one wave per SIMD: a single layer's waves are not limited by a layer below
+  if (choose_split(m, ncnt, staged_bytes, dev.lds_per_block, 4, lp)) {
     L.staged = 1;
     lp->stream = 0;
-  } else if (choose_split(m, ncnt, 0, dev.lds_per_block, lp)) {
+  } else if (choose_split(m, ncnt, 0, dev.lds_per_block, 4, lp)) {
     L.staged = 0;
     lp->stream = 1;
   } else {
@@ -142,7 +150,10 @@ bool plan_wavefront(int l0, int n, int Mt, int nch_h, int nch_in0, int ncnt, con
     mmax = std::max(mmax, mt[k]);
     staged_max = std::max(staged_max, mt[k] * nchl[k] * 64 * kFragBytes);
   }
-  if (!choose_split(mmax, ncnt, staged_max, dev.lds_per_block, lp)) return false;
+  // two waves per SIMD: a wave waiting on one dependency leaves the SIMD to its partner
+  if (!choose_split(mmax, ncnt, staged_max, dev.lds_per_block, 8, lp) &&
+      !choose_split(mmax, ncnt, staged_max, dev.lds_per_block, 4, lp))
+    return false;
   lp->stream = 0;
   lp->grid = round_grid(begin);
   for (int k = 0; k < n; ++k)

@@ -27,6 +27,7 @@ struct LaunchPlan {
   int nlayers = 0;
   LayerPlan layers[kMaxLayersPerLaunch];
   int stream = 0;       // 1: weight rows streamed from global memory every step
+  int nwaves = 4;       // waves per workgroup (4: one per SIMD, 8: two per SIMD)
   int ks = 4, ntgm = 1, ntgn = 1, mw = 1, nw = 1;
   int lds_bytes = 0, red_off = 0;
   int grid = 0;

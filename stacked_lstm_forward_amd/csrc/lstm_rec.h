@@ -23,24 +23,38 @@ namespace lstm {
 // Every wait is bounded: past `timeout` wall-clock ticks the error word is set
 // and all workgroups leave the kernel.
 
-// Executed by one whole wave: true once every counter of flags[0..count) is
-// >= target.  False if another workgroup reported an error or the wait timed out.
-// The loads of one poll are unconditional (indices clamped) so they are all in
-// flight together.
-__device__ bool wait_counts(const int* flags, int count, int target, int* err, long long timeout) {
+// One poll of flags[0..min(count, 256)) by one whole wave: lane i loads
+// counters i, i+64, i+128, i+192 (indices clamped, so all loads are
+// unconditional and in flight together).
+__device__ __forceinline__ void poll_issue(const int* flags, int count, int (&v)[4]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = min(lane + 64 * k, count - 1);
+    v[k] = __hip_atomic_load(flags + (long)i * kFlagStride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Executed by one whole wave: true once every counter of a[0..na) is >= ta
+// and every counter of b[0..nb) is >= tb (b may be null).  Both sets are
+// polled with one batch of loads, so a satisfied wait costs one round trip.
+// False if another workgroup reported an error or the wait timed out.
+__device__ bool wait_counts(const int* a, int na, int ta, const int* b, int nb, int tb, int* err,
+                            long long timeout) {
   const int lane = threadIdx.x & 63;
   const long long start = wall_clock64();
   while (true) {
     int ok = 1;
-    for (int base = 0; base < count; base += 256) {
-      int v[4];
+    const int n = max(na, b ? nb : 0);
+    for (int base = 0; base < n; base += 256) {
+      int va[4], vb[4];
+      if (base < na) poll_issue(a + (long)base * kFlagStride, na - base, va);
+      if (b && base < nb) poll_issue(b + (long)base * kFlagStride, nb - base, vb);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const int i = min(base + lane + 64 * k, count - 1);
-        v[k] = __hip_atomic_load(flags + (long)i * kFlagStride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (base < na) ok &= (va[k] >= ta) ? 1 : 0;
+        if (b && base < nb) ok &= (vb[k] >= tb) ? 1 : 0;
       }
-#pragma unroll
-      for (int k = 0; k < 4; ++k) ok &= (v[k] >= target) ? 1 : 0;
     }
     if (__all(ok)) return true;
     if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return false;
@@ -72,14 +86,17 @@ __device__ __forceinline__ void store_coherent(typename Dt<BF16>::T* p, typename
 // never used).  With no branch around a load, the compiler's wait counting
 // stays exact and a wave keeps PD chunks of loads in flight ahead of its
 // MFMAs.  !VEC handles ragged sizes with per-element loads (slow, correct).
+// PD: chunks of loads in flight per wave, from a budget of 48 registers for the
+// ring (two waves share a SIMD, so a wave has at most 256 registers in all).
 template <int MW, int NW, bool STREAM>
 struct RecShape {
   static constexpr int kRegsPerChunk = 8 * NW + (STREAM ? 8 * MW : 0);
-  static constexpr int PD = (128 / kRegsPerChunk) < 2 ? 2 : ((128 / kRegsPerChunk) > 8 ? 8 : 128 / kRegsPerChunk);
+  static constexpr int kBudget = 48;
+  static constexpr int PD = (kBudget / kRegsPerChunk) < 2 ? 2 : ((kBudget / kRegsPerChunk) > 8 ? 8 : kBudget / kRegsPerChunk);
 };
 
-template <bool BF16, int MW, int NW, bool STREAM, bool VEC>
-__global__ void __launch_bounds__(kRecThreads) lstm_rec_kernel(const RecParams P) {
+template <bool BF16, int MW, int NW, bool STREAM, bool VEC, int NWV>
+__global__ void __launch_bounds__(64 * NWV) lstm_rec_kernel(const RecParams P) {
   typedef typename Dt<BF16>::T T;
   constexpr int KC = Dt<BF16>::KC;
   constexpr int FQ = KC / 4;
@@ -124,7 +141,7 @@ __global__ void __launch_bounds__(kRecThreads) lstm_rec_kernel(const RecParams P
   // ---- keep this workgroup's weight rows on chip for the whole sequence
   if (!STREAM && LY(staged)) {
     const int total = mcnt * nch * 64;
-    for (int f = tid; f < total; f += kRecThreads) {
+    for (int f = tid; f < total; f += 64 * NWV) {
       const int ln = f & 63;
       const int c = (f >> 6) % nch;
       const int m = (f >> 6) / nch;
@@ -191,6 +208,10 @@ __global__ void __launch_bounds__(kRecThreads) lstm_rec_kernel(const RecParams P
   auto stamp = [&](int t, int k) {
     if (trc && tid == 0) trc[t * 8 + k] = wall_clock64();
   };
+  // shader-clock counter next to wall-clock stamps 0 and 2 (gives the core clock)
+  auto stamp_clk = [&](int t, int k) {
+    if (trc && tid == 0) trc[t * 8 + k] = clock64();
+  };
 
   const T* Wp = reinterpret_cast<const T*>(LY(W));
   const T* Rp = reinterpret_cast<const T*>(LY(R));
@@ -207,6 +228,7 @@ __global__ void __launch_bounds__(kRecThreads) lstm_rec_kernel(const RecParams P
 
   for (int t = 0; t < T_; ++t) {
     stamp(t, 0);
+    stamp_clk(t, 6);
     // ---- hoisted pre-activations of this wave's tiles (do not depend on the wait)
     f32x4 gq[MW][NW];
     if (Gp) {
@@ -218,13 +240,12 @@ __global__ void __launch_bounds__(kRecThreads) lstm_rec_kernel(const RecParams P
     }
 
     // ---- wait for h^l_{t-1} (own layer) and h^{l-1}_t (producer in this launch)
-    const bool need_own = t > 0;
-    const bool need_dep = LY(dep_flags) != nullptr;
-    if (need_own || need_dep) {
+    const int* own = t > 0 ? LY(flags) : nullptr;
+    const int* dep = LY(dep_flags);
+    if (own || dep) {
       if (wave == 0) {
-        bool ok = true;
-        if (need_own) ok = wait_counts(LY(flags), LY(wg_count), t, P.err, P.timeout_ticks);
-        if (ok && need_dep) ok = wait_counts(LY(dep_flags), LY(dep_count), t + 1, P.err, P.timeout_ticks);
+        const bool ok = own ? wait_counts(own, LY(wg_count), t, dep, LY(dep_count), t + 1, P.err, P.timeout_ticks)
+                            : wait_counts(dep, LY(dep_count), t + 1, nullptr, 0, 0, P.err, P.timeout_ticks);
         if (lane == 0) s_ok = ok ? 1 : 0;
       }
       __syncthreads();
@@ -232,7 +253,6 @@ __global__ void __launch_bounds__(kRecThreads) lstm_rec_kernel(const RecParams P
     }
     stamp(t, 1);
 
-    // ---- grouped products: [W_l | R_l] (rows of this workgroup) x [u_t ; h_{t-1}]
     f32x4 acc[MW][NW];
 #pragma unroll
     for (int i = 0; i < MW; ++i)
@@ -241,13 +261,11 @@ __global__ void __launch_bounds__(kRecThreads) lstm_rec_kernel(const RecParams P
 
     const T* hsrc = t > 0 ? Xp + (long)(t - 1) * slot : reinterpret_cast<const T*>(LY(h0));
     const T* usrc = Kin ? Up + (long)t * slot : nullptr;
-    const int c_end = hsrc ? nch : nch_u;
-    const int n_my = c_end > kg ? (c_end - kg + ks - 1) / ks : 0;
 
     Frag rb[PD][NW];
     Frag ra[STREAM ? PD : 1][MW];
-    auto issue = [&](Frag (&b)[NW], Frag (&a)[MW], int ci) {
-      const int c = kg + ci * ks;
+    // loads of chunk c (c < nch_u: input part, else recurrent part)
+    auto issue = [&](Frag (&b)[NW], Frag (&a)[MW], int c) {
       const bool is_u = c < nch_u;
       const int Kseg = is_u ? Kin : H;
       const int kk = (is_u ? c : c - nch_u) * KC + q * FQ;
@@ -271,63 +289,73 @@ __global__ void __launch_bounds__(kRecThreads) lstm_rec_kernel(const RecParams P
         }
       }
     };
-    // Weight fragments from LDS are read one chunk ahead (acur holds chunk ci's
-    // when compute(s, ci) starts), so their latency hides behind the MFMAs.
-    Frag acur[MW];
-    auto lds_a = [&](int ci) {
-      const int c = kg + min(ci, n_my - 1) * ks;
+    // this wave's chunks of one part: c = c0 + ci * ks for ci < n
+    auto products = [&](int c0, int n) {
+      // Weight fragments from LDS are read one chunk ahead (acur holds chunk
+      // ci's when compute(s, ci) starts), so their latency hides behind the MFMAs.
+      Frag acur[MW];
+      auto lds_a = [&](int ci) {
+        const int c = c0 + min(ci, n - 1) * ks;
 #pragma unroll
-      for (int i = 0; i < MW; ++i)
-        if (mval[i]) acur[i] = As[(mloc[i] * nch + c) * 64 + lane];
-    };
-    auto compute = [&](int s, int ci) {
-      Frag a[MW];
+        for (int i = 0; i < MW; ++i)
+          if (mval[i]) acur[i] = As[(mloc[i] * nch + c) * 64 + lane];
+      };
+      auto compute = [&](int s, int ci) {
+        Frag a[MW];
 #pragma unroll
-      for (int i = 0; i < MW; ++i) {
-        if (STREAM)
-          a[i] = ra[STREAM ? s : 0][i];
-        else
-          a[i] = acur[i];
-      }
-      if (!STREAM) lds_a(ci + 1);
+        for (int i = 0; i < MW; ++i) {
+          if (STREAM)
+            a[i] = ra[STREAM ? s : 0][i];
+          else
+            a[i] = acur[i];
+        }
+        if (!STREAM) lds_a(ci + 1);
 #pragma unroll
-      for (int i = 0; i < MW; ++i)
+        for (int i = 0; i < MW; ++i)
 #pragma unroll
-        for (int j = 0; j < NW; ++j)
-          if (mval[i] && nval[j]) mfma_frag<BF16>(acc[i][j], a[i], rb[s][j]);
-    };
-    if (n_my > 0 && n_my <= PD) {
-      // burst: every chunk of this wave in flight at once
+          for (int j = 0; j < NW; ++j)
+            if (mval[i] && nval[j]) mfma_frag<BF16>(acc[i][j], a[i], rb[s][j]);
+      };
+      if (n > 0 && n <= PD) {
+        // burst: every chunk of this wave in flight at once
 #pragma unroll
-      for (int s = 0; s < PD; ++s) issue(rb[s], ra[STREAM ? s : 0], min(s, n_my - 1));
-      if (!STREAM) lds_a(0);
-      __builtin_amdgcn_sched_barrier(0);
+        for (int s = 0; s < PD; ++s) issue(rb[s], ra[STREAM ? s : 0], c0 + min(s, n - 1) * ks);
+        if (!STREAM) lds_a(0);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int s = 0; s < PD; ++s)
-        if (s < n_my) compute(s, s);
-    } else if (n_my > PD) {
-      // ring: every issue is unconditional (chunk index clamped to the last one)
-      // and the loop runs to a multiple of PD, so the load stream has no
-      // branches; only the MFMAs of the padded tail are skipped.  The scheduling
-      // barriers keep each refill where it is written instead of next to its use.
-      const int n_pad = (n_my + PD - 1) / PD * PD;
+        for (int s = 0; s < PD; ++s)
+          if (s < n) compute(s, s);
+      } else if (n > PD) {
+        // ring: every issue is unconditional (chunk index clamped to the last one)
+        // and the loop runs to a multiple of PD, so the load stream has no
+        // branches; only the MFMAs of the padded tail are skipped.  The
+        // scheduling barriers keep each refill where it is written instead of
+        // next to its use.
+        const int n_pad = (n + PD - 1) / PD * PD;
 #pragma unroll
-      for (int s = 0; s < PD; ++s) issue(rb[s], ra[STREAM ? s : 0], s);
-      if (!STREAM) lds_a(0);
-      __builtin_amdgcn_sched_barrier(0);
-      for (int i0 = 0; i0 < n_pad; i0 += PD) {
+        for (int s = 0; s < PD; ++s) issue(rb[s], ra[STREAM ? s : 0], c0 + s * ks);
+        if (!STREAM) lds_a(0);
+        __builtin_amdgcn_sched_barrier(0);
+        for (int i0 = 0; i0 < n_pad; i0 += PD) {
 #pragma unroll
-        for (int s = 0; s < PD; ++s) {
-          const int ci = i0 + s;
-          if (ci < n_my) compute(s, ci);
-          issue(rb[s], ra[STREAM ? s : 0], min(ci + PD, n_my - 1));
-          __builtin_amdgcn_sched_barrier(0);
+          for (int s = 0; s < PD; ++s) {
+            const int ci = i0 + s;
+            if (ci < n) compute(s, ci);
+            issue(rb[s], ra[STREAM ? s : 0], c0 + min(ci + PD, n - 1) * ks);
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
       }
-    }
-    stamp(t, 2);
+    };
 
-    // ---- combine the K-split partial sums
+    // a null h_{t-1} (t = 0 without h0) is zero: only the input chunks remain
+    const int c_end = hsrc ? nch : nch_u;
+    products(kg, c_end > kg ? (c_end - kg + ks - 1) / ks : 0);
+    stamp(t, 2);
+    stamp_clk(t, 7);
+
+    // ---- combine the K-split partial sums: tile e is finalised by K-group
+    // e % ks; every other K-group of its tile group leaves one partial in LDS
     if (ks > 1) {
       f32x4* red = reinterpret_cast<f32x4*>(smem + P.red_off);
       const int tpg = P.mw * P.nw;
@@ -337,7 +365,9 @@ __global__ void __launch_bounds__(kRecThreads) lstm_rec_kernel(const RecParams P
         for (int j = 0; j < NW; ++j) {
           if (!(mval[i] && nval[j]) || fin(i, j)) continue;
           const int e = i * P.nw + j;
-          red[((tg * tpg + e) * ks + kg) * 64 + lane] = acc[i][j];
+          const int f = e % ks;
+          const int slot_r = kg < f ? kg : kg - 1;
+          red[((tg * tpg + e) * (ks - 1) + slot_r) * 64 + lane] = acc[i][j];
         }
       __syncthreads();
 #pragma unroll
@@ -346,8 +376,7 @@ __global__ void __launch_bounds__(kRecThreads) lstm_rec_kernel(const RecParams P
         for (int j = 0; j < NW; ++j) {
           if (!(mval[i] && nval[j]) || !fin(i, j)) continue;
           const int e = i * P.nw + j;
-          for (int k2 = 0; k2 < ks; ++k2)
-            if (k2 != kg) acc[i][j] += red[((tg * tpg + e) * ks + k2) * 64 + lane];
+          for (int r = 0; r < ks - 1; ++r) acc[i][j] += red[((tg * tpg + e) * (ks - 1) + r) * 64 + lane];
         }
     }
     stamp(t, 3);
