@@ -53,6 +53,42 @@ def kernel_flops(cfg, kind: int, regime: int, launch_index: int) -> float:
     return 2.0 * 4 * H * H * B * T  # layerwise: one layer's recurrence
 
 
+def kernel_source_digest() -> str:
+    """sha256 over the library sources (kernels, planner, launch code): HBM counter
+    figures taken for other sources no longer describe the kernel."""
+    import hashlib
+    csrc = os.path.join(ROOT, "stacked_lstm_forward_amd", "csrc")
+    h = hashlib.sha256()
+    for fn in sorted(os.listdir(csrc)):
+        if fn.endswith((".h", ".hip", ".cpp")):
+            h.update(fn.encode())
+            h.update(open(os.path.join(csrc, fn), "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` on `workload` from the committed counter
+    summaries in profiles/ (a line 'bench-traffic: {json}'), or None when there
+    is none for the current sources."""
+    pdir = os.path.join(ROOT, "profiles")
+    if not os.path.isdir(pdir):
+        return None
+    digest = kernel_source_digest()
+    for fn in sorted(os.listdir(pdir)):
+        if not fn.endswith((".md", ".txt")):
+            continue
+        for line in open(os.path.join(pdir, fn)):
+            if not line.startswith("bench-traffic:"):
+                continue
+            try:
+                rec = json.loads(line.split(":", 1)[1])
+            except ValueError:
+                continue
+            if rec.get("workload") == workload and rec.get("kernel") == kernel and rec.get("source_sha256") == digest:
+                return int(rec["fetch_bytes"] + rec["write_bytes"])
+    return None
+
+
 def cpu_baseline(inp, cfg, min_seconds: float) -> dict:
     import numpy as np  # noqa: F401
     from oracle.lstm_oracle import lstm_forward_inputs
@@ -86,8 +122,13 @@ def main() -> int:
                     help="only run a device-to-device copy of this many MiB (calibrates HBM traffic counters)")
     ap.add_argument("--plain-launch", action="store_true",
                     help="ordinary (not cooperative) launch of the persistent kernel, for profilers")
+    ap.add_argument("--source-digest", action="store_true",
+                    help="print the digest of the library sources that counter summaries are keyed on")
     args = ap.parse_args()
 
+    if args.source_digest:
+        print(kernel_source_digest())
+        return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the forward pass here runs on a single MI355X and this build "
@@ -217,7 +258,8 @@ def main() -> int:
         "config": {"workload": WORKLOAD_TEXT[cfg.name], "L": cfg.L, "I": cfg.I, "H": cfg.H, "B": cfg.B,
                    "T": cfg.T, "regime": plan["regime"], "gflop_per_step": round(cfg.flops / 1e9, 3)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "frac": round(achieved / peak, 4),
+                     "traffic": measured_traffic(cfg.name, kname.get(dom, str(dom))),
                      "kernel": kname.get(dom, str(dom)), "ms_per_launch": round(dom_ms, 5),
                      "gflop_per_launch": round(dom_flops / 1e9, 3)},
         "whole_step_frac_of_mfma_peak": round(value / peak, 4),
