@@ -41,15 +41,18 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_flops(cfg, kind: int, regime: int, launch_index: int) -> float:
+def kernel_flops(cfg, kind: int, plan: dict, launch_index: int) -> float:
     """Algorithmic FLOPs of one launch (2 per multiply-add; bias and gate math excluded)."""
     H, B, T, L, I = cfg.H, cfg.B, cfg.T, cfg.L, cfg.I
     if kind == 1:  # input GEMM of one layer; launch 0 is layer 0
-        layer = 0 if regime == 2 else launch_index // 2
+        layer = 0 if plan["regime"] == "wavefront" else launch_index // 2
         il = I if layer == 0 else H
         return 2.0 * 4 * H * il * B * T
-    if regime == 2:  # wavefront: R h for every layer + fused W u for layers >= 1
-        return 2.0 * 4 * H * H * B * T * L + 2.0 * 4 * H * H * B * T * (L - 1)
+    if kind != 2:  # clearing the step counters
+        return 0.0
+    if plan["regime"] == "wavefront":  # R h for every layer + the fused W u products
+        fused_in = (I + (L - 1) * H) if plan["input_gemms"] == 0 else (L - 1) * H
+        return 2.0 * 4 * H * H * B * T * L + 2.0 * 4 * H * fused_in * B * T
     return 2.0 * 4 * H * H * B * T  # layerwise: one layer's recurrence
 
 
@@ -221,7 +224,7 @@ def main() -> int:
             kind = kinds[k][j]
             d = evs[k][j].elapsed_time(evs[k][maxl + j])
             per_kind.setdefault(kind, []).append(d)
-            flops_kind.setdefault(kind, []).append(kernel_flops(cfg, kind, regime, j))
+            flops_kind.setdefault(kind, []).append(kernel_flops(cfg, kind, plan, j))
     dom = max(per_kind, key=lambda kk: sum(per_kind[kk]))
     dom_ms = sum(per_kind[dom]) / len(per_kind[dom])
     dom_flops = sum(flops_kind[dom]) / len(flops_kind[dom])
@@ -240,7 +243,7 @@ def main() -> int:
         log("timing the fp64 oracle on the host (cpu_baseline)")
         cpu = cpu_baseline(inp, cfg, args.cpu_seconds)
 
-    kname = {1: "lstm_input_gemm", 2: "lstm_rec_kernel"}
+    kname = {1: "lstm_input_gemm", 2: "lstm_rec_kernel", 3: "lstm_clear"}
     out = {
         "metric": "stacked-LSTM fwd TFLOPS (% of MI355X roofline) and ms/sequence",
         "value": round(value, 4),

@@ -82,7 +82,12 @@ typedef enum {
 } lstm_regime_t;
 
 /* Kinds of kernel launch reported through lstm_fwd_opts_t. */
-typedef enum { LSTM_KERNEL_INPUT_GEMM = 1, LSTM_KERNEL_RECURRENT = 2 } lstm_kernel_kind_t;
+typedef enum {
+  LSTM_KERNEL_INPUT_GEMM = 1, /* grouped input projection of one layer over all steps            */
+  LSTM_KERNEL_RECURRENT = 2,  /* persistent recurrence (one layer, or several as a wavefront)     */
+  LSTM_KERNEL_CLEAR = 3       /* clears the error word and step counters when no input GEMM
+                                 runs first (every layer's input product fused into the steps)   */
+} lstm_kernel_kind_t;
 
 /* Size in bytes of the workspace lstm_fwd needs for `d`; 0 if `d` is invalid or unsupported. */
 size_t lstm_fwd_workspace_size(const lstm_desc_t *d);
@@ -168,6 +173,8 @@ typedef struct {
   int32_t wave_tiles_m;      /* most M-tiles one wave computes                                 */
   int32_t wave_tiles_n;      /* most column tiles one wave computes                            */
   int32_t weights_streamed;  /* 1 if the first recurrent launch reads weights from HBM per step */
+  int32_t input_gemms;       /* input-projection GEMM launches per call; 0 when every layer's
+                                input product W_l u_t is fused into its recurrent steps          */
 } lstm_plan_info_t;
 
 /*

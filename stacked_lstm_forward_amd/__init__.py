@@ -29,7 +29,7 @@ LIB_PATH = os.path.join(HERE, "lib", "liblstm_fwd.so")
 LSTM_F32, LSTM_BF16 = 0, 1
 LSTM_OK, LSTM_ERR_INVALID_ARG, LSTM_ERR_UNSUPPORTED, LSTM_ERR_WORKSPACE, LSTM_ERR_HIP, LSTM_ERR_BARRIER_TIMEOUT = range(6)
 LSTM_REGIME_AUTO, LSTM_REGIME_LAYERWISE, LSTM_REGIME_WAVEFRONT = 0, 1, 2
-LSTM_KERNEL_INPUT_GEMM, LSTM_KERNEL_RECURRENT = 1, 2
+LSTM_KERNEL_INPUT_GEMM, LSTM_KERNEL_RECURRENT, LSTM_KERNEL_CLEAR = 1, 2, 3
 
 EXPORTED = ("lstm_fwd_workspace_size", "lstm_fwd", "lstm_fwd_ex", "lstm_status_string",
             "lstm_fwd_validate", "lstm_fwd_last_error", "lstm_fwd_plan")
@@ -55,7 +55,7 @@ class PlanInfo(ctypes.Structure):
                 ("wg_per_layer", ctypes.c_int32 * 16), ("mtiles_per_wg", ctypes.c_int32 * 16),
                 ("tile_groups_m", ctypes.c_int32), ("tile_groups_n", ctypes.c_int32),
                 ("wave_tiles_m", ctypes.c_int32), ("wave_tiles_n", ctypes.c_int32),
-                ("weights_streamed", ctypes.c_int32)]
+                ("weights_streamed", ctypes.c_int32), ("input_gemms", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
         n = self.layers_per_launch
@@ -66,7 +66,7 @@ class PlanInfo(ctypes.Structure):
                 "mtiles_per_wg": list(self.mtiles_per_wg[:n]),
                 "tile_groups": [self.tile_groups_m, self.tile_groups_n],
                 "wave_tiles": [self.wave_tiles_m, self.wave_tiles_n],
-                "weights_streamed": bool(self.weights_streamed)}
+                "weights_streamed": bool(self.weights_streamed), "input_gemms": self.input_gemms}
 
 
 class LstmError(RuntimeError):

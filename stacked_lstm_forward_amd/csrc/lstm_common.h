@@ -13,12 +13,16 @@
 // one (unit, column) pair, so the gate non-linearities and the cell update run
 // in registers straight after the product.
 //
-// Operand fragments: per MFMA group a lane loads 32 contiguous bytes of one
-// row (8 fp32 or 16 bf16).  A "chunk" is the K range one 16-row tile covers
-// with one such load per lane: 32 fp32 or 64 bf16 columns (128 bytes per row).
-// The weight fragment and the activation fragment of a lane cover the same K
-// indices, so the sum over K is exact whatever order the hardware uses inside
-// one MFMA.
+// Operand fragments: a "chunk" is 128 bytes of every row of a 16-row tile
+// (32 fp32 or 64 bf16 K columns).  Lane l serves row l%16 and quad q = l/16;
+// it holds two 16-byte halves: half h covers the chunk's columns
+// [h*KC/2 + q*KC/8, h*KC/2 + (q+1)*KC/8).  The four quads' halves h together
+// cover 64 contiguous bytes of the row, so every 16-byte load (global or LDS)
+// of a wave touches whole 64-byte pieces.  The weight fragment and the
+// activation fragment of a lane cover the same K indices, so the sum over K is
+// exact whatever order the hardware uses inside one MFMA.  In LDS a block of
+// 64 fragments is stored half-major (all lanes' half 0, then all lanes' half
+// 1), so a wave's 16-byte LDS access is 1 KiB contiguous.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -30,7 +34,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 struct Frag {
-  uint4 v[2];  // 32 bytes: 8 fp32 or 16 bf16 of one row
+  uint4 v[2];  // two 16-byte halves of one row's chunk (see above)
 };
 
 template <bool BF16>
@@ -79,41 +83,62 @@ __device__ __forceinline__ void mfma_frag<false>(f32x4& acc, const Frag& a, cons
   for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa1[e], fb1[e], acc, 0, 0, 0);
 }
 
-// 32 bytes at p (16-byte aligned), two unconditional 16-byte loads
-__device__ __forceinline__ Frag load_frag_vec(const void* p) {
-  const uint4* q = reinterpret_cast<const uint4*>(p);
+// Column of half h of quad q's fragment, relative to the chunk start.
+template <bool BF16>
+__device__ __forceinline__ int frag_col(int q, int h) {
+  return h * (Dt<BF16>::KC / 2) + q * (Dt<BF16>::KC / 8);
+}
+
+// Quad q's fragment of the chunk that starts at element p of a row (16-byte
+// aligned): two unconditional 16-byte loads.
+template <bool BF16>
+__device__ __forceinline__ Frag load_frag_vec(const typename Dt<BF16>::T* p, int q) {
   Frag f;
-  f.v[0] = q[0];
-  f.v[1] = q[1];
+  f.v[0] = *reinterpret_cast<const uint4*>(p + frag_col<BF16>(q, 0));
+  f.v[1] = *reinterpret_cast<const uint4*>(p + frag_col<BF16>(q, 1));
   return f;
 }
 
-// Load 32 bytes (8 fp32 or 16 bf16) starting at element off + k0 of a row of
-// length K, zero-filling columns >= K.  `vec_ok` says 16-byte loads are
-// aligned there (every row start is a multiple of 16 bytes).
+// Quad q's fragment of the chunk starting at column k0 of the row at element
+// offset `off` (row length K), zero-filling columns >= K.  `vec_ok` says
+// 16-byte loads are aligned (every row start is a multiple of 16 bytes).
 template <bool BF16>
-__device__ __forceinline__ Frag load_frag_off(const void* base, long off, int k0, int K, bool vec_ok) {
+__device__ __forceinline__ Frag load_frag_off(const void* base, long off, int k0, int q, int K, bool vec_ok) {
   typedef typename Dt<BF16>::T T;
-  constexpr int N = 32 / Dt<BF16>::SZ;
-  const T* p = reinterpret_cast<const T*>(base) + off + k0;
+  constexpr int N = 16 / Dt<BF16>::SZ;  // elements per half
+  const T* row = reinterpret_cast<const T*>(base) + off;
   Frag f;
-  if (vec_ok && k0 + N <= K) {
-    const uint4* q = reinterpret_cast<const uint4*>(p);
-    f.v[0] = q[0];
-    f.v[1] = q[1];
-    return f;
-  }
-  T tmp[N];
 #pragma unroll
-  for (int e = 0; e < N; ++e) tmp[e] = (k0 + e < K) ? p[e] : T(0);
-  __builtin_memcpy(&f, tmp, 32);
+  for (int h = 0; h < 2; ++h) {
+    const int k = k0 + frag_col<BF16>(q, h);
+    if (vec_ok && k + N <= K) {
+      f.v[h] = *reinterpret_cast<const uint4*>(row + k);
+    } else {
+      T tmp[N];
+#pragma unroll
+      for (int e = 0; e < N; ++e) tmp[e] = (k + e < K) ? row[k + e] : T(0);
+      __builtin_memcpy(&f.v[h], tmp, 16);
+    }
+  }
   return f;
 }
 
 // Same for row `row` of a row-major [rows][ld] matrix.
 template <bool BF16>
-__device__ __forceinline__ Frag load_frag(const void* base, long ld, long row, int k0, int K, bool vec_ok) {
-  return load_frag_off<BF16>(base, row * ld, k0, K, vec_ok);
+__device__ __forceinline__ Frag load_frag(const void* base, long ld, long row, int k0, int q, int K, bool vec_ok) {
+  return load_frag_off<BF16>(base, row * ld, k0, q, K, vec_ok);
+}
+
+// A block of 64 fragments in LDS, half-major: lane l's half h at [h * 64 + l].
+__device__ __forceinline__ void lds_put(uint4* blk, int lane, const Frag& f) {
+  blk[lane] = f.v[0];
+  blk[64 + lane] = f.v[1];
+}
+__device__ __forceinline__ Frag lds_get(const uint4* blk, int lane) {
+  Frag f;
+  f.v[0] = blk[lane];
+  f.v[1] = blk[64 + lane];
+  return f;
 }
 
 // Caller row of tile row rho of M-tile mt (gate-interleaved order); -1 past H.

@@ -18,6 +18,7 @@
 namespace lstm {
 hipError_t launch_input_gemm(bool bf16, const GemmParams& p, hipStream_t s);
 hipError_t rec_prepare(bool bf16, bool stream, bool vec, int nwv, int mw, int nw, int lds_bytes, int* max_blocks_per_cu);
+hipError_t launch_clear(int* p, long long n, hipStream_t s);
 hipError_t launch_rec(bool bf16, bool stream, bool vec, int nwv, const RecParams& p, int lds_bytes, bool plain,
                       hipStream_t s);
 }  // namespace lstm
@@ -122,6 +123,7 @@ lstm_status_t lstm_fwd_plan(const lstm_desc_t* d, int32_t force_regime, int32_t 
   out->wave_tiles_m = p.rec[0].mw;
   out->wave_tiles_n = p.rec[0].nw;
   out->weights_streamed = p.rec[0].stream;
+  out->input_gemms = p.ngemm;
   return LSTM_OK;
 }
 
@@ -256,7 +258,8 @@ lstm_status_t lstm_fwd_ex(const lstm_desc_t* d, const void* x, const void* h0, c
       r.R = R_l(l);
       r.bias = b_l(l);
       r.G = pl.hoisted ? G : nullptr;
-      r.U = pl.hoisted ? nullptr : xbuf(l - 1);
+      r.U = pl.hoisted ? nullptr : (l == 0 ? x : xbuf(l - 1));
+      r.u_slot = pl.hoisted ? 0 : (l == 0 ? (long long)B * I : (long long)slot);
       r.X = xbuf(l);
       r.Yout = (l == L - 1) ? y : nullptr;
       r.h0 = state(h0, l, ds);
@@ -267,14 +270,15 @@ lstm_status_t lstm_fwd_ex(const lstm_desc_t* d, const void* x, const void* h0, c
       const bool dep_here = !pl.hoisted && k > 0;
       r.dep_flags = dep_here ? flags + (size_t)(l - 1) * kFlagsPerLayer * kFlagStride : nullptr;
       r.dep_count = dep_here ? lp.layers[k - 1].wg_count : 0;
-      r.Kin = pl.hoisted ? 0 : H;
+      r.Kin = pl.Kin;
       r.wg_begin = pl.wg_begin;
       r.wg_count = pl.wg_count;
       r.mt_per_wg = pl.mt_per_wg;
       r.staged = pl.staged;
       const size_t row_bytes = (size_t)H * ds;
       r.vec_ok = (row_bytes % 16 == 0) && aligned16(r.R) && aligned16(r.X) && (!r.W || aligned16(r.W)) &&
-                 (!r.U || aligned16(r.U)) && (!r.h0 || aligned16(r.h0));
+                 (!r.U || aligned16(r.U)) && (!r.h0 || aligned16(r.h0)) && (r.Kin % p.KC) == 0 &&
+                 ((size_t)r.u_slot * ds) % 16 == 0;
     }
     for (int k = lp.nlayers; k < kMaxLayersPerLaunch; ++k) rp.layer[k] = RecLayer();
     // aligned fast path: whole chunks and 16-byte aligned rows in every layer of the launch
@@ -291,9 +295,16 @@ lstm_status_t lstm_fwd_ex(const lstm_desc_t* d, const void* x, const void* h0, c
     return LSTM_OK;
   };
 
-  // layer 0 input projection (+ zeroing of the error word and step counters)
-  st = gemm(0, x, (long long)B * I, I, true);
-  if (st != LSTM_OK) return st;
+  if (p.ngemm > 0) {
+    // layer 0 input projection (+ zeroing of the error word and step counters)
+    st = gemm(0, x, (long long)B * I, I, true);
+    if (st != LSTM_OK) return st;
+  } else {
+    // every input product is fused into the steps: only the counters need clearing
+    if (!before(LSTM_KERNEL_CLEAR)) return LSTM_ERR_HIP;
+    if (launch_clear(reinterpret_cast<int*>(wsb), (long long)p.zero_ints, stream) != hipSuccess) return LSTM_ERR_HIP;
+    if (!after()) return LSTM_ERR_HIP;
+  }
   if (p.regime == LSTM_REGIME_WAVEFRONT) {
     for (int r = 0; r < p.nrec; ++r) {
       st = rec(p.rec[r]);

@@ -18,6 +18,8 @@
 //    proposed method: overlapping layers).  Steps are ordered with per-workgroup
 //    step counters (agent-scope release/acquire), polled with a time limit so a
 //    wait can never hang.
+#include <algorithm>
+
 #include "lstm_common.h"
 #include "lstm_params.h"
 
@@ -35,31 +37,31 @@ namespace lstm {
 // VEC: K is a whole number of chunks and rows are 16-byte aligned, so every
 // fragment load is unconditional (rows past the end are clamped to a valid row
 // and their results dropped); the ragged path loads element by element.
+// (k0: first column of the chunk; q: the lane's quad)
 template <bool BF16, bool VEC>
-__device__ __forceinline__ Frag gemm_load_a(const GemmParams& P, long arow, int k0) {
+__device__ __forceinline__ Frag gemm_load_a(const GemmParams& P, long arow, int k0, int q) {
   typedef typename Dt<BF16>::T T;
-  if (VEC) return load_frag_vec(reinterpret_cast<const T*>(P.W) + arow * P.K + k0);
-  return arow >= 0 ? load_frag<BF16>(P.W, P.K, arow, k0, P.K, P.vec_ok_w) : zero_frag();
+  if (VEC) return load_frag_vec<BF16>(reinterpret_cast<const T*>(P.W) + arow * P.K + k0, q);
+  return arow >= 0 ? load_frag<BF16>(P.W, P.K, arow, k0, q, P.K, P.vec_ok_w) : zero_frag();
 }
 
 template <bool BF16, bool VEC>
-__device__ __forceinline__ Frag gemm_load_b(const GemmParams& P, long boff, bool bval, int k0) {
+__device__ __forceinline__ Frag gemm_load_b(const GemmParams& P, long boff, bool bval, int k0, int q) {
   typedef typename Dt<BF16>::T T;
-  if (VEC) return load_frag_vec(reinterpret_cast<const T*>(P.U) + boff + k0);
-  return bval ? load_frag_off<BF16>(P.U, boff, k0, P.K, P.vec_ok_u) : zero_frag();
+  if (VEC) return load_frag_vec<BF16>(reinterpret_cast<const T*>(P.U) + boff + k0, q);
+  return bval ? load_frag_off<BF16>(P.U, boff, k0, q, P.K, P.vec_ok_u) : zero_frag();
 }
 
 template <bool BF16, bool VEC>
 __global__ void __launch_bounds__(kGemmThreads) lstm_input_gemm(const GemmParams P) {
   constexpr int KC = Dt<BF16>::KC;
-  constexpr int FQ = KC / 4;
   constexpr int MTW = kGemmTileM / 16;  // M-tiles per workgroup (16)
   constexpr int NTW = kGemmTileN / 16;  // column tiles per workgroup (8)
   constexpr int NA = MTW * 64 / kGemmThreads;  // A fragments staged per thread per chunk (4)
   constexpr int NB = NTW * 64 / kGemmThreads;  // B fragments staged per thread per chunk (2)
-  constexpr int STAGE = (MTW + NTW) * 64;      // fragments per LDS stage
+  constexpr int STAGE = (MTW + NTW) * 128;     // 16-byte halves per LDS stage
   extern __shared__ __align__(16) unsigned char gsmem[];
-  Frag* lds = reinterpret_cast<Frag*>(gsmem);
+  uint4* lds = reinterpret_cast<uint4*>(gsmem);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -104,39 +106,39 @@ __global__ void __launch_bounds__(kGemmThreads) lstm_input_gemm(const GemmParams
   Frag ra[NA], rb[NB];
   if (nch > 0) {
 #pragma unroll
-    for (int s = 0; s < NA; ++s) ra[s] = gemm_load_a<BF16, VEC>(P, arow[s], q * FQ);
+    for (int s = 0; s < NA; ++s) ra[s] = gemm_load_a<BF16, VEC>(P, arow[s], 0, q);
 #pragma unroll
-    for (int s = 0; s < NB; ++s) rb[s] = gemm_load_b<BF16, VEC>(P, boff[s], bval[s], q * FQ);
+    for (int s = 0; s < NB; ++s) rb[s] = gemm_load_b<BF16, VEC>(P, boff[s], bval[s], 0, q);
 #pragma unroll
-    for (int s = 0; s < NA; ++s) lds[tid + s * kGemmThreads] = ra[s];
+    for (int s = 0; s < NA; ++s) lds_put(lds + (tid / 64 + s * (kGemmThreads / 64)) * 128, lane, ra[s]);
 #pragma unroll
-    for (int s = 0; s < NB; ++s) lds[MTW * 64 + tid + s * kGemmThreads] = rb[s];
+    for (int s = 0; s < NB; ++s) lds_put(lds + (MTW + tid / 64 + s * (kGemmThreads / 64)) * 128, lane, rb[s]);
     __syncthreads();
   }
   for (int c = 0; c < nch; ++c) {
     // next chunk's loads go out before this chunk's MFMAs (clamped, unconditional)
     const int cn = min(c + 1, nch - 1);
 #pragma unroll
-    for (int s = 0; s < NA; ++s) ra[s] = gemm_load_a<BF16, VEC>(P, arow[s], cn * KC + q * FQ);
+    for (int s = 0; s < NA; ++s) ra[s] = gemm_load_a<BF16, VEC>(P, arow[s], cn * KC, q);
 #pragma unroll
-    for (int s = 0; s < NB; ++s) rb[s] = gemm_load_b<BF16, VEC>(P, boff[s], bval[s], cn * KC + q * FQ);
+    for (int s = 0; s < NB; ++s) rb[s] = gemm_load_b<BF16, VEC>(P, boff[s], bval[s], cn * KC, q);
     __builtin_amdgcn_sched_barrier(0);
-    const Frag* st = lds + (c & 1) * STAGE;
+    const uint4* st = lds + (c & 1) * STAGE;
     Frag b[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = st[MTW * 64 + (4 * wn + j) * 64 + lane];
+    for (int j = 0; j < 4; ++j) b[j] = lds_get(st + (MTW + 4 * wn + j) * 128, lane);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const Frag a = st[(8 * wm + i) * 64 + lane];
+      const Frag a = lds_get(st + (8 * wm + i) * 128, lane);
 #pragma unroll
       for (int j = 0; j < 4; ++j) mfma_frag<BF16>(acc[i][j], a, b[j]);
     }
     if (c + 1 < nch) {
-      Frag* nx = lds + ((c + 1) & 1) * STAGE;
+      uint4* nx = lds + ((c + 1) & 1) * STAGE;
 #pragma unroll
-      for (int s = 0; s < NA; ++s) nx[tid + s * kGemmThreads] = ra[s];
+      for (int s = 0; s < NA; ++s) lds_put(nx + (tid / 64 + s * (kGemmThreads / 64)) * 128, lane, ra[s]);
 #pragma unroll
-      for (int s = 0; s < NB; ++s) nx[MTW * 64 + tid + s * kGemmThreads] = rb[s];
+      for (int s = 0; s < NB; ++s) lds_put(nx + (MTW + tid / 64 + s * (kGemmThreads / 64)) * 128, lane, rb[s]);
     }
     __syncthreads();
   }
@@ -163,6 +165,13 @@ __global__ void __launch_bounds__(kGemmThreads) lstm_input_gemm(const GemmParams
       *reinterpret_cast<f32x4*>(dst) = acc[i][j] + bv;
     }
   }
+}
+
+// Zeroes n ints (the error word and the step counters) when no input GEMM
+// runs before the recurrence to do it.  A fill kernel rather than a memset, so
+// the call stays capturable in a HIP graph.
+__global__ void __launch_bounds__(256) lstm_clear(int* p, long long n) {
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256) p[i] = 0;
 }
 
 // ----------------------------------------------------------------------------
@@ -202,6 +211,13 @@ hipError_t launch_input_gemm(bool bf16, const GemmParams& p, hipStream_t s) {
   if (e != hipSuccess) return e;
   void* args[] = {const_cast<GemmParams*>(&p)};
   return hipLaunchKernel(fn, grid, dim3(kGemmThreads), args, lds, s);
+}
+
+hipError_t launch_clear(int* p, long long n, hipStream_t s) {
+  const long long blocks = std::min<long long>((n + 255) / 256, 1024);
+  if (blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(lstm_clear, dim3((unsigned)blocks), dim3(256), 0, s, p, n);
+  return hipGetLastError();
 }
 
 hipError_t rec_prepare(bool bf16, bool stream, bool vec, int nwv, int mw, int nw, int lds_bytes, int* max_blocks_per_cu) {

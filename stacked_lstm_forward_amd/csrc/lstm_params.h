@@ -34,7 +34,8 @@ struct RecLayer {
   const void* R;          // R_l [4H][H]
   const void* bias;       // b_l [4H] (fused input only; hoisted G already holds the bias)
   const float* G;         // hoisted pre-activations [T][Mt][B][16], or null
-  const void* U;          // exchange buffer of the layer below ([T] slots of [B][Kin]), or null
+  const void* U;          // fused input: step t, batch b at U + t*u_slot + b*Kin (the layer
+                          // below's exchange buffer, or x for layer 0), or null
   void* X;                // this layer's exchange buffer: [T] slots of [B][H]
   void* Yout;             // caller's y [T][B][H] (top layer), or null
   const void* h0;         // [B][H] or null (zeros)
@@ -44,6 +45,7 @@ struct RecLayer {
   int* flags;             // per-workgroup step counters of this layer, kFlagStride apart
   const int* dep_flags;   // step counters of the producer of U in this launch, or null
   int dep_count;          // workgroups of that producer
+  long long u_slot;       // elements between two steps of U
   int Kin;                // fused input width (0 when hoisted)
   int wg_begin, wg_count; // virtual workgroup ids owned by this layer
   int mt_per_wg;          // M-tiles per workgroup

@@ -104,14 +104,17 @@ bool plan_single(int layer, int Mt, int nch, int ncnt, const DeviceInfo& dev, La
   return wgs <= kFlagsPerLayer && lp->grid <= std::max(gmax, 8);
 }
 
-// Wavefront launch over layers [l0, l0+n): layer 0 hoisted, others fused.
-bool plan_wavefront(int l0, int n, int Mt, int nch_h, int nch_in0, int ncnt, const DeviceInfo& dev,
-                    LaunchPlan* lp) {
+// Wavefront launch over layers [l0, l0+n).  Layers >= 1 fuse their input
+// product; layer 0 fuses it too when fuse0 (K = I + H), else its input is
+// hoisted into the input GEMM.
+bool plan_wavefront(int l0, int n, int Mt, int nch_h, int nch_x, int I, int H, bool fuse0, int ncnt,
+                    const DeviceInfo& dev, LaunchPlan* lp) {
   const int gmax = dev.num_cus;
   int nchl[kMaxLayersPerLaunch];
   for (int k = 0; k < n; ++k) {
     const int l = l0 + k;
-    nchl[k] = (l == 0) ? nch_h : nch_in0 + nch_h;  // fused layers: input chunks + recurrent chunks
+    // fused layers: input chunks + recurrent chunks
+    nchl[k] = (l == 0) ? (fuse0 ? nch_x + nch_h : nch_h) : nch_h + nch_h;
   }
   // smallest per-workgroup budget (chunks x M-tiles) whose partition fits the grid
   int best_budget = -1;
@@ -134,13 +137,25 @@ bool plan_wavefront(int l0, int n, int Mt, int nch_h, int nch_in0, int ncnt, con
     if (ok && tot <= gmax) { best_budget = wb; break; }
   }
   if (best_budget < 0) return false;
+  // Equal M-tiles per workgroup in every layer when the grid has room: a wave
+  // then owns the same tile set in every layer and none of its tiles is empty
+  // (layers with fewer rows per workgroup only finish their steps sooner).
+  {
+    int mmin = 16;
+    for (int k = 0; k < n; ++k) mmin = std::min(mmin, mt[k]);
+    int tot = 0;
+    for (int k = 0; k < n; ++k) tot += cdiv(Mt, mmin);
+    if (tot <= gmax)
+      for (int k = 0; k < n; ++k) mt[k] = mmin;
+  }
   int mmax = 1, staged_max = 0, begin = 0;
   lp->nlayers = n;
   for (int k = 0; k < n; ++k) {
     LayerPlan& L = lp->layers[k];
     L = LayerPlan();
     L.layer = l0 + k;
-    L.hoisted = (l0 + k == 0) ? 1 : 0;
+    L.hoisted = (l0 + k == 0 && !fuse0) ? 1 : 0;
+    L.Kin = L.hoisted ? 0 : (l0 + k == 0 ? I : H);
     L.nch = nchl[k];
     L.mt_per_wg = mt[k];
     L.wg_count = cdiv(Mt, mt[k]);
@@ -181,34 +196,41 @@ int make_plan(const int32_t L, const int32_t I, const int32_t H, const int32_t B
   if ((long long)T * B > (1LL << 31) / 16 || (long long)H * 4 > (1LL << 30)) return kUnsupported;
 
   const int nch_h = cdiv(H, p.KC);
-  const int nch_hin = cdiv(H, p.KC);  // input width of layers >= 1 is H
+  const int nch_x = cdiv(I, p.KC);
 
   bool wave = false;
   if (force_regime == kRegimeWavefront || (force_regime == kRegimeAuto && L >= 2)) {
-    // try the wavefront: groups of up to 16 layers per launch
-    int nrec = 0;
-    bool ok = true;
-    for (int l0 = 0; l0 < L; l0 += kMaxLayersPerLaunch) {
-      const int n = std::min(kMaxLayersPerLaunch, L - l0);
-      if (!plan_wavefront(l0, n, p.Mt, nch_h, nch_hin, p.ncnt, dev, &p.rec[nrec])) { ok = false; break; }
-      ++nrec;
+    // try the wavefront: groups of up to 16 layers per launch; layer 0's input
+    // product fused into its steps when that fits, else hoisted into one GEMM
+    for (int fuse0 = 1; fuse0 >= 0 && !wave; --fuse0) {
+      int nrec = 0;
+      bool ok = true;
+      for (int l0 = 0; l0 < L; l0 += kMaxLayersPerLaunch) {
+        const int n = std::min(kMaxLayersPerLaunch, L - l0);
+        if (!plan_wavefront(l0, n, p.Mt, nch_h, nch_x, I, H, fuse0 != 0, p.ncnt, dev, &p.rec[nrec])) {
+          ok = false;
+          break;
+        }
+        ++nrec;
+      }
+      if (ok) {
+        wave = true;
+        p.nrec = nrec;
+        p.ngemm = fuse0 ? 0 : 1;
+        p.nclear = fuse0 ? 1 : 0;
+      }
     }
-    if (ok) {
-      wave = true;
-      p.nrec = nrec;
-      p.ngemm = 1;
-    } else if (force_regime == kRegimeWavefront) {
-      return kUnsupported;
-    }
+    if (!wave && force_regime == kRegimeWavefront) return kUnsupported;
   }
   if (!wave) {
     p.nrec = L;
     p.ngemm = L;
+    p.nclear = 0;
     for (int l = 0; l < L; ++l)
       if (!plan_single(l, p.Mt, nch_h, p.ncnt, dev, &p.rec[l])) return kUnsupported;
   }
   p.regime = wave ? kRegimeWavefront : kRegimeLayerwise;
-  p.num_launches = p.nrec + p.ngemm;
+  p.num_launches = p.nrec + p.ngemm + p.nclear;
 
   // workspace: [error word | step counters L x kFlagsPerLayer, one 128-byte line each |
   //             G (one layer) | exchange buffers of all L layers, T slots each]

@@ -42,6 +42,7 @@ struct Plan {
   int nrec = 0;         // recurrent launches
   LaunchPlan rec[64];   // layerwise: one per layer; wavefront: one per group of up to 16 layers
   int ngemm = 0;        // input-GEMM launches
+  int nclear = 0;       // 1: a clear kernel zeroes the error word and step counters (no input GEMM does)
   int num_launches = 0;
   // workspace layout (bytes)
   size_t err_off = 0, flags_off = 0, G_off = 0, hist_off = 0, ws_bytes = 0;

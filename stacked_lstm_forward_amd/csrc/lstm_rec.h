@@ -87,19 +87,20 @@ __device__ __forceinline__ void store_coherent(typename Dt<BF16>::T* p, typename
 // stays exact and a wave keeps PD chunks of loads in flight ahead of its
 // MFMAs.  !VEC handles ragged sizes with per-element loads (slow, correct).
 // PD: chunks of loads in flight per wave, from a budget of 48 registers for the
-// ring (two waves share a SIMD, so a wave has at most 256 registers in all).
+// ring (two waves share a SIMD, so a wave has at most 256 registers in all);
+// even, so that the two LDS weight buffers alternate with the ring slot.
 template <int MW, int NW, bool STREAM>
 struct RecShape {
   static constexpr int kRegsPerChunk = 8 * NW + (STREAM ? 8 * MW : 0);
   static constexpr int kBudget = 48;
-  static constexpr int PD = (kBudget / kRegsPerChunk) < 2 ? 2 : ((kBudget / kRegsPerChunk) > 8 ? 8 : kBudget / kRegsPerChunk);
+  static constexpr int kFit = kBudget / kRegsPerChunk;
+  static constexpr int PD = kFit < 2 ? 2 : (kFit > 8 ? 8 : (kFit & ~1));
 };
 
 template <bool BF16, int MW, int NW, bool STREAM, bool VEC, int NWV>
 __global__ void __launch_bounds__(64 * NWV) lstm_rec_kernel(const RecParams P) {
   typedef typename Dt<BF16>::T T;
   constexpr int KC = Dt<BF16>::KC;
-  constexpr int FQ = KC / 4;
   constexpr int PD = RecShape<MW, NW, STREAM>::PD;
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int s_ok;
@@ -136,7 +137,7 @@ __global__ void __launch_bounds__(64 * NWV) lstm_rec_kernel(const RecParams P) {
   const int nch = nch_u + nch_h;
   const bool vec = LY(vec_ok);
   const int q = lane >> 4;
-  Frag* As = reinterpret_cast<Frag*>(smem);
+  uint4* As = reinterpret_cast<uint4*>(smem);  // fragment block (m, c) at As + (m * nch + c) * 128
 
   // ---- keep this workgroup's weight rows on chip for the whole sequence
   if (!STREAM && LY(staged)) {
@@ -150,11 +151,11 @@ __global__ void __launch_bounds__(64 * NWV) lstm_rec_kernel(const RecParams P) {
       Frag fr = zero_frag();
       if (row >= 0) {
         if (c < nch_u)
-          fr = load_frag<BF16>(LY(W), Kin, row, c * KC + qq * FQ, Kin, vec);
+          fr = load_frag<BF16>(LY(W), Kin, row, c * KC, qq, Kin, vec);
         else
-          fr = load_frag<BF16>(LY(R), H, row, (c - nch_u) * KC + qq * FQ, H, vec);
+          fr = load_frag<BF16>(LY(R), H, row, (c - nch_u) * KC, qq, H, vec);
       }
-      As[f] = fr;
+      lds_put(As + (long)(f >> 6) * 128, ln, fr);
     }
     __syncthreads();
   }
@@ -162,13 +163,16 @@ __global__ void __launch_bounds__(64 * NWV) lstm_rec_kernel(const RecParams P) {
   // ---- per-wave tile bookkeeping
   bool mval[MW], nval[NW];
   int mloc[MW];
+  int mblk[MW];   // LDS block row of M-tile i, clamped to a valid one (reads stay unconditional)
   long arow[MW];  // caller weight row this lane loads for M-tile i (streamed weights; clamped)
   int unit[MW], bcol[NW];
-  long boff[NW];  // element offset of this lane's activation row (clamped to a valid row)
+  long boff[NW];  // element offset of this lane's row of h (clamped to a valid row)
+  long uoff[NW];  // ... and of its row of the fused input u (rows of Kin elements)
 #pragma unroll
   for (int i = 0; i < MW; ++i) {
     mloc[i] = gm + i * P.ntgm;
     mval[i] = i < P.mw && mloc[i] < mcnt;
+    mblk[i] = min(mloc[i], mcnt - 1);
     const long r = mval[i] ? tile_row(mt0 + mloc[i], lane & 15, H) : -1;
     arow[i] = VEC ? (r >= 0 ? r : 0) : r;
     unit[i] = 4 * (mt0 + mloc[i]) + q;
@@ -178,7 +182,8 @@ __global__ void __launch_bounds__(64 * NWV) lstm_rec_kernel(const RecParams P) {
     const int nloc = gn + j * P.ntgn;
     nval[j] = j < P.nw && nloc < P.ncnt;
     bcol[j] = 16 * nloc + (lane & 15);
-    boff[j] = (long)min(bcol[j], B - 1) * H;  // every activation row has H elements (I_l = H for l >= 1)
+    boff[j] = (long)min(bcol[j], B - 1) * H;
+    uoff[j] = (long)min(bcol[j], B - 1) * Kin;
   }
   auto fin = [&](int i, int j) { return ((i * P.nw + j) % ks) == kg; };
   auto live = [&](int i, int j) { return mval[i] && nval[j] && fin(i, j) && unit[i] < H && bcol[j] < B; };
@@ -260,7 +265,7 @@ __global__ void __launch_bounds__(64 * NWV) lstm_rec_kernel(const RecParams P) {
       for (int j = 0; j < NW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const T* hsrc = t > 0 ? Xp + (long)(t - 1) * slot : reinterpret_cast<const T*>(LY(h0));
-    const T* usrc = Kin ? Up + (long)t * slot : nullptr;
+    const T* usrc = Kin ? Up + (long)t * LY(u_slot) : nullptr;
 
     Frag rb[PD][NW];
     Frag ra[STREAM ? PD : 1][MW];
@@ -268,48 +273,43 @@ __global__ void __launch_bounds__(64 * NWV) lstm_rec_kernel(const RecParams P) {
     auto issue = [&](Frag (&b)[NW], Frag (&a)[MW], int c) {
       const bool is_u = c < nch_u;
       const int Kseg = is_u ? Kin : H;
-      const int kk = (is_u ? c : c - nch_u) * KC + q * FQ;
+      const int kk = (is_u ? c : c - nch_u) * KC;  // first column of the chunk
       const T* bsrc = is_u ? usrc : hsrc;
       const T* asrc = is_u ? Wp : Rp;
       if (VEC) {
 #pragma unroll
-        for (int j = 0; j < NW; ++j) b[j] = load_frag_vec(bsrc + boff[j] + kk);
+        for (int j = 0; j < NW; ++j) b[j] = load_frag_vec<BF16>(bsrc + (is_u ? uoff[j] : boff[j]) + kk, q);
         if (STREAM) {
 #pragma unroll
-          for (int i = 0; i < MW; ++i) a[i] = load_frag_vec(asrc + arow[i] * Kseg + kk);
+          for (int i = 0; i < MW; ++i) a[i] = load_frag_vec<BF16>(asrc + arow[i] * Kseg + kk, q);
         }
       } else {
 #pragma unroll
         for (int j = 0; j < NW; ++j)
-          if (nval[j]) b[j] = bcol[j] < B ? load_frag_off<BF16>(bsrc, (long)bcol[j] * Kseg, kk, Kseg, false) : zero_frag();
+          if (nval[j]) b[j] = bcol[j] < B ? load_frag_off<BF16>(bsrc, (long)bcol[j] * Kseg, kk, q, Kseg, false) : zero_frag();
         if (STREAM) {
 #pragma unroll
           for (int i = 0; i < MW; ++i)
-            if (mval[i]) a[i] = arow[i] >= 0 ? load_frag<BF16>(asrc, Kseg, arow[i], kk, Kseg, false) : zero_frag();
+            if (mval[i]) a[i] = arow[i] >= 0 ? load_frag<BF16>(asrc, Kseg, arow[i], kk, q, Kseg, false) : zero_frag();
         }
       }
     };
     // this wave's chunks of one part: c = c0 + ci * ks for ci < n
     auto products = [&](int c0, int n) {
-      // Weight fragments from LDS are read one chunk ahead (acur holds chunk
-      // ci's when compute(s, ci) starts), so their latency hides behind the MFMAs.
-      Frag acur[MW];
-      auto lds_a = [&](int ci) {
+      // Weight fragments from LDS are read one chunk ahead into the other of
+      // two buffers (chunk ci uses al[ci & 1], and ci & 1 == s & 1 because PD
+      // is even), so their latency hides behind the MFMAs and nothing is copied.
+      // The reads are unconditional (clamped tile rows): with no branch around
+      // them the compiler's LDS wait counts stay exact instead of draining.
+      Frag al[STREAM ? 1 : 2][MW];
+      auto lds_a = [&](Frag (&dst)[MW], int ci) {
         const int c = c0 + min(ci, n - 1) * ks;
 #pragma unroll
-        for (int i = 0; i < MW; ++i)
-          if (mval[i]) acur[i] = As[(mloc[i] * nch + c) * 64 + lane];
+        for (int i = 0; i < MW; ++i) dst[i] = lds_get(As + (mblk[i] * nch + c) * 128, lane);
       };
       auto compute = [&](int s, int ci) {
-        Frag a[MW];
-#pragma unroll
-        for (int i = 0; i < MW; ++i) {
-          if (STREAM)
-            a[i] = ra[STREAM ? s : 0][i];
-          else
-            a[i] = acur[i];
-        }
-        if (!STREAM) lds_a(ci + 1);
+        if (!STREAM) lds_a(al[STREAM ? 0 : ((s + 1) & 1)], ci + 1);
+        Frag (&a)[MW] = STREAM ? ra[STREAM ? s : 0] : al[STREAM ? 0 : (s & 1)];
 #pragma unroll
         for (int i = 0; i < MW; ++i)
 #pragma unroll
@@ -320,7 +320,7 @@ __global__ void __launch_bounds__(64 * NWV) lstm_rec_kernel(const RecParams P) {
         // burst: every chunk of this wave in flight at once
 #pragma unroll
         for (int s = 0; s < PD; ++s) issue(rb[s], ra[STREAM ? s : 0], c0 + min(s, n - 1) * ks);
-        if (!STREAM) lds_a(0);
+        if (!STREAM) lds_a(al[0], 0);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int s = 0; s < PD; ++s)
@@ -334,7 +334,7 @@ __global__ void __launch_bounds__(64 * NWV) lstm_rec_kernel(const RecParams P) {
         const int n_pad = (n + PD - 1) / PD * PD;
 #pragma unroll
         for (int s = 0; s < PD; ++s) issue(rb[s], ra[STREAM ? s : 0], c0 + s * ks);
-        if (!STREAM) lds_a(0);
+        if (!STREAM) lds_a(al[0], 0);
         __builtin_amdgcn_sched_barrier(0);
         for (int i0 = 0; i0 < n_pad; i0 += PD) {
 #pragma unroll

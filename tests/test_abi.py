@@ -106,9 +106,19 @@ def test_planner_on_mi355x_shape(name):
         assert not info.weights_on_chip  # 128 MiB per layer of R cannot stay in LDS
     if info.regime == 2:
         assert info.layers_per_launch == c.L
-        assert info.num_launches == 2
+        assert info.num_launches == 2  # clear + one recurrent launch: every input product fused
+        assert info.input_gemms == 0
+        assert len(set(info.mtiles_per_wg[:c.L])) == 1  # equal tiles per workgroup in every layer
     else:
         assert info.num_launches == 2 * c.L
+
+
+def test_planner_wavefront_falls_back_to_hoisted_first_layer():
+    # [W_0 | R_0] rows of a 4096-wide input do not fit one workgroup's LDS
+    info = sl.lstm_fwd_plan(sl.make_desc(2, 4096, 16, 4, 3, "f32"), 2, 256, 160 * 1024)
+    assert info.regime == 2 and info.input_gemms == 1 and info.num_launches == 2
+    info = sl.lstm_fwd_plan(sl.make_desc(2, 64, 16, 4, 3, "f32"), 2, 256, 160 * 1024)
+    assert info.regime == 2 and info.input_gemms == 0
 
 
 def test_planner_forced_regimes_and_small_devices():

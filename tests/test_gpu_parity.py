@@ -284,7 +284,29 @@ def test_gpu_launch_events(dev):
     opts.num_launches = ctypes.pointer(nl)
     prob.run(opts=opts)
     torch.cuda.synchronize()
-    assert nl.value == 2
-    assert list(kinds[:2]) == [sl.LSTM_KERNEL_INPUT_GEMM, sl.LSTM_KERNEL_RECURRENT]
+    plan = sl.lstm_fwd_plan(prob.desc).as_dict()
+    first = sl.LSTM_KERNEL_INPUT_GEMM if plan["input_gemms"] else sl.LSTM_KERNEL_CLEAR
+    assert nl.value == plan["num_launches"] == 2
+    assert list(kinds[:2]) == [first, sl.LSTM_KERNEL_RECURRENT]
     for k in range(2):
         assert evs[k].elapsed_time(evs[n + k]) > 0
+    # layerwise: input GEMM then recurrence, per layer
+    opts.force_regime = 1
+    prob.run(opts=opts)
+    torch.cuda.synchronize()
+    assert nl.value == 2 * cfg.L
+    assert list(kinds[:nl.value]) == [sl.LSTM_KERNEL_INPUT_GEMM, sl.LSTM_KERNEL_RECURRENT] * cfg.L
+
+
+def test_gpu_wavefront_with_hoisted_first_layer(dev):
+    """A first layer too wide to keep [W_0 | R_0] on chip: the wavefront hoists its
+    input product into the input GEMM and fuses only the layers above."""
+    import stacked_lstm_forward_amd as sl
+    cfg = li.custom_config(2, 4096, 16, 4, 3, "f32", cfg_id=79)
+    inp = li.make_inputs(cfg, random_state=True)
+    say("wavefront with hoisted layer 0 (I=4096, H=16)")
+    d = sl.make_desc(cfg.L, cfg.I, cfg.H, cfg.B, cfg.T, cfg.dtype)
+    plan = sl.lstm_fwd_plan(d, 2).as_dict()
+    assert plan["regime"] == "wavefront" and plan["input_gemms"] == 1
+    got = run_gpu(inp, dev, regime=2)
+    check_close(got, orc.lstm_forward_inputs(inp), TOL["f32"], "wavefront hoisted layer 0")
