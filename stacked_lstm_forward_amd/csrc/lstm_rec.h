@@ -88,7 +88,9 @@ __device__ __forceinline__ void store_coherent(typename Dt<BF16>::T* p, typename
 // MFMAs.  !VEC handles ragged sizes with per-element loads (slow, correct).
 // PD: chunks of loads in flight per wave, from a budget of 48 registers for the
 // ring (two waves share a SIMD, so a wave has at most 256 registers in all);
-// even, so that the two LDS weight buffers alternate with the ring slot.
+// even, so that the two LDS weight buffers alternate with the ring slot.  A
+// deeper ring measured slower: every wave's burst of loads at the start of a
+// step then queues in front of the first chunk everybody waits for.
 template <int MW, int NW, bool STREAM>
 struct RecShape {
   static constexpr int kRegsPerChunk = 8 * NW + (STREAM ? 8 * MW : 0);
