@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the stacked-LSTM forward pass.
+"""Seeded synthetic inputs for the stacked recurrent forward pass (LSTM, GRU, simple RNN).
 
 This module holds shapes, seeds, value distributions and storage formats only.
 It contains none of the LSTM arithmetic: both the fp64 CPU oracle (``oracle/``)
@@ -18,7 +18,8 @@ minibatch-32 question; "Persistent RNNs" on small batches):
 
 Distributions: W, R, b ~ U(-1/sqrt(H), 1/sqrt(H)); x ~ N(0, 1); h0 = c0 = 0
 unless a test asks for random initial states.  Gate blocks inside W, R, b are
-ordered i, f, g, o.
+ordered i, f, g, o (LSTM); r, z, n with bias blocks b_r, b_z, b_Wn, b_Rn
+(GRU); a simple RNN has one block.  Row counts per cell are in ``ROWS``.
 
 Seeds: ``np.random.default_rng([cfg_id, layer, tensor_id])`` with tensor_id
 W=0, R=1, b=2; x uses ``[cfg_id, 1000, 0]``; random h0/c0 use
@@ -37,6 +38,9 @@ from typing import Dict, List, Optional
 import numpy as np
 
 DTYPES = ("f32", "bf16")
+CELLS = ("lstm", "gru", "rnn_tanh", "rnn_relu")
+# (weight-row blocks, bias blocks) per cell, in multiples of H
+ROWS = {"lstm": (4, 4), "gru": (3, 4), "rnn_tanh": (1, 1), "rnn_relu": (1, 1)}
 
 
 @dataclass(frozen=True)
@@ -49,14 +53,20 @@ class Config:
     B: int
     T: int
     dtype: str
+    cell: str = "lstm"
+
+    @property
+    def gates(self) -> int:
+        return ROWS[self.cell][0]
 
     @property
     def flops(self) -> int:
-        """2 * 4H * (I_l + H) * B * T summed over layers (bias and pointwise work excluded)."""
+        """2 * G*H * (I_l + H) * B * T summed over layers, G = 4 (LSTM), 3 (GRU), 1 (RNN);
+        bias and pointwise work excluded."""
         tot = 0
         for l in range(self.L):
             il = self.I if l == 0 else self.H
-            tot += 2 * 4 * self.H * (il + self.H) * self.B * self.T
+            tot += 2 * self.gates * self.H * (il + self.H) * self.B * self.T
         return tot
 
 
@@ -69,10 +79,19 @@ CONFIGS: Dict[str, Config] = {
 }
 
 
-def custom_config(L: int, I: int, H: int, B: int, T: int, dtype: str, cfg_id: int = 99) -> Config:
+def custom_config(L: int, I: int, H: int, B: int, T: int, dtype: str, cfg_id: int = 99,
+                  cell: str = "lstm") -> Config:
     if dtype not in DTYPES:
         raise ValueError(f"dtype must be one of {DTYPES}")
-    return Config(f"L{L}I{I}H{H}B{B}T{T}{dtype}", cfg_id, L, I, H, B, T, dtype)
+    if cell not in CELLS:
+        raise ValueError(f"cell must be one of {CELLS}")
+    tag = "" if cell == "lstm" else cell
+    return Config(f"{tag}L{L}I{I}H{H}B{B}T{T}{dtype}", cfg_id, L, I, H, B, T, dtype, cell)
+
+
+def with_cell(cfg: Config, cell: str) -> Config:
+    """The same shapes and seeds with another cell."""
+    return Config(f"{cfg.name}-{cell}", cfg.cfg_id, cfg.L, cfg.I, cfg.H, cfg.B, cfg.T, cfg.dtype, cell)
 
 
 # ----------------------------------------------------------------------------- formats
@@ -117,8 +136,8 @@ def exact_f32(stored: np.ndarray, dtype: str) -> np.ndarray:
 class Inputs:
     """Storage-form tensors of one workload.
 
-    x: [T, B, I]; W[l]: [4H, I_l]; R[l]: [4H, H]; b[l]: [4H]; h0: [L, B, H] (dtype);
-    c0: [L, B, H] (always fp32).  Storage is float32 for "f32" and uint16 bf16 bits
+    x: [T, B, I]; W[l]: [G*H, I_l]; R[l]: [G*H, H]; b[l]: [NB*H] with (G, NB) = ROWS[cell];
+    h0: [L, B, H] (dtype); c0: [L, B, H] (always fp32, LSTM only).  Storage is float32 for "f32" and uint16 bf16 bits
     for "bf16".  h0 / c0 are None for zero initial states.
     """
 
@@ -152,7 +171,7 @@ class Inputs:
 
     # packed C-ABI layout
     def packed(self) -> Dict[str, Optional[np.ndarray]]:
-        """Contiguous arrays in the library's layout: W = W_0 ++ W_1 ++ ..., R = [L,4H,H], b = [L,4H]."""
+        """Contiguous arrays in the library's layout: W = W_0 ++ W_1 ++ ..., R = [L,G*H,H], b = [L,NB*H]."""
         return {
             "x": np.ascontiguousarray(self.x),
             "W": np.concatenate([w.reshape(-1) for w in self.W]),
@@ -166,7 +185,7 @@ class Inputs:
         """The same workload restricted to batch columns ``idx`` (sequences are independent)."""
         idx = np.asarray(idx)
         cfg = Config(self.cfg.name + "-sub", self.cfg.cfg_id, self.cfg.L, self.cfg.I, self.cfg.H,
-                     len(idx), self.cfg.T, self.cfg.dtype)
+                     len(idx), self.cfg.T, self.cfg.dtype, self.cfg.cell)
         return Inputs(cfg, np.ascontiguousarray(self.x[:, idx]), self.W, self.R, self.b,
                       None if self.h0 is None else np.ascontiguousarray(self.h0[:, idx]),
                       None if self.c0 is None else np.ascontiguousarray(self.c0[:, idx]),
@@ -184,13 +203,14 @@ def make_inputs(cfg: Config, random_state: bool = False, state_scale: float = 0.
     definition); True draws h0, c0 ~ U(-state_scale, state_scale) for tests.
     """
     L, I, H, B, T, dt = cfg.L, cfg.I, cfg.H, cfg.B, cfg.T, cfg.dtype
+    G, NB = ROWS[cfg.cell]
     bound = 1.0 / np.sqrt(H)
     W, R, b = [], [], []
     for l in range(L):
         il = I if l == 0 else H
-        W.append(to_storage(_uniform(np.random.default_rng([cfg.cfg_id, l, 0]), (4 * H, il), bound), dt))
-        R.append(to_storage(_uniform(np.random.default_rng([cfg.cfg_id, l, 1]), (4 * H, H), bound), dt))
-        b.append(to_storage(_uniform(np.random.default_rng([cfg.cfg_id, l, 2]), (4 * H,), bound), dt))
+        W.append(to_storage(_uniform(np.random.default_rng([cfg.cfg_id, l, 0]), (G * H, il), bound), dt))
+        R.append(to_storage(_uniform(np.random.default_rng([cfg.cfg_id, l, 1]), (G * H, H), bound), dt))
+        b.append(to_storage(_uniform(np.random.default_rng([cfg.cfg_id, l, 2]), (NB * H,), bound), dt))
     x = to_storage(np.random.default_rng([cfg.cfg_id, 1000, 0]).standard_normal((T, B, I)), dt)
     h0 = c0 = None
     if random_state:
@@ -205,13 +225,14 @@ def make_inputs(cfg: Config, random_state: bool = False, state_scale: float = 0.
 
 
 def from_arrays(L: int, I: int, H: int, B: int, T: int, dtype: str, x64, W64, R64, b64,
-                h064=None, c064=None) -> Inputs:
+                h064=None, c064=None, cell: str = "lstm") -> Inputs:
     """Build storage-form inputs from explicit fp64 arrays (structured pin inputs)."""
-    cfg = custom_config(L, I, H, B, T, dtype)
+    cfg = custom_config(L, I, H, B, T, dtype, cell=cell)
+    G, NB = ROWS[cell]
     x = to_storage(np.asarray(x64, dtype=np.float64).reshape(T, B, I), dtype)
-    W = [to_storage(np.asarray(W64[l], dtype=np.float64).reshape(4 * H, I if l == 0 else H), dtype) for l in range(L)]
-    R = [to_storage(np.asarray(R64[l], dtype=np.float64).reshape(4 * H, H), dtype) for l in range(L)]
-    b = [to_storage(np.asarray(b64[l], dtype=np.float64).reshape(4 * H), dtype) for l in range(L)]
+    W = [to_storage(np.asarray(W64[l], dtype=np.float64).reshape(G * H, I if l == 0 else H), dtype) for l in range(L)]
+    R = [to_storage(np.asarray(R64[l], dtype=np.float64).reshape(G * H, H), dtype) for l in range(L)]
+    b = [to_storage(np.asarray(b64[l], dtype=np.float64).reshape(NB * H), dtype) for l in range(L)]
     h0 = None if h064 is None else to_storage(np.asarray(h064, dtype=np.float64).reshape(L, B, H), dtype)
     c0 = None if c064 is None else np.asarray(c064, dtype=np.float64).reshape(L, B, H).astype(np.float32)
     return Inputs(cfg, x, W, R, b, h0, c0, {"structured": True})
