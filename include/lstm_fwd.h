@@ -13,7 +13,22 @@
  *     h_t = o * tanh(c_t)
  *
  * The four per-gate matrices are grouped into one 4H-row matrix per weight
- * (same page, proposed method: gate grouping).  How the library schedules the
+ * (same page, proposed method: gate grouping).
+ *
+ * The same page applies the method to GRU cells (three grouped matrices) and
+ * to the simple RNN (one matrix); desc.cell selects them, read as cuDNN v5's
+ * cells (the pages print their equations nowhere):
+ *   LSTM_CELL_GRU       W_l [3H][I_l], R_l [3H][H], gate blocks r, z, n;
+ *                       b_l [4H] = b_r, b_z, b_Wn, b_Rn
+ *                         r = sigmoid(W_r u + R_r h + b_r)
+ *                         z = sigmoid(W_z u + R_z h + b_z)
+ *                         n = tanh(W_n u + b_Wn + r * (R_n h + b_Rn))
+ *                         h_t = (1 - z) * n + z * h_{t-1}
+ *   LSTM_CELL_RNN_TANH  W_l [H][I_l], R_l [H][H], b_l [H]:  h_t = tanh(W u + R h + b)
+ *   LSTM_CELL_RNN_RELU  the same with max(0, .)
+ * These cells have no cell state: c0 and cT are ignored (may be NULL).  With
+ * G = 4, 3, 1 weight-row blocks and NB = 4, 4, 1 bias blocks, the layouts below
+ * read G*H for 4H in W and R and NB*H for 4H in b.  How the library schedules the
  * work (hoisted input projection, persistent recurrent kernel with weights kept
  * on chip -- "Persistent RNNs: Stashing Recurrent Weights On-Chip" -- and the
  * layer wavefront -- first page, proposed method: layer overlap) is not part of
@@ -58,10 +73,19 @@ extern "C" {
 
 typedef enum { LSTM_F32 = 0, LSTM_BF16 = 1 } lstm_dtype_t;
 
-/* Problem description.  L, I, H, B, T >= 1. dtype is an lstm_dtype_t. */
+/* Recurrent cell of every layer (0, the LSTM, when the field is left zeroed). */
+typedef enum {
+  LSTM_CELL_LSTM = 0,
+  LSTM_CELL_GRU = 1,
+  LSTM_CELL_RNN_TANH = 2,
+  LSTM_CELL_RNN_RELU = 3
+} lstm_cell_t;
+
+/* Problem description.  L, I, H, B, T >= 1. dtype is an lstm_dtype_t, cell an lstm_cell_t. */
 typedef struct {
   int32_t L, I, H, B, T;
   int32_t dtype;
+  int32_t cell;
 } lstm_desc_t;
 
 typedef enum {

@@ -30,6 +30,9 @@ LSTM_F32, LSTM_BF16 = 0, 1
 LSTM_OK, LSTM_ERR_INVALID_ARG, LSTM_ERR_UNSUPPORTED, LSTM_ERR_WORKSPACE, LSTM_ERR_HIP, LSTM_ERR_BARRIER_TIMEOUT = range(6)
 LSTM_REGIME_AUTO, LSTM_REGIME_LAYERWISE, LSTM_REGIME_WAVEFRONT = 0, 1, 2
 LSTM_KERNEL_INPUT_GEMM, LSTM_KERNEL_RECURRENT, LSTM_KERNEL_CLEAR = 1, 2, 3
+LSTM_CELL_LSTM, LSTM_CELL_GRU, LSTM_CELL_RNN_TANH, LSTM_CELL_RNN_RELU = range(4)
+CELL_IDS = {"lstm": LSTM_CELL_LSTM, "gru": LSTM_CELL_GRU, "rnn_tanh": LSTM_CELL_RNN_TANH,
+            "rnn_relu": LSTM_CELL_RNN_RELU}
 
 EXPORTED = ("lstm_fwd_workspace_size", "lstm_fwd", "lstm_fwd_ex", "lstm_status_string",
             "lstm_fwd_validate", "lstm_fwd_last_error", "lstm_fwd_plan")
@@ -37,7 +40,7 @@ EXPORTED = ("lstm_fwd_workspace_size", "lstm_fwd", "lstm_fwd_ex", "lstm_status_s
 
 class LstmDesc(ctypes.Structure):
     _fields_ = [("L", ctypes.c_int32), ("I", ctypes.c_int32), ("H", ctypes.c_int32),
-                ("B", ctypes.c_int32), ("T", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("B", ctypes.c_int32), ("T", ctypes.c_int32), ("dtype", ctypes.c_int32), ("cell", ctypes.c_int32)]
 
 
 class LstmOpts(ctypes.Structure):
@@ -123,9 +126,9 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream
 
 
-def make_desc(L: int, I: int, H: int, B: int, T: int, dtype) -> LstmDesc:
+def make_desc(L: int, I: int, H: int, B: int, T: int, dtype, cell="lstm") -> LstmDesc:
     dt = {"f32": LSTM_F32, "bf16": LSTM_BF16}.get(dtype, dtype)
-    return LstmDesc(L, I, H, B, T, dt)
+    return LstmDesc(L, I, H, B, T, dt, CELL_IDS.get(cell, cell))
 
 
 def lstm_status_string(status: int) -> str:

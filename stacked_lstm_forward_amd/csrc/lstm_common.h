@@ -129,6 +129,17 @@ __device__ __forceinline__ Frag load_frag(const void* base, long ld, long row, i
   return load_frag_off<BF16>(base, row * ld, k0, q, K, vec_ok);
 }
 
+// f &= mask on every 32-bit word (mask 0 zeroes a fragment without a branch)
+__device__ __forceinline__ void frag_mask(Frag& f, uint32_t m) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    f.v[h].x &= m;
+    f.v[h].y &= m;
+    f.v[h].z &= m;
+    f.v[h].w &= m;
+  }
+}
+
 // A block of 64 fragments in LDS, half-major: lane l's half h at [h * 64 + l].
 __device__ __forceinline__ void lds_put(uint4* blk, int lane, const Frag& f) {
   blk[lane] = f.v[0];
@@ -141,10 +152,44 @@ __device__ __forceinline__ Frag lds_get(const uint4* blk, int lane) {
   return f;
 }
 
-// Caller row of tile row rho of M-tile mt (gate-interleaved order); -1 past H.
-__device__ __forceinline__ long tile_row(int mt, int rho, int H) {
-  const int j = 4 * mt + (rho >> 2);
-  return j < H ? (long)(rho & 3) * H + j : -1;
+// Cells (lstm_cell_t).  LSTM and GRU tiles hold 4 units x 4 rows; the GRU's
+// four rows per unit are r, z, the input half of n and the recurrent half of
+// n, kept apart because the reset gate multiplies only the recurrent half
+// ("three matrix groups" with the n group split in two).  A simple-RNN tile
+// holds 16 units of one row each.
+constexpr int kCellLstm = 0, kCellGru = 1, kCellRnnTanh = 2, kCellRnnRelu = 3;
+
+__device__ __host__ __forceinline__ int cell_units_per_tile(int cell) { return cell >= kCellRnnTanh ? 16 : 4; }
+
+struct CellRow {
+  long w;  // input-weight row (-1: none -- past H, or the GRU's recurrent half of n)
+  long r;  // recurrent-weight row (-1: none -- past H, or the GRU's input half of n)
+  int bi;  // bias element (-1: past H)
+};
+
+// Rows behind tile row rho of M-tile mt (gate-interleaved order).
+__device__ __forceinline__ CellRow cell_row(int cell, int mt, int rho, int H) {
+  CellRow c{-1, -1, -1};
+  if (cell >= kCellRnnTanh) {
+    const int j = 16 * mt + rho;
+    if (j < H) c.w = c.r = c.bi = j;
+    return c;
+  }
+  const int j = 4 * mt + (rho >> 2), k = rho & 3;
+  if (j >= H) return c;
+  if (cell == kCellGru) {
+    if (k < 2) {
+      c.w = c.r = c.bi = (long)k * H + j;
+    } else if (k == 2) {
+      c.w = c.bi = 2L * H + j;  // W_n u + b_Wn
+    } else {
+      c.r = 2L * H + j;         // R_n h + b_Rn
+      c.bi = 3 * H + j;
+    }
+    return c;
+  }
+  c.w = c.r = c.bi = (long)k * H + j;
+  return c;
 }
 
 // Logistic function from its definition 1 / (1 + e^{-z}), with the hardware

@@ -64,6 +64,7 @@ lstm_status_t validate(const lstm_desc_t* d, const void* x, const void* W, const
   if (!d) return LSTM_ERR_INVALID_ARG;
   if (d->L < 1 || d->I < 1 || d->H < 1 || d->B < 1 || d->T < 1) return LSTM_ERR_INVALID_ARG;
   if (d->dtype != LSTM_F32 && d->dtype != LSTM_BF16) return LSTM_ERR_INVALID_ARG;
+  if (d->cell < LSTM_CELL_LSTM || d->cell > LSTM_CELL_RNN_RELU) return LSTM_ERR_INVALID_ARG;
   if (!x || !W || !R || !b || !y) return LSTM_ERR_INVALID_ARG;
   if (!ws) return LSTM_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return LSTM_ERR_WORKSPACE;
@@ -100,7 +101,7 @@ lstm_status_t lstm_fwd_plan(const lstm_desc_t* d, int32_t force_regime, int32_t 
     info = c.info;
   }
   Plan p;
-  const int rc = make_plan(d->L, d->I, d->H, d->B, d->T, d->dtype, force_regime, info, &p);
+  const int rc = make_plan(d->L, d->I, d->H, d->B, d->T, d->dtype, d->cell, force_regime, info, &p);
   if (rc) return (lstm_status_t)rc;
   *out = lstm_plan_info_t();
   out->regime = p.regime;
@@ -132,7 +133,7 @@ size_t lstm_fwd_workspace_size(const lstm_desc_t* d) {
   // the layout does not depend on the device; any partition fits the same buffers
   DeviceInfo info;
   Plan p;
-  if (make_plan(d->L, d->I, d->H, d->B, d->T, d->dtype, LSTM_REGIME_LAYERWISE, info, &p)) return 0;
+  if (make_plan(d->L, d->I, d->H, d->B, d->T, d->dtype, d->cell, LSTM_REGIME_LAYERWISE, info, &p)) return 0;
   return p.ws_bytes;
 }
 
@@ -164,7 +165,7 @@ lstm_status_t lstm_fwd_ex(const lstm_desc_t* d, const void* x, const void* h0, c
   if (st != LSTM_OK) return st;
   const int force = opts ? opts->force_regime : LSTM_REGIME_AUTO;
   Plan p;
-  const int rc = make_plan(d->L, d->I, d->H, d->B, d->T, d->dtype, force, dev.info, &p);
+  const int rc = make_plan(d->L, d->I, d->H, d->B, d->T, d->dtype, d->cell, force, dev.info, &p);
   if (rc) return (lstm_status_t)rc;
 
   const int L = d->L, I = d->I, H = d->H, B = d->B, T = d->T;
@@ -179,11 +180,13 @@ lstm_status_t lstm_fwd_ex(const lstm_desc_t* d, const void* x, const void* h0, c
   const char* Wb = static_cast<const char*>(W);
   const char* Rb = static_cast<const char*>(R);
   const char* bb = static_cast<const char*>(b);
+  const size_t ng = p.gates, nbias = p.bias_rows;  // row blocks of W/R and of b
   auto W_l = [&](int l) -> const void* {
-    return l == 0 ? Wb : Wb + ((size_t)4 * H * I + (size_t)(l - 1) * 4 * H * H) * ds;
+    return l == 0 ? Wb : Wb + (ng * H * I + (size_t)(l - 1) * ng * H * H) * ds;
   };
-  auto R_l = [&](int l) -> const void* { return Rb + (size_t)l * 4 * H * H * ds; };
-  auto b_l = [&](int l) -> const void* { return bb + (size_t)l * 4 * H * ds; };
+  auto R_l = [&](int l) -> const void* { return Rb + (size_t)l * ng * H * H * ds; };
+  auto b_l = [&](int l) -> const void* { return bb + (size_t)l * nbias * H * ds; };
+  if (p.cell != LSTM_CELL_LSTM) c0 = nullptr, cT = nullptr;  // no cell state
   auto xbuf = [&](int l) -> void* {  // layer l's exchange buffer: T slots of [B][H]
     return static_cast<void*>(hist + (size_t)l * T * slot * ds);
   };
@@ -226,6 +229,7 @@ lstm_status_t lstm_fwd_ex(const lstm_desc_t* d, const void* x, const void* h0, c
     gp.N = T * B;
     gp.vec_ok_w = aligned16(gp.W) && ((size_t)K * ds) % 16 == 0;
     gp.vec_ok_u = aligned16(U) && ((size_t)K * ds) % 16 == 0 && ((size_t)u_slot * ds) % 16 == 0;
+    gp.cell = p.cell;
     if (!before(LSTM_KERNEL_INPUT_GEMM)) return LSTM_ERR_HIP;
     if (launch_input_gemm(bf16, gp, stream) != hipSuccess) return LSTM_ERR_HIP;
     if (!after()) return LSTM_ERR_HIP;
@@ -238,6 +242,7 @@ lstm_status_t lstm_fwd_ex(const lstm_desc_t* d, const void* x, const void* h0, c
     rp.nlayers = lp.nlayers;
     rp.slot = (long long)slot;
     rp.T = T, rp.B = B, rp.H = H, rp.Mt = p.Mt, rp.ncnt = p.ncnt;
+    rp.cell = p.cell;
     rp.ks = lp.ks;
     rp.ntgm = lp.ntgm, rp.ntgn = lp.ntgn, rp.mw = lp.mw, rp.nw = lp.nw;
     rp.red_off = lp.red_off;

@@ -77,13 +77,15 @@ __global__ void __launch_bounds__(kGemmThreads) lstm_input_gemm(const GemmParams
 
   // staging slots of this thread: fragment f = tid + s * 256 of the A and B blocks
   long arow[NA];
+  uint32_t amask[NA];  // 0 where the tile row has no input-weight row (its fragment is zero)
   long boff[NB];
   bool bval[NB];
 #pragma unroll
   for (int s = 0; s < NA; ++s) {
     const int f = tid + s * kGemmThreads;
     const int mtl = f >> 6;
-    long r = (mtb + mtl < P.Mt) ? tile_row(mtb + mtl, f & 15, P.H) : -1;
+    long r = (mtb + mtl < P.Mt) ? cell_row(P.cell, mtb + mtl, f & 15, P.H).w : -1;
+    amask[s] = r >= 0 ? 0xffffffffu : 0u;
     if (VEC && r < 0) r = 0;
     arow[s] = r;
   }
@@ -110,7 +112,10 @@ __global__ void __launch_bounds__(kGemmThreads) lstm_input_gemm(const GemmParams
 #pragma unroll
     for (int s = 0; s < NB; ++s) rb[s] = gemm_load_b<BF16, VEC>(P, boff[s], bval[s], 0, q);
 #pragma unroll
-    for (int s = 0; s < NA; ++s) lds_put(lds + (tid / 64 + s * (kGemmThreads / 64)) * 128, lane, ra[s]);
+    for (int s = 0; s < NA; ++s) {
+      frag_mask(ra[s], amask[s]);
+      lds_put(lds + (tid / 64 + s * (kGemmThreads / 64)) * 128, lane, ra[s]);
+    }
 #pragma unroll
     for (int s = 0; s < NB; ++s) lds_put(lds + (MTW + tid / 64 + s * (kGemmThreads / 64)) * 128, lane, rb[s]);
     __syncthreads();
@@ -136,7 +141,10 @@ __global__ void __launch_bounds__(kGemmThreads) lstm_input_gemm(const GemmParams
     if (c + 1 < nch) {
       uint4* nx = lds + ((c + 1) & 1) * STAGE;
 #pragma unroll
-      for (int s = 0; s < NA; ++s) lds_put(nx + (tid / 64 + s * (kGemmThreads / 64)) * 128, lane, ra[s]);
+      for (int s = 0; s < NA; ++s) {
+        frag_mask(ra[s], amask[s]);
+        lds_put(nx + (tid / 64 + s * (kGemmThreads / 64)) * 128, lane, ra[s]);
+      }
 #pragma unroll
       for (int s = 0; s < NB; ++s) lds_put(nx + (MTW + tid / 64 + s * (kGemmThreads / 64)) * 128, lane, rb[s]);
     }
@@ -149,13 +157,13 @@ __global__ void __launch_bounds__(kGemmThreads) lstm_input_gemm(const GemmParams
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int mt = mtb + 8 * wm + i;
-    const int unit = 4 * mt + (lane >> 4);
-    if (mt >= P.Mt || unit >= P.H) continue;
-    f32x4 bv;
-    bv[0] = to_float(bias[0 * P.H + unit]);
-    bv[1] = to_float(bias[1 * P.H + unit]);
-    bv[2] = to_float(bias[2 * P.H + unit]);
-    bv[3] = to_float(bias[3 * P.H + unit]);
+    if (mt >= P.Mt) continue;
+    f32x4 bv;  // this lane's four rows 4*(lane/16) + k of the tile (rows past H are never read)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int bi = cell_row(P.cell, mt, 4 * (lane >> 4) + k, P.H).bi;
+      bv[k] = bi >= 0 ? to_float(bias[bi]) : 0.f;
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const long col = n0 + 16 * (4 * wn + j) + (lane & 15);

@@ -15,7 +15,7 @@ constexpr int kSlotAlign = 256;          // bytes: exchange slots never share a 
 
 // Input projection G = W_l U^T + b_l over all T*B columns (hoisted out of the recurrence).
 // Output layout [T][Mt][B][16] fp32: for step t, M-tile mt, batch b, the 16
-// gate-interleaved rows (unit 4*mt + rho/4, gate rho%4).
+// gate-interleaved rows of the tile (see cell_row).
 struct GemmParams {
   const void* W;     // [4H][K] (caller layout, gate blocks)
   const void* U;     // input sequence: step t, batch b at U + t*u_slot + b*K (elements)
@@ -26,6 +26,7 @@ struct GemmParams {
   int zero_count;
   int K, H, Mt, B, N;  // N = T*B
   int vec_ok_w, vec_ok_u;
+  int cell;            // lstm_cell_t
 };
 
 // One layer of a recurrent launch.
@@ -58,6 +59,7 @@ struct RecParams {
   long long slot;         // elements between two steps of an exchange buffer
   int nlayers;
   int T, B, H, Mt, ncnt;  // ncnt = ceil(B/16) column tiles
+  int cell;               // lstm_cell_t
   int ks;                 // waves splitting the K chunks of one tile (1, 2, 4 or 8)
   int ntgm, ntgn;         // tile groups: ntgm*ntgn = waves/ks; group g -> (g%ntgm, g/ntgm)
   int mw, nw;             // tiles per wave in M and N (<= the kernel's MW, NW)

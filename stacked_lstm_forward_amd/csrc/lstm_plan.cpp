@@ -179,17 +179,21 @@ bool plan_wavefront(int l0, int n, int Mt, int nch_h, int nch_x, int I, int H, b
 }  // namespace
 
 int make_plan(const int32_t L, const int32_t I, const int32_t H, const int32_t B, const int32_t T,
-              const int32_t dtype, int force_regime, const DeviceInfo& dev, Plan* out) {
+              const int32_t dtype, const int32_t cell, int force_regime, const DeviceInfo& dev, Plan* out) {
   if (L < 1 || I < 1 || H < 1 || B < 1 || T < 1) return kInvalid;
   if (dtype != 0 && dtype != 1) return kInvalid;
+  if (cell < 0 || cell > 3) return kInvalid;
   if (force_regime < kRegimeAuto || force_regime > kRegimeWavefront) return kInvalid;
   if (dev.num_cus < 1) return kInvalid;
   Plan& p = *out;
   p = Plan();
   p.bf16 = dtype == 1;
+  p.cell = cell;
+  p.gates = cell == 0 ? 4 : (cell == 1 ? 3 : 1);
+  p.bias_rows = cell <= 1 ? 4 : 1;
   p.KC = p.bf16 ? 64 : 32;
   p.dsize = p.bf16 ? 2 : 4;
-  p.Mt = cdiv(H, 4);
+  p.Mt = cdiv(H, cell >= 2 ? 16 : 4);  // 16-row tiles: 4 units x 4 rows, or 16 units x 1 row
   p.ncnt = cdiv(B, 16);
   if (p.ncnt > 16) return kUnsupported;                     // B > 256
   if ((long long)L > 64) return kUnsupported;

@@ -35,6 +35,9 @@ struct LaunchPlan {
 
 struct Plan {
   int regime = 0;       // lstm_regime_t
+  int cell = 0;         // lstm_cell_t
+  int gates = 4;        // weight-row blocks of H rows (4 LSTM, 3 GRU, 1 simple RNN)
+  int bias_rows = 4;    // bias blocks of H (4 LSTM, 4 GRU, 1 simple RNN)
   int bf16 = 0;
   int KC = 32;          // K columns per chunk
   int dsize = 4;
@@ -52,6 +55,6 @@ struct Plan {
 
 // Returns 0 on success, else an lstm_status_t.
 int make_plan(const int32_t L, const int32_t I, const int32_t H, const int32_t B, const int32_t T,
-              const int32_t dtype, int force_regime, const DeviceInfo& dev, Plan* out);
+              const int32_t dtype, const int32_t cell, int force_regime, const DeviceInfo& dev, Plan* out);
 
 }  // namespace lstm

@@ -139,6 +139,7 @@ __global__ void __launch_bounds__(64 * NWV) lstm_rec_kernel(const RecParams P) {
   const int nch = nch_u + nch_h;
   const bool vec = LY(vec_ok);
   const int q = lane >> 4;
+  const int cell = P.cell;
   uint4* As = reinterpret_cast<uint4*>(smem);  // fragment block (m, c) at As + (m * nch + c) * 128
 
   // ---- keep this workgroup's weight rows on chip for the whole sequence
@@ -148,14 +149,13 @@ __global__ void __launch_bounds__(64 * NWV) lstm_rec_kernel(const RecParams P) {
       const int ln = f & 63;
       const int c = (f >> 6) % nch;
       const int m = (f >> 6) / nch;
-      const long row = tile_row(mt0 + m, ln & 15, H);
+      const CellRow cr = cell_row(cell, mt0 + m, ln & 15, H);
       const int qq = ln >> 4;
       Frag fr = zero_frag();
-      if (row >= 0) {
-        if (c < nch_u)
-          fr = load_frag<BF16>(LY(W), Kin, row, c * KC, qq, Kin, vec);
-        else
-          fr = load_frag<BF16>(LY(R), H, row, (c - nch_u) * KC, qq, H, vec);
+      if (c < nch_u) {
+        if (cr.w >= 0) fr = load_frag<BF16>(LY(W), Kin, cr.w, c * KC, qq, Kin, vec);
+      } else {
+        if (cr.r >= 0) fr = load_frag<BF16>(LY(R), H, cr.r, (c - nch_u) * KC, qq, H, vec);
       }
       lds_put(As + (long)(f >> 6) * 128, ln, fr);
     }
@@ -167,7 +167,8 @@ __global__ void __launch_bounds__(64 * NWV) lstm_rec_kernel(const RecParams P) {
   int mloc[MW];
   int mblk[MW];   // LDS block row of M-tile i, clamped to a valid one (reads stay unconditional)
   long arow[MW];  // caller weight row this lane loads for M-tile i (streamed weights; clamped)
-  int unit[MW], bcol[NW];
+  uint32_t mw_[MW], mr_[MW];  // 0 where that row has no input / recurrent weights (streamed fragment zeroed)
+  int unit[MW], bcol[NW];     // first unit of this lane's rows; batch column
   long boff[NW];  // element offset of this lane's row of h (clamped to a valid row)
   long uoff[NW];  // ... and of its row of the fused input u (rows of Kin elements)
 #pragma unroll
@@ -175,9 +176,14 @@ __global__ void __launch_bounds__(64 * NWV) lstm_rec_kernel(const RecParams P) {
     mloc[i] = gm + i * P.ntgm;
     mval[i] = i < P.mw && mloc[i] < mcnt;
     mblk[i] = min(mloc[i], mcnt - 1);
-    const long r = mval[i] ? tile_row(mt0 + mloc[i], lane & 15, H) : -1;
+    const CellRow cr = cell_row(cell, mt0 + mloc[i], lane & 15, H);
+    const long r = mval[i] ? (cr.w >= 0 ? cr.w : cr.r) : -1;  // LSTM, RNN: w == r; GRU n: one of them
+    mw_[i] = (mval[i] && cr.w >= 0) ? 0xffffffffu : 0u;
+    mr_[i] = (mval[i] && cr.r >= 0) ? 0xffffffffu : 0u;
     arow[i] = VEC ? (r >= 0 ? r : 0) : r;
-    unit[i] = 4 * (mt0 + mloc[i]) + q;
+    // LSTM / GRU: the lane's four rows are the four rows of unit 4*mt + q;
+    // simple RNN: they are units 16*mt + 4*q + k, k = 0..3
+    unit[i] = cell >= kCellRnnTanh ? 16 * (mt0 + mloc[i]) + 4 * q : 4 * (mt0 + mloc[i]) + q;
   }
 #pragma unroll
   for (int j = 0; j < NW; ++j) {
@@ -190,21 +196,30 @@ __global__ void __launch_bounds__(64 * NWV) lstm_rec_kernel(const RecParams P) {
   auto fin = [&](int i, int j) { return ((i * P.nw + j) % ks) == kg; };
   auto live = [&](int i, int j) { return mval[i] && nval[j] && fin(i, j) && unit[i] < H && bcol[j] < B; };
 
-  // cell state (fp32, registers) and bias of fused-input layers
+  // per-lane state in registers, fp32: the LSTM's cell state c, the GRU's
+  // previous h (for z * h_{t-1}); and the bias of fused-input layers
   float creg[MW][NW];
   f32x4 breg[MW];
   const T* bias = reinterpret_cast<const T*>(LY(bias));
+  const T* h0p = reinterpret_cast<const T*>(LY(h0));
 #pragma unroll
   for (int i = 0; i < MW; ++i) {
     breg[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (Kin && mval[i] && unit[i] < H) {
+    if (Kin && mval[i]) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) breg[i][k] = to_float(bias[k * H + unit[i]]);
+      for (int k = 0; k < 4; ++k) {
+        const int bi = cell_row(cell, mt0 + mloc[i], 4 * q + k, H).bi;
+        if (bi >= 0) breg[i][k] = to_float(bias[bi]);
+      }
     }
 #pragma unroll
     for (int j = 0; j < NW; ++j) {
       creg[i][j] = 0.f;
-      if (LY(c0) && live(i, j)) creg[i][j] = LY(c0)[(long)bcol[j] * H + unit[i]];
+      if (live(i, j)) {
+        const long o = (long)bcol[j] * H + unit[i];
+        if (cell == kCellLstm && LY(c0)) creg[i][j] = LY(c0)[o];
+        if (cell == kCellGru && h0p) creg[i][j] = to_float(h0p[o]);
+      }
     }
   }
 
@@ -283,7 +298,10 @@ __global__ void __launch_bounds__(64 * NWV) lstm_rec_kernel(const RecParams P) {
         for (int j = 0; j < NW; ++j) b[j] = load_frag_vec<BF16>(bsrc + (is_u ? uoff[j] : boff[j]) + kk, q);
         if (STREAM) {
 #pragma unroll
-          for (int i = 0; i < MW; ++i) a[i] = load_frag_vec<BF16>(asrc + arow[i] * Kseg + kk, q);
+          for (int i = 0; i < MW; ++i) {
+            a[i] = load_frag_vec<BF16>(asrc + arow[i] * Kseg + kk, q);
+            frag_mask(a[i], is_u ? mw_[i] : mr_[i]);
+          }
         }
       } else {
 #pragma unroll
@@ -292,7 +310,10 @@ __global__ void __launch_bounds__(64 * NWV) lstm_rec_kernel(const RecParams P) {
         if (STREAM) {
 #pragma unroll
           for (int i = 0; i < MW; ++i)
-            if (mval[i]) a[i] = arow[i] >= 0 ? load_frag<BF16>(asrc, Kseg, arow[i], kk, q, Kseg, false) : zero_frag();
+            if (mval[i]) {
+              a[i] = arow[i] >= 0 ? load_frag<BF16>(asrc, Kseg, arow[i], kk, q, Kseg, false) : zero_frag();
+              frag_mask(a[i], is_u ? mw_[i] : mr_[i]);
+            }
         }
       }
     };
@@ -393,19 +414,33 @@ __global__ void __launch_bounds__(64 * NWV) lstm_rec_kernel(const RecParams P) {
       for (int j = 0; j < NW; ++j) {
         if (!live(i, j)) continue;
         const f32x4 p = acc[i][j] + (Gp ? gq[i][j] : breg[i]);
-        const float ig = sigmoid_f(p[0]);
-        const float fg = sigmoid_f(p[1]);
-        const float gg = tanh_f(p[2]);
-        const float og = sigmoid_f(p[3]);
-        const float cn = fg * creg[i][j] + ig * gg;
-        creg[i][j] = cn;
-        const T hv = from_float<BF16>(og * tanh_f(cn));
         const long o = (long)bcol[j] * H + unit[i];
-        store_coherent<BF16>(xout + o, hv);
-        if (yout) yout[o] = hv;
-        if (last) {
-          if (LY(hT)) reinterpret_cast<T*>(LY(hT))[o] = hv;
-          if (LY(cT)) LY(cT)[o] = cn;
+        auto emit = [&](long oo, float h) {  // h_t to the exchange slot, y and (last step) hT
+          const T hv = from_float<BF16>(h);
+          store_coherent<BF16>(xout + oo, hv);
+          if (yout) yout[oo] = hv;
+          if (last && LY(hT)) reinterpret_cast<T*>(LY(hT))[oo] = hv;
+        };
+        if (cell == kCellLstm) {
+          const float ig = sigmoid_f(p[0]);
+          const float fg = sigmoid_f(p[1]);
+          const float gg = tanh_f(p[2]);
+          const float og = sigmoid_f(p[3]);
+          const float cn = fg * creg[i][j] + ig * gg;
+          creg[i][j] = cn;
+          emit(o, og * tanh_f(cn));
+          if (last && LY(cT)) LY(cT)[o] = cn;
+        } else if (cell == kCellGru) {
+          const float rg = sigmoid_f(p[0]);
+          const float zg = sigmoid_f(p[1]);
+          const float ng = tanh_f(p[2] + rg * p[3]);
+          const float hn = (1.f - zg) * ng + zg * creg[i][j];
+          creg[i][j] = hn;
+          emit(o, hn);
+        } else {
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            if (unit[i] + k < H) emit(o + k, cell == kCellRnnRelu ? fmaxf(p[k], 0.f) : tanh_f(p[k]));
         }
       }
     stamp(t, 4);

@@ -1,5 +1,5 @@
 """Torch plumbing around the C ABI: device copies of host arrays, output and
-workspace allocation, and one call of ``lstm_fwd``.  No LSTM arithmetic here.
+workspace allocation, and one call of ``lstm_fwd``.  No cell arithmetic here.
 """
 from __future__ import annotations
 
@@ -55,8 +55,9 @@ class DeviceProblem:
         check(st, "lstm_fwd")
 
     def outputs_f32(self):
-        """(y, hT, cT) as float32 numpy arrays (synchronises)."""
-        return (self.y.float().cpu().numpy(), self.hT.float().cpu().numpy(), self.cT.float().cpu().numpy())
+        """(y, hT, cT) as float32 numpy arrays (synchronises); cT is None for cells without one."""
+        return (self.y.float().cpu().numpy(), self.hT.float().cpu().numpy(),
+                None if self.cT is None else self.cT.float().cpu().numpy())
 
 
 def workspace(desc: LstmDesc, device):
@@ -74,7 +75,8 @@ def prepare(inp, device="cuda:0") -> DeviceProblem:
     """Copy an ``lstm_inputs.Inputs`` to the device and allocate outputs and workspace."""
     torch = _torch()
     c = inp.cfg
-    desc = make_desc(c.L, c.I, c.H, c.B, c.T, c.dtype)
+    cell = getattr(c, "cell", "lstm")
+    desc = make_desc(c.L, c.I, c.H, c.B, c.T, c.dtype, cell)
     pk = inp.packed()
     tdt = torch.bfloat16 if c.dtype == "bf16" else torch.float32
     x = to_device_array(pk["x"], c.dtype, device)
@@ -85,7 +87,7 @@ def prepare(inp, device="cuda:0") -> DeviceProblem:
     c0 = None if pk["c0"] is None else torch.from_numpy(pk["c0"]).to(device)
     y = torch.empty((c.T, c.B, c.H), dtype=tdt, device=device)
     hT = torch.empty((c.L, c.B, c.H), dtype=tdt, device=device)
-    cT = torch.empty((c.L, c.B, c.H), dtype=torch.float32, device=device)
+    cT = torch.empty((c.L, c.B, c.H), dtype=torch.float32, device=device) if cell == "lstm" else None
     ws, n = workspace(desc, device)
     return DeviceProblem(desc, x, W, R, b, h0, c0, y, hT, cT, ws, n)
 
