@@ -111,11 +111,12 @@ __global__ void __launch_bounds__(kGemmThreads) lstm_input_gemm(const GemmParams
     for (int s = 0; s < NA; ++s) ra[s] = gemm_load_a<BF16, VEC>(P, arow[s], 0, q);
 #pragma unroll
     for (int s = 0; s < NB; ++s) rb[s] = gemm_load_b<BF16, VEC>(P, boff[s], bval[s], 0, q);
+    if (P.cell == kCellGru) {
 #pragma unroll
-    for (int s = 0; s < NA; ++s) {
-      frag_mask(ra[s], amask[s]);
-      lds_put(lds + (tid / 64 + s * (kGemmThreads / 64)) * 128, lane, ra[s]);
+      for (int s = 0; s < NA; ++s) frag_mask(ra[s], amask[s]);
     }
+#pragma unroll
+    for (int s = 0; s < NA; ++s) lds_put(lds + (tid / 64 + s * (kGemmThreads / 64)) * 128, lane, ra[s]);
 #pragma unroll
     for (int s = 0; s < NB; ++s) lds_put(lds + (MTW + tid / 64 + s * (kGemmThreads / 64)) * 128, lane, rb[s]);
     __syncthreads();
@@ -140,11 +141,12 @@ __global__ void __launch_bounds__(kGemmThreads) lstm_input_gemm(const GemmParams
     }
     if (c + 1 < nch) {
       uint4* nx = lds + ((c + 1) & 1) * STAGE;
+      if (P.cell == kCellGru) {  // rows with no input weights (the recurrent half of n)
 #pragma unroll
-      for (int s = 0; s < NA; ++s) {
-        frag_mask(ra[s], amask[s]);
-        lds_put(nx + (tid / 64 + s * (kGemmThreads / 64)) * 128, lane, ra[s]);
+        for (int s = 0; s < NA; ++s) frag_mask(ra[s], amask[s]);
       }
+#pragma unroll
+      for (int s = 0; s < NA; ++s) lds_put(nx + (tid / 64 + s * (kGemmThreads / 64)) * 128, lane, ra[s]);
 #pragma unroll
       for (int s = 0; s < NB; ++s) lds_put(nx + (MTW + tid / 64 + s * (kGemmThreads / 64)) * 128, lane, rb[s]);
     }
@@ -170,6 +172,141 @@ __global__ void __launch_bounds__(kGemmThreads) lstm_input_gemm(const GemmParams
       if (col >= P.N) continue;
       const long t = col / P.B, bb = col % P.B;
       float* dst = P.G + ((t * P.Mt + mt) * P.B + bb) * 16 + 4 * (lane >> 4);
+      *reinterpret_cast<f32x4*>(dst) = acc[i][j] + bv;
+    }
+  }
+}
+
+// Fast path of the input projection (K a whole number of chunks, every row
+// 16-byte aligned, no rows without input weights): a 256 x 256 workgroup
+// tile, 4 waves of 128 x 128 (8 x 8 MFMA tiles, accumulators in the
+// accumulation registers).  Operands go from global memory straight into LDS
+// with the gfx950 direct-to-LDS loads (each wave-wide 16-byte load fills one
+// 1 KiB half of a fragment block, lane l at byte 16*l -- the half-major block
+// layout), two stages deep: chunk c+1 streams in while chunk c is multiplied.
+// Per chunk a wave reads 32 KiB from LDS for 128 MFMAs (2 per tile, chained on
+// one accumulator, which keeps the matrix pipe issuing back to back).
+constexpr int kDmaTiles = 16;                    // M-tiles and column tiles per workgroup
+constexpr int kDmaStage = 2 * kDmaTiles * 128;   // 16-byte units per LDS stage (64 KiB)
+
+template <bool BF16>
+__global__ void __launch_bounds__(kGemmThreads) lstm_input_gemm_dma(const GemmParams P) {
+  typedef typename Dt<BF16>::T T;
+  typedef __attribute__((address_space(1))) const void* gptr_t;
+  typedef __attribute__((address_space(3))) void* lptr_t;
+  constexpr int KC = Dt<BF16>::KC;
+  extern __shared__ __align__(16) unsigned char gsmem[];
+  uint4* lds = reinterpret_cast<uint4*>(gsmem);
+
+  const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (P.zero_ptr) {  // grid-stride zeroing of the error word and step counters
+    const long nwg = (long)gridDim.x * gridDim.y;
+    const long wg = (long)blockIdx.y * gridDim.x + blockIdx.x;
+    for (long i = wg * kGemmThreads + tid; i < P.zero_count; i += nwg * kGemmThreads) P.zero_ptr[i] = 0;
+  }
+  // Tile order: the 1-D grid (a multiple of 8) goes round-robin over the 8
+  // XCDs, so workgroup ids are first regrouped into one contiguous range per
+  // XCD, and that range walks the (M, N) tile grid in groups of 4 M-blocks
+  // with N inner: the ~32 workgroups an XCD runs at once share 4 blocks of W
+  // rows and 8 blocks of U columns through their L2 instead of each pulling
+  // its own from memory.
+  const int nM = (P.Mt + kDmaTiles - 1) / kDmaTiles;
+  const int nN = (P.N + kDmaTiles * 16 - 1) / (kDmaTiles * 16);
+  const int total = nM * nN;
+  const int per_xcd = (int)gridDim.x >> 3;
+  const int v = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (v >= total) return;
+  constexpr int kGroupM = 4;
+  const int in_group = kGroupM * nN;
+  const int first_m = (v / in_group) * kGroupM;
+  const int gsize = min(nM - first_m, kGroupM);
+  const int mblk = first_m + (v % in_group) % gsize;
+  const int nblk = (v % in_group) / gsize;
+  const int mtb = mblk * kDmaTiles;                  // first M-tile
+  const long n0 = (long)nblk * kDmaTiles * 16;       // first column
+  const int nch = P.K / KC;
+
+  // staging: wave w fills fragment blocks 8w .. 8w+7 of every stage (blocks
+  // 0-15: the A tiles, W rows; 16-31: the B tiles, columns of U), both halves.
+  // Rows and columns past the end are clamped to valid ones (results unused).
+  const T* gbase = reinterpret_cast<const T*>(wave < 2 ? P.W : P.U);
+  long src[8];
+#pragma unroll
+  for (int s8 = 0; s8 < 8; ++s8) {
+    const int blk = 8 * wave + s8;
+    if (wave < 2) {
+      const int mt = mtb + blk;
+      long r = mt < P.Mt ? cell_row(P.cell, mt, lane & 15, P.H).w : -1;
+      src[s8] = (r < 0 ? 0 : r) * P.K;
+    } else {
+      long col = n0 + 16 * (blk - kDmaTiles) + (lane & 15);
+      col = col < P.N ? col : P.N - 1;
+      src[s8] = (col / P.B) * P.u_slot + (col % P.B) * P.K;  // column n: step n / B, sequence n % B
+    }
+  }
+  auto stage_load = [&](int c, int buf) {
+#pragma unroll
+    for (int s8 = 0; s8 < 8; ++s8)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const T* g = gbase + src[s8] + (long)c * KC + frag_col<BF16>(q, h);
+        uint4* l = lds + buf * kDmaStage + (8 * wave + s8) * 128 + h * 64;
+        __builtin_amdgcn_global_load_lds((gptr_t)g, (lptr_t)l, 16, 0, 0);
+      }
+  };
+
+  const int wm = wave & 1, wn = wave >> 1;
+  f32x4 acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (nch > 0) stage_load(0, 0);
+  for (int c = 0; c < nch; ++c) {
+    // this wave's loads of chunk c have landed (nothing else is outstanding);
+    // after the barrier everybody's have, and nobody still reads buffer (c+1)&1
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (c + 1 < nch) stage_load(c + 1, (c + 1) & 1);
+    // operand reads from LDS run two tile rows ahead of the MFMAs that use
+    // them (the scheduling barriers keep that order), so the matrix pipe starts
+    // after the B fragments and two A fragments instead of after all sixteen
+    const uint4* st = lds + (c & 1) * kDmaStage;
+    Frag a[8], b[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) b[j] = lds_get(st + (kDmaTiles + 8 * wn + j) * 128, lane);
+    a[0] = lds_get(st + (8 * wm + 0) * 128, lane);
+    a[1] = lds_get(st + (8 * wm + 1) * 128, lane);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i + 2 < 8) a[i + 2] = lds_get(st + (8 * wm + i + 2) * 128, lane);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mfma_frag<BF16>(acc[i][j], a[i], b[j]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // epilogue: add bias, write [T][Mt][B][16]
+  const T* bias = reinterpret_cast<const T*>(P.bias);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int mt = mtb + 8 * wm + i;
+    if (mt >= P.Mt) continue;
+    f32x4 bv;  // this lane's four rows 4*(lane/16) + k of the tile (rows past H are never read)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int bi = cell_row(P.cell, mt, 4 * q + k, P.H).bi;
+      bv[k] = bi >= 0 ? to_float(bias[bi]) : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const long col = n0 + 16 * (8 * wn + j) + (lane & 15);
+      if (col >= P.N) continue;
+      const long t = col / P.B, bb = col % P.B;
+      float* dst = P.G + ((t * P.Mt + mt) * P.B + bb) * 16 + 4 * q;
       *reinterpret_cast<f32x4*>(dst) = acc[i][j] + bv;
     }
   }
@@ -205,6 +342,21 @@ const void* rec_kernel_fn(bool bf16, bool stream, bool vec, int nwv, int mw, int
 
 hipError_t launch_input_gemm(bool bf16, const GemmParams& p, hipStream_t s) {
   constexpr int kMTW = kGemmTileM / 16, kNTW = kGemmTileN / 16;
+  const bool whole = (p.K % (bf16 ? Dt<true>::KC : Dt<false>::KC)) == 0;
+  // the 256 x 256 direct-to-LDS kernel pays off on long K (measured: 0.45 vs
+  // 0.53 ms at K = 4096, 0.33 vs 0.35 ms at K = 1536); short K keeps the
+  // register-staged 256 x 128 kernel, whose smaller tiles fill more CUs
+  if (p.vec_ok_w && p.vec_ok_u && whole && p.cell != kCellGru && p.K >= 1024) {
+    const unsigned lds = 2 * kDmaStage * sizeof(uint4);
+    const void* fn = bf16 ? reinterpret_cast<const void*>(&lstm_input_gemm_dma<true>)
+                          : reinterpret_cast<const void*>(&lstm_input_gemm_dma<false>);
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    const int tiles = ((p.N + kDmaTiles * 16 - 1) / (kDmaTiles * 16)) * ((p.Mt + kDmaTiles - 1) / kDmaTiles);
+    const dim3 grid((tiles + 7) & ~7);  // a multiple of the 8 XCDs (extra workgroups only help zeroing)
+    void* args[] = {const_cast<GemmParams*>(&p)};
+    return hipLaunchKernel(fn, grid, dim3(kGemmThreads), args, lds, s);
+  }
   const unsigned lds = 2 * (kMTW + kNTW) * 64 * sizeof(Frag);
   const dim3 grid((p.N + kGemmTileN - 1) / kGemmTileN, (p.Mt + kMTW - 1) / kMTW);
   const bool vec = p.vec_ok_w && p.vec_ok_u && (p.K % (bf16 ? Dt<true>::KC : Dt<false>::KC)) == 0;
