@@ -42,18 +42,19 @@ def log(msg: str) -> None:
 
 
 def kernel_flops(cfg, kind: int, plan: dict, launch_index: int) -> float:
-    """Algorithmic FLOPs of one launch (2 per multiply-add; bias and gate math excluded)."""
-    H, B, T, L, I = cfg.H, cfg.B, cfg.T, cfg.L, cfg.I
+    """Algorithmic FLOPs of one launch (2 per multiply-add; bias and gate math excluded).
+    G*H weight rows per matrix: G = 4 (LSTM), 3 (GRU), 1 (simple RNN)."""
+    H, B, T, L, I, G = cfg.H, cfg.B, cfg.T, cfg.L, cfg.I, cfg.gates
     if kind == 1:  # input GEMM of one layer; launch 0 is layer 0
         layer = 0 if plan["regime"] == "wavefront" else launch_index // 2
         il = I if layer == 0 else H
-        return 2.0 * 4 * H * il * B * T
+        return 2.0 * G * H * il * B * T
     if kind != 2:  # clearing the step counters
         return 0.0
     if plan["regime"] == "wavefront":  # R h for every layer + the fused W u products
         fused_in = (I + (L - 1) * H) if plan["input_gemms"] == 0 else (L - 1) * H
-        return 2.0 * 4 * H * H * B * T * L + 2.0 * 4 * H * fused_in * B * T
-    return 2.0 * 4 * H * H * B * T  # layerwise: one layer's recurrence
+        return 2.0 * G * H * H * B * T * L + 2.0 * G * H * fused_in * B * T
+    return 2.0 * G * H * H * B * T  # layerwise: one layer's recurrence
 
 
 def kernel_source_digest() -> str:
@@ -118,6 +119,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="c2", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--cell", default="lstm", choices=["lstm", "gru", "rnn_tanh", "rnn_relu"],
+                    help="recurrent cell at the workload's shapes (the headline metric is the LSTM)")
     ap.add_argument("--regime", type=int, default=0, help="0 auto, 1 layerwise, 2 wavefront")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -157,11 +160,14 @@ def main() -> int:
         return 0
     sl.load_library()
     cfg = li.CONFIGS[args.config]
-    log(f"workload {cfg.name}: {WORKLOAD_TEXT[cfg.name]}; generating inputs")
+    workload = WORKLOAD_TEXT[cfg.name]
+    if args.cell != "lstm":
+        cfg = li.with_cell(cfg, args.cell)
+        workload = workload.replace("LSTM", args.cell.upper().replace("_", "-"))
+    log(f"workload {cfg.name}: {workload}; generating inputs")
     inp = li.make_inputs(cfg)
     prob = runner.prepare(inp, "cuda:0")
     plan = sl.lstm_fwd_plan(prob.desc, args.regime).as_dict()
-    regime = 2 if plan["regime"] == "wavefront" else 1
     log(f"plan {plan}")
 
     stream = torch.cuda.current_stream()
@@ -202,10 +208,15 @@ def main() -> int:
     log(f"warm-up done ({args.warmup} steps); timing {args.steps} steps")
 
     t_start, t_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    step_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    for e in step_ev:
+        e.record(stream)
     torch.cuda.synchronize()
     t_start.record(stream)
+    step_ev[0].record(stream)
     for k in range(args.steps):
         prob.run(stream, opts_list[k])
+        step_ev[k + 1].record(stream)
     t_stop.record(stream)
     torch.cuda.synchronize()
     st = sl.lstm_fwd_last_error(prob.ws, stream)
@@ -214,6 +225,9 @@ def main() -> int:
         return 1
     total_ms = t_start.elapsed_time(t_stop)
     ms_step = total_ms / args.steps
+    per_step = sorted(step_ev[k].elapsed_time(step_ev[k + 1]) for k in range(args.steps))
+    ms_median = per_step[len(per_step) // 2] if len(per_step) % 2 else 0.5 * (
+        per_step[len(per_step) // 2 - 1] + per_step[len(per_step) // 2])
 
     # per-kernel durations from the library's launch events
     per_kind: dict = {}
@@ -233,7 +247,7 @@ def main() -> int:
     value = cfg.flops / (ms_step * 1e-3) / 1e12
     y, hT, cT = prob.outputs_f32()
     import numpy as np
-    if not (np.all(np.isfinite(y)) and np.all(np.isfinite(cT))):
+    if not (np.all(np.isfinite(y)) and np.all(np.isfinite(hT)) and (cT is None or np.all(np.isfinite(cT)))):
         print("non-finite outputs", file=sys.stderr)
         return 1
     log(f"{ms_step:.4f} ms/step, {value:.2f} TFLOP/s; dominant kernel kind {dom}: {dom_ms:.4f} ms/launch")
@@ -252,13 +266,15 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
+        "ms_per_step_median": round(ms_median, 5),
+        "ms_per_step_min": round(per_step[0], 5),
         "ms_per_sequence": round(ms_step / cfg.B, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32" if cfg.dtype == "f32" else "bf16",
         "data": "synthetic (seeded: W,R,b ~ U(-1/sqrt(H),1/sqrt(H)), x ~ N(0,1), h0=c0=0)",
-        "config": {"workload": WORKLOAD_TEXT[cfg.name], "L": cfg.L, "I": cfg.I, "H": cfg.H, "B": cfg.B,
+        "config": {"workload": workload, "cell": cfg.cell, "L": cfg.L, "I": cfg.I, "H": cfg.H, "B": cfg.B,
                    "T": cfg.T, "regime": plan["regime"], "gflop_per_step": round(cfg.flops / 1e9, 3)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4),
