@@ -188,7 +188,8 @@ typedef struct {
   int32_t block;             /* threads per workgroup of the recurrent kernel                  */
   int32_t lds_bytes;         /* dynamic LDS per workgroup of the recurrent kernel              */
   int32_t ksplit;            /* waves that split the K dimension of one output tile            */
-  int32_t weights_on_chip;   /* 1 if every recurrent workgroup keeps its weight rows in LDS    */
+  int32_t weights_on_chip;   /* 1 if every recurrent workgroup keeps its weight rows on chip for
+                                the whole sequence (in LDS, or in LDS plus registers)         */
   int32_t layers_per_launch; /* layers one recurrent launch runs concurrently                  */
   int32_t wg_per_layer[16];  /* workgroups given to each layer of the first recurrent launch   */
   int32_t mtiles_per_wg[16]; /* 16-row tiles (4 units x 4 gates) per workgroup, per layer      */
@@ -199,6 +200,8 @@ typedef struct {
   int32_t weights_streamed;  /* 1 if the first recurrent launch reads weights from HBM per step */
   int32_t input_gemms;       /* input-projection GEMM launches per call; 0 when every layer's
                                 input product W_l u_t is fused into its recurrent steps          */
+  int32_t weight_blocks_in_registers; /* 2 KiB weight blocks each wave of the first recurrent
+                                launch keeps in registers (0: weights in LDS only, or streamed) */
 } lstm_plan_info_t;
 
 /*

@@ -58,7 +58,8 @@ class PlanInfo(ctypes.Structure):
                 ("wg_per_layer", ctypes.c_int32 * 16), ("mtiles_per_wg", ctypes.c_int32 * 16),
                 ("tile_groups_m", ctypes.c_int32), ("tile_groups_n", ctypes.c_int32),
                 ("wave_tiles_m", ctypes.c_int32), ("wave_tiles_n", ctypes.c_int32),
-                ("weights_streamed", ctypes.c_int32), ("input_gemms", ctypes.c_int32)]
+                ("weights_streamed", ctypes.c_int32), ("input_gemms", ctypes.c_int32),
+                ("weight_blocks_in_registers", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
         n = self.layers_per_launch
@@ -69,7 +70,8 @@ class PlanInfo(ctypes.Structure):
                 "mtiles_per_wg": list(self.mtiles_per_wg[:n]),
                 "tile_groups": [self.tile_groups_m, self.tile_groups_n],
                 "wave_tiles": [self.wave_tiles_m, self.wave_tiles_n],
-                "weights_streamed": bool(self.weights_streamed), "input_gemms": self.input_gemms}
+                "weights_streamed": bool(self.weights_streamed), "input_gemms": self.input_gemms,
+                "weight_blocks_in_registers": self.weight_blocks_in_registers}
 
 
 class LstmError(RuntimeError):

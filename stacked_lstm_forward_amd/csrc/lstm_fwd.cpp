@@ -21,6 +21,8 @@ hipError_t rec_prepare(bool bf16, bool stream, bool vec, int nwv, int mw, int nw
 hipError_t launch_clear(int* p, long long n, hipStream_t s);
 hipError_t launch_rec(bool bf16, bool stream, bool vec, int nwv, const RecParams& p, int lds_bytes, bool plain,
                       hipStream_t s);
+hipError_t res_prepare(bool bf16, int mw, int nw, int nci, int nrb, int lds_bytes, int* max_blocks_per_cu);
+hipError_t launch_rec_res(bool bf16, int nci, int nrb, const RecParams& p, int lds_bytes, bool plain, hipStream_t s);
 }  // namespace lstm
 
 using namespace lstm;
@@ -125,6 +127,7 @@ lstm_status_t lstm_fwd_plan(const lstm_desc_t* d, int32_t force_regime, int32_t 
   out->wave_tiles_n = p.rec[0].nw;
   out->weights_streamed = p.rec[0].stream;
   out->input_gemms = p.ngemm;
+  out->weight_blocks_in_registers = p.rec[0].res_nrb;
   return LSTM_OK;
 }
 
@@ -165,7 +168,8 @@ lstm_status_t lstm_fwd_ex(const lstm_desc_t* d, const void* x, const void* h0, c
   if (st != LSTM_OK) return st;
   const int force = opts ? opts->force_regime : LSTM_REGIME_AUTO;
   Plan p;
-  const int rc = make_plan(d->L, d->I, d->H, d->B, d->T, d->dtype, d->cell, force, dev.info, &p);
+  const int rc = make_plan(d->L, d->I, d->H, d->B, d->T, d->dtype, d->cell, force, dev.info, &p,
+                           aligned16(R) && (!h0 || aligned16(h0)));
   if (rc) return (lstm_status_t)rc;
 
   const int L = d->L, I = d->I, H = d->H, B = d->B, T = d->T;
@@ -290,12 +294,17 @@ lstm_status_t lstm_fwd_ex(const lstm_desc_t* d, const void* x, const void* h0, c
     bool vec = (H % p.KC) == 0;
     for (int k = 0; k < lp.nlayers; ++k) vec = vec && rp.layer[k].vec_ok;
     int per_cu = 0;
-    if (rec_prepare(bf16, lp.stream, vec, lp.nwaves, lp.mw, lp.nw, lp.lds_bytes, &per_cu) != hipSuccess)
-      return LSTM_ERR_HIP;
+    const bool res = lp.res_nrb > 0;
+    if (res && !vec) return LSTM_ERR_UNSUPPORTED;  // planned only for aligned whole-chunk rows
+    const hipError_t pe = res ? res_prepare(bf16, lp.mw, lp.nw, lp.res_nci, lp.res_nrb, lp.lds_bytes, &per_cu)
+                              : rec_prepare(bf16, lp.stream, vec, lp.nwaves, lp.mw, lp.nw, lp.lds_bytes, &per_cu);
+    if (pe != hipSuccess) return LSTM_ERR_HIP;
     if ((long long)per_cu * dev.info.num_cus < lp.grid) return LSTM_ERR_UNSUPPORTED;  // not co-resident
     if (!before(LSTM_KERNEL_RECURRENT)) return LSTM_ERR_HIP;
     const bool plain = opts && opts->plain_launch;
-    if (launch_rec(bf16, lp.stream, vec, lp.nwaves, rp, lp.lds_bytes, plain, stream) != hipSuccess) return LSTM_ERR_HIP;
+    const hipError_t le = res ? launch_rec_res(bf16, lp.res_nci, lp.res_nrb, rp, lp.lds_bytes, plain, stream)
+                              : launch_rec(bf16, lp.stream, vec, lp.nwaves, rp, lp.lds_bytes, plain, stream);
+    if (le != hipSuccess) return LSTM_ERR_HIP;
     if (!after()) return LSTM_ERR_HIP;
     return LSTM_OK;
   };

@@ -329,6 +329,8 @@ LSTM_DECL(f32, lds, 4) LSTM_DECL(f32, stream, 4) LSTM_DECL(bf16, lds, 4) LSTM_DE
 LSTM_DECL(f32, lds, 8) LSTM_DECL(f32, stream, 8) LSTM_DECL(bf16, lds, 8) LSTM_DECL(bf16, stream, 8)
 #undef LSTM_DECL
 
+const void* rec_res_kernel_ptr(bool bf16, int mw, int nw, int nci, int nrb);
+
 namespace {
 const void* rec_kernel_fn(bool bf16, bool stream, bool vec, int nwv, int mw, int nw) {
   if (nwv == 8) {
@@ -386,6 +388,22 @@ hipError_t rec_prepare(bool bf16, bool stream, bool vec, int nwv, int mw, int nw
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
   if (e != hipSuccess) return e;
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(max_blocks_per_cu, fn, 64 * nwv, lds_bytes);
+}
+
+hipError_t res_prepare(bool bf16, int mw, int nw, int nci, int nrb, int lds_bytes, int* max_blocks_per_cu) {
+  const void* fn = rec_res_kernel_ptr(bf16, mw, nw, nci, nrb);
+  if (!fn) return hipErrorInvalidValue;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+  if (e != hipSuccess) return e;
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(max_blocks_per_cu, fn, 64 * 4, lds_bytes);
+}
+
+hipError_t launch_rec_res(bool bf16, int nci, int nrb, const RecParams& p, int lds_bytes, bool plain, hipStream_t s) {
+  const void* fn = rec_res_kernel_ptr(bf16, p.mw, p.nw, nci, nrb);
+  if (!fn) return hipErrorInvalidValue;
+  void* args[] = {const_cast<RecParams*>(&p)};
+  if (plain) return hipLaunchKernel(fn, dim3(p.grid), dim3(64 * 4), args, (unsigned)lds_bytes, s);
+  return hipLaunchCooperativeKernel(fn, dim3(p.grid), dim3(64 * 4), args, (unsigned)lds_bytes, s);
 }
 
 hipError_t launch_rec(bool bf16, bool stream, bool vec, int nwv, const RecParams& p, int lds_bytes, bool plain,

@@ -12,6 +12,10 @@ constexpr int kGemmThreads = 256;
 constexpr int kGemmTileM = 256;          // rows (16 M-tiles) per input-GEMM workgroup
 constexpr int kGemmTileN = 128;          // columns (time x batch) per input-GEMM workgroup
 constexpr int kSlotAlign = 256;          // bytes: exchange slots never share a cache line
+// Register-resident recurrent kernel (one layer, weights in registers + LDS):
+// 4 waves = 4 K-groups, kResMW M-tiles per workgroup, kResNCI chunks per
+// K-group, kResNRB of each wave's kResMW * kResNCI blocks in registers.
+constexpr int kResMW = 4, kResNCI = 16, kResNRB = 48;
 
 // Input projection G = W_l U^T + b_l over all T*B columns (hoisted out of the recurrence).
 // Output layout [T][Mt][B][16] fp32: for step t, M-tile mt, batch b, the 16

@@ -78,8 +78,26 @@ bool choose_split(int mmax, int ncnt, int staged_bytes, int lds_limit, int nwave
 
 int round_grid(int g) { return (g + 7) & ~7; }
 
+// Register-resident launch of one layer: the weight rows stay on chip, split
+// between the registers and the LDS of each workgroup.  Only the bf16 shape
+// the kernel is instantiated for: 4 M-tiles per workgroup, 4 K-groups of
+// exactly kResNCI chunks each (H = 4096), at most two 16-column batch tiles.
+bool plan_resident(int m, int nch, int ncnt, bool bf16, bool aligned, const DeviceInfo& dev, LaunchPlan* lp) {
+  if (!bf16 || !aligned || m > kResMW || nch != 4 * kResNCI || ncnt > 2) return false;
+  const int nlb = kResMW * kResNCI - kResNRB;  // LDS blocks per wave
+  const int red = kResMW * 4 * 64 * 16;        // one 1 KiB partial per (M-tile, K-group)
+  const int red_off = 4 * nlb * 64 * kFragBytes;
+  if (red_off + red + kLdsReserve > dev.lds_per_block) return false;
+  lp->res_nrb = kResNRB, lp->res_nci = kResNCI;
+  lp->nwaves = 4, lp->ks = 4, lp->ntgm = 1, lp->ntgn = 1, lp->mw = kResMW, lp->nw = ncnt;
+  lp->red_off = red_off, lp->lds_bytes = red_off + red;
+  lp->stream = 0;
+  return true;
+}
+
 // Single-layer persistent launch (hoisted input).
-bool plan_single(int layer, int Mt, int nch, int ncnt, const DeviceInfo& dev, LaunchPlan* lp) {
+bool plan_single(int layer, int Mt, int nch, int ncnt, bool bf16, bool aligned, const DeviceInfo& dev,
+                 LaunchPlan* lp) {
   const int gmax = dev.num_cus;
   int m = std::max(1, cdiv(Mt, gmax));
   if (m > 16) return false;
@@ -94,6 +112,8 @@ bool plan_single(int layer, int Mt, int nch, int ncnt, const DeviceInfo& dev, La
   if (choose_split(m, ncnt, staged_bytes, dev.lds_per_block, 4, lp)) {
     L.staged = 1;
     lp->stream = 0;
+  } else if (plan_resident(m, nch, ncnt, bf16, aligned, dev, lp)) {
+    L.staged = 1;
   } else if (choose_split(m, ncnt, 0, dev.lds_per_block, 4, lp)) {
     L.staged = 0;
     lp->stream = 1;
@@ -179,7 +199,8 @@ bool plan_wavefront(int l0, int n, int Mt, int nch_h, int nch_x, int I, int H, b
 }  // namespace
 
 int make_plan(const int32_t L, const int32_t I, const int32_t H, const int32_t B, const int32_t T,
-              const int32_t dtype, const int32_t cell, int force_regime, const DeviceInfo& dev, Plan* out) {
+              const int32_t dtype, const int32_t cell, int force_regime, const DeviceInfo& dev, Plan* out,
+              bool aligned) {
   if (L < 1 || I < 1 || H < 1 || B < 1 || T < 1) return kInvalid;
   if (dtype != 0 && dtype != 1) return kInvalid;
   if (cell < 0 || cell > 3) return kInvalid;
@@ -231,7 +252,8 @@ int make_plan(const int32_t L, const int32_t I, const int32_t H, const int32_t B
     p.ngemm = L;
     p.nclear = 0;
     for (int l = 0; l < L; ++l)
-      if (!plan_single(l, p.Mt, nch_h, p.ncnt, dev, &p.rec[l])) return kUnsupported;
+      if (!plan_single(l, p.Mt, nch_h, p.ncnt, p.bf16 != 0, aligned && (H % p.KC) == 0, dev, &p.rec[l]))
+        return kUnsupported;
   }
   p.regime = wave ? kRegimeWavefront : kRegimeLayerwise;
   p.num_launches = p.nrec + p.ngemm + p.nclear;

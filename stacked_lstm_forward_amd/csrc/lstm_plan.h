@@ -27,6 +27,8 @@ struct LaunchPlan {
   int nlayers = 0;
   LayerPlan layers[kMaxLayersPerLaunch];
   int stream = 0;       // 1: weight rows streamed from global memory every step
+  int res_nrb = 0;      // > 0: register-resident kernel; weight blocks per wave in registers
+  int res_nci = 0;      // ... and chunks per wave (K-group)
   int nwaves = 4;       // waves per workgroup (4: one per SIMD, 8: two per SIMD)
   int ks = 4, ntgm = 1, ntgn = 1, mw = 1, nw = 1;
   int lds_bytes = 0, red_off = 0;
@@ -54,7 +56,10 @@ struct Plan {
 };
 
 // Returns 0 on success, else an lstm_status_t.
+// `aligned`: the caller's R (and h0) allow 16-byte loads; the register-resident
+// kernel needs it.
 int make_plan(const int32_t L, const int32_t I, const int32_t H, const int32_t B, const int32_t T,
-              const int32_t dtype, const int32_t cell, int force_regime, const DeviceInfo& dev, Plan* out);
+              const int32_t dtype, const int32_t cell, int force_regime, const DeviceInfo& dev, Plan* out,
+              bool aligned = true);
 
 }  // namespace lstm

@@ -71,6 +71,36 @@ __device__ __forceinline__ void store_coherent(typename Dt<BF16>::T* p, typename
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// One lane's gate non-linearities and state update.  p holds the lane's four
+// pre-activation rows of its tile (LSTM: i, f, g, o of one unit; GRU: r, z and
+// the input and recurrent halves of n; simple RNN: four consecutive units).
+// `st` is the lane's fp32 state: the LSTM's cell c, the GRU's h_{t-1}; unused
+// by the simple RNN.  emit(k, h) receives the new hidden value of the lane's
+// unit + k (k = 0 except for the simple RNN, which emits min(4, left) units).
+template <class Emit>
+__device__ __forceinline__ void cell_update(int cell, const f32x4 p, float& st, int left, Emit&& emit) {
+  if (cell == kCellLstm) {
+    const float ig = sigmoid_f(p[0]);
+    const float fg = sigmoid_f(p[1]);
+    const float gg = tanh_f(p[2]);
+    const float og = sigmoid_f(p[3]);
+    const float cn = fg * st + ig * gg;
+    st = cn;
+    emit(0, og * tanh_f(cn));
+  } else if (cell == kCellGru) {
+    const float rg = sigmoid_f(p[0]);
+    const float zg = sigmoid_f(p[1]);
+    const float ng = tanh_f(p[2] + rg * p[3]);
+    const float hn = (1.f - zg) * ng + zg * st;
+    st = hn;
+    emit(0, hn);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (k < left) emit(k, cell == kCellRnnRelu ? fmaxf(p[k], 0.f) : tanh_f(p[k]));
+  }
+}
+
 // ----------------------------------------------------------------------------
 // Persistent recurrence (optionally several layers as a wavefront)
 // ----------------------------------------------------------------------------
@@ -421,27 +451,8 @@ __global__ void __launch_bounds__(64 * NWV) lstm_rec_kernel(const RecParams P) {
           if (yout) yout[oo] = hv;
           if (last && LY(hT)) reinterpret_cast<T*>(LY(hT))[oo] = hv;
         };
-        if (cell == kCellLstm) {
-          const float ig = sigmoid_f(p[0]);
-          const float fg = sigmoid_f(p[1]);
-          const float gg = tanh_f(p[2]);
-          const float og = sigmoid_f(p[3]);
-          const float cn = fg * creg[i][j] + ig * gg;
-          creg[i][j] = cn;
-          emit(o, og * tanh_f(cn));
-          if (last && LY(cT)) LY(cT)[o] = cn;
-        } else if (cell == kCellGru) {
-          const float rg = sigmoid_f(p[0]);
-          const float zg = sigmoid_f(p[1]);
-          const float ng = tanh_f(p[2] + rg * p[3]);
-          const float hn = (1.f - zg) * ng + zg * creg[i][j];
-          creg[i][j] = hn;
-          emit(o, hn);
-        } else {
-#pragma unroll
-          for (int k = 0; k < 4; ++k)
-            if (unit[i] + k < H) emit(o + k, cell == kCellRnnRelu ? fmaxf(p[k], 0.f) : tanh_f(p[k]));
-        }
+        cell_update(cell, p, creg[i][j], H - unit[i], [&](int k, float h) { emit(o + k, h); });
+        if (cell == kCellLstm && last && LY(cT)) LY(cT)[o] = creg[i][j];
       }
     stamp(t, 4);
 

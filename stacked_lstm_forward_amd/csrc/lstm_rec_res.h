@@ -1,0 +1,220 @@
+// Persistent recurrent kernel of one layer whose recurrent weights do not fit
+// in LDS but do fit in LDS plus the register file (template definitions;
+// instantiated by lstm_rec_res_inst.hip).
+//
+// The persistent-kernel idea ("Persistent RNNs") is to read R_l from memory
+// once per sequence and keep it on chip for all T steps.  A 4H x H layer with
+// H = 4096 in bf16 is 128 MiB: more than the 40 MiB of LDS of the whole chip,
+// less than LDS plus the 128 MiB of vector registers.  Here each of the four
+// waves of a workgroup (one per SIMD, so a wave may use all 512 registers)
+// holds NRB fragment blocks of its K share in registers for the whole launch
+// and the rest of its blocks in LDS; per step only h_{t-1} and the hoisted
+// pre-activations are read from memory.
+//
+// Work split: wave w is K-group w of 4.  It owns chunks c = w, w + 4, ... of
+// every M-tile of the workgroup (MW tiles) for every column tile (NW tiles),
+// so it reads a quarter of h_{t-1} and the four waves together read it once.
+// The launcher guarantees H = 4 * NCI chunks exactly (aligned rows), so every
+// wave has NCI chunks and all its offsets are compile-time constants.
+// Block b of a wave is (chunk index ci = b / MW, M-tile b % MW); blocks
+// b < NRB live in registers, the others in LDS.  The NW column tiles are
+// done one after the other (MW accumulators and one h fragment per chunk in
+// registers); after each, the four K-groups' partial sums meet in LDS and
+// K-group i finishes M-tile i of that column tile.
+// The step protocol (write-through stores, step counters, bounded waits) is the
+// one of lstm_rec_kernel.
+#pragma once
+
+#include "lstm_rec.h"
+
+namespace lstm {
+
+constexpr int kResWaves = 4;  // waves per workgroup = K-groups
+
+template <bool BF16, int MW, int NW, int NCI, int NRB>
+__global__ void __launch_bounds__(64 * kResWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
+lstm_rec_res_kernel(const RecParams P) {
+  typedef typename Dt<BF16>::T T;
+  constexpr int KC = Dt<BF16>::KC;
+  constexpr int KS = kResWaves;
+  constexpr int NB = MW * NCI;     // fragment blocks per wave
+  constexpr int NLB = NB - NRB;    // ... of which in LDS
+  constexpr int PD = 2;            // chunks of h loads in flight
+  static_assert(NRB >= 0 && NRB <= NB, "register blocks");
+  static_assert(MW <= KS, "one finishing K-group per M-tile");
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int s_ok;
+
+  const RecLayer& Lr = P.layer[0];
+  const int bid = blockIdx.x;
+  const int v = P.xcd_remap ? ((bid & 7) * (P.grid >> 3) + (bid >> 3)) : bid;
+  if (v >= Lr.wg_count) return;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int kg = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int q = lane >> 4;
+  const int H = P.H, B = P.B, T_ = P.T, cell = P.cell;
+  const long slot = P.slot;
+  const int mt0 = v * Lr.mt_per_wg;
+  const int mcnt = min(Lr.mt_per_wg, P.Mt - mt0);
+  uint4* As = reinterpret_cast<uint4*>(smem) + (long)kg * NLB * 128;  // this wave's LDS blocks
+  f32x4* red = reinterpret_cast<f32x4*>(smem + P.red_off);
+
+  bool mval[MW];
+  long arow[MW];
+  uint32_t mr_[MW];
+  int boff[NW];  // element offset of this lane's h row plus the wave's first chunk
+#pragma unroll
+  for (int i = 0; i < MW; ++i) {
+    mval[i] = i < mcnt;
+    const CellRow cr = cell_row(cell, mt0 + min(i, mcnt - 1), lane & 15, H);
+    mr_[i] = (mval[i] && cr.r >= 0) ? 0xffffffffu : 0u;
+    arow[i] = cr.r >= 0 ? cr.r : 0;
+  }
+#pragma unroll
+  for (int j = 0; j < NW; ++j) {
+    boff[j] = min(16 * j + (lane & 15), B - 1) * H + kg * KC;
+  }
+
+  // ---- this wave's weight blocks: registers for b < NRB, LDS for the rest
+  const T* Rp = reinterpret_cast<const T*>(Lr.R) + kg * KC;
+  Frag wreg[NRB > 0 ? NRB : 1];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int ci = b / MW, i = b % MW;
+    Frag f = load_frag_vec<BF16>(Rp + arow[i] * H + ci * KS * KC, q);
+    frag_mask(f, mr_[i]);
+    if (b < NRB)
+      wreg[b < NRB ? b : 0] = f;
+    else
+      lds_put(As + (b - NRB) * 128, lane, f);
+  }
+
+  // ---- per column tile j: this wave finishes M-tile kg (if it exists)
+  const bool fm = kg < mcnt;
+  const int funit = cell >= kCellRnnTanh ? 16 * (mt0 + kg) + 4 * q : 4 * (mt0 + kg) + q;
+  bool flive[NW];
+  long fgoff[NW];
+  float st[NW];
+  const T* h0p = reinterpret_cast<const T*>(Lr.h0);
+#pragma unroll
+  for (int j = 0; j < NW; ++j) {
+    const int bc = 16 * j + (lane & 15);
+    flive[j] = fm && j < P.ncnt && funit < H && bc < B;
+    fgoff[j] = ((long)min(mt0 + kg, P.Mt - 1) * B + min(bc, B - 1)) * 16 + 4 * q;
+    st[j] = 0.f;
+    if (flive[j]) {
+      const long o = (long)bc * H + funit;
+      if (cell == kCellLstm && Lr.c0) st[j] = Lr.c0[o];
+      if (cell == kCellGru && h0p) st[j] = to_float(h0p[o]);
+    }
+  }
+
+  long long* trc = nullptr;
+  if (P.trace && v % P.trace_stride == 0 && v / P.trace_stride < P.trace_wgs)
+    trc = P.trace + (long)(v / P.trace_stride) * T_ * 8;
+  auto stamp = [&](int t, int k) {
+    if (trc && tid == 0) trc[t * 8 + k] = wall_clock64();
+  };
+  auto stamp_clk = [&](int t, int k) {
+    if (trc && tid == 0) trc[t * 8 + k] = clock64();
+  };
+
+  T* Xp = reinterpret_cast<T*>(Lr.X);
+  const float* Gp = Lr.G;
+
+  for (int t = 0; t < T_; ++t) {
+    stamp(t, 0);
+    stamp_clk(t, 6);
+    f32x4 gq[NW];
+    {
+      const float* gt = Gp + (long)t * P.Mt * B * 16;
+#pragma unroll
+      for (int j = 0; j < NW; ++j) gq[j] = *reinterpret_cast<const f32x4*>(gt + fgoff[j]);
+    }
+
+    if (t > 0) {
+      if (kg == 0) {
+        const bool ok = wait_counts(Lr.flags, Lr.wg_count, t, nullptr, 0, 0, P.err, P.timeout_ticks);
+        if (lane == 0) s_ok = ok ? 1 : 0;
+      }
+      __syncthreads();
+      if (!s_ok) return;
+    }
+    stamp(t, 1);
+
+    // a null h_{t-1} (t = 0 without h0) is zero: nothing to multiply
+    const T* hsrc = t > 0 ? Xp + (long)(t - 1) * slot : h0p;
+    T* xout = Xp + (long)t * slot;
+    T* yout = Lr.Yout ? reinterpret_cast<T*>(Lr.Yout) + (long)t * B * H : nullptr;
+    const bool last = (t == T_ - 1);
+
+#pragma unroll
+    for (int j = 0; j < NW; ++j) {
+      f32x4 acc[MW];
+#pragma unroll
+      for (int i = 0; i < MW; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (hsrc) {
+        Frag rb[PD];
+        auto issue = [&](Frag& dst, int ci) { dst = load_frag_vec<BF16>(hsrc + boff[j] + ci * KS * KC, q); };
+        // LDS blocks are read one block ahead into the other of two buffers
+        Frag al[2];
+#pragma unroll
+        for (int s = 0; s < PD; ++s) issue(rb[s], s);
+        if (NLB > 0) al[0] = lds_get(As, lane);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ci = 0; ci < NCI; ++ci) {
+          const int s = ci % PD;
+#pragma unroll
+          for (int i = 0; i < MW; ++i) {
+            const int b = ci * MW + i;
+            if (b >= NRB && b + 1 < NB) al[(b + 1 - NRB) & 1] = lds_get(As + (b + 1 - NRB) * 128, lane);
+            const Frag& a = b < NRB ? wreg[b < NRB ? b : 0] : al[(b - NRB) & 1];
+            // no branch: a missing M-tile has zero weights and a missing
+            // column tile a clamped h row; their sums are never finished
+            mfma_frag<BF16>(acc[i], a, rb[s]);
+          }
+          if (ci + PD < NCI) issue(rb[s], ci + PD);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if (j == 0) {
+        stamp(t, 2);
+        stamp_clk(t, 7);
+      }
+
+      // ---- every K-group leaves its partial sums of the column tile in LDS;
+      // K-group kg then adds the four partials of M-tile kg in a fixed order
+#pragma unroll
+      for (int i = 0; i < MW; ++i) red[(i * KS + kg) * 64 + lane] = acc[i];
+      __syncthreads();
+      if (j == 0) stamp(t, 3);
+      if (flive[j]) {
+        f32x4 p = gq[j];
+#pragma unroll
+        for (int r = 0; r < KS; ++r) p += red[(kg * KS + r) * 64 + lane];
+        const long o = (long)(16 * j + (lane & 15)) * H + funit;
+        cell_update(cell, p, st[j], H - funit, [&](int u, float h) {
+          const T hv = from_float<BF16>(h);
+          store_coherent<BF16>(xout + o + u, hv);
+          if (yout) yout[o + u] = hv;
+          if (last && Lr.hT) reinterpret_cast<T*>(Lr.hT)[o + u] = hv;
+        });
+        if (cell == kCellLstm && last && Lr.cT) Lr.cT[o] = st[j];
+      }
+      // the next column tile reuses the partial-sum area
+      if (j + 1 < NW) __syncthreads();
+    }
+    stamp(t, 4);
+
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0)
+      __hip_atomic_store(Lr.flags + (long)v * kFlagStride, t + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    stamp(t, 5);
+  }
+}
+
+}  // namespace lstm

@@ -103,7 +103,10 @@ def test_planner_on_mi355x_shape(name):
     if name in ("c2", "c3", "c5", "c1"):
         assert info.weights_on_chip
     if name == "c4":
-        assert not info.weights_on_chip  # 128 MiB per layer of R cannot stay in LDS
+        # 128 MiB of R per layer: 48 of each wave's 64 blocks in registers, the rest in LDS
+        assert info.weights_on_chip and info.weight_blocks_in_registers == 48 and not info.weights_streamed
+    else:
+        assert info.weight_blocks_in_registers == 0
     if info.regime == 2:
         assert info.layers_per_launch == c.L
         assert info.num_launches == 2  # clear + one recurrent launch: every input product fused

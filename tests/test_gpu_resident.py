@@ -1,0 +1,109 @@
+"""GPU parity of the register-resident recurrent kernel (bf16 layers with H = 4096,
+whose 128 MiB of recurrent weights stay on chip in registers plus LDS).
+
+The oracle runs on sampled batch columns (sequences are independent); the same
+tolerances as every bf16 workload: max-norm relative error 2e-2 per output.
+Every case prints its name before touching the GPU.
+"""
+import numpy as np
+import pytest
+
+import lstm_inputs as li
+import oracle.lstm_oracle as orc
+from tests.pins import rel_err
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    import stacked_lstm_forward_amd as sl
+    sl.load_library()
+    return "cuda:0"
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+def resident_plan(cfg):
+    import stacked_lstm_forward_amd as sl
+    d = sl.make_desc(cfg.L, cfg.I, cfg.H, cfg.B, cfg.T, cfg.dtype, cfg.cell)
+    return sl.lstm_fwd_plan(d, 0, 0, 0)
+
+
+def run(inp, dev):
+    import stacked_lstm_forward_amd as sl
+    from stacked_lstm_forward_amd import runner
+    prob = runner.prepare(inp, dev)
+    prob.run()
+    st = sl.lstm_fwd_last_error(prob.ws)
+    assert st == sl.LSTM_OK, sl.lstm_status_string(st)
+    return prob
+
+
+def check(got, ref, what):
+    names = ("y", "hT", "cT")
+    errs = {}
+    for n, g, r in zip(names, got, ref):
+        if r is None:
+            assert g is None
+            continue
+        assert np.all(np.isfinite(g)), (what, n)
+        errs[n] = rel_err(g, r)
+    say(f"{what}: " + " ".join(f"{n}={e:.2e}" for n, e in errs.items()))
+    for n, e in errs.items():
+        assert e <= TOL, (what, n, e)
+
+
+# B = 16: one column tile; 20: a ragged second tile; 32: two full tiles
+@pytest.mark.parametrize("B,cols", [(16, [0, 7, 15]), (20, [0, 15, 16, 19]), (32, [1, 14, 17, 31])])
+@pytest.mark.parametrize("random_state", [False, True])
+def test_gpu_resident_lstm(dev, B, cols, random_state):
+    cfg = li.custom_config(1, 256, 4096, B, 4, "bf16", cfg_id=310 + B)
+    info = resident_plan(cfg)
+    assert info.weight_blocks_in_registers == 48 and info.weights_on_chip and not info.weights_streamed
+    inp = li.make_inputs(cfg, random_state=random_state)
+    say(f"resident lstm H=4096 B={B} random_state={random_state}")
+    y, hT, cT = run(inp, dev).outputs_f32()
+    c = np.array(cols)
+    ref = orc.forward_inputs(inp.batch_subset(c))
+    check((y[:, c], hT[:, c], cT[:, c]), ref, f"resident lstm B={B} rs={int(random_state)}")
+
+
+def test_gpu_resident_gru(dev):
+    cfg = li.with_cell(li.custom_config(1, 256, 4096, 32, 3, "bf16", cfg_id=341), "gru")
+    assert resident_plan(cfg).weight_blocks_in_registers == 48
+    inp = li.make_inputs(cfg, random_state=True)
+    say("resident gru H=4096 B=32")
+    y, hT, cT = run(inp, dev).outputs_f32()
+    c = np.array([0, 13, 31])
+    ref = orc.forward_inputs(inp.batch_subset(c))
+    check((y[:, c], hT[:, c], None), ref, "resident gru")
+
+
+def test_gpu_resident_two_layers_deterministic(dev):
+    """Two resident layers in a row (layer 1 reads layer 0's exchange buffer),
+    and three calls give the same bits whatever the workspace held."""
+    import torch
+    cfg = li.custom_config(2, 128, 4096, 24, 3, "bf16", cfg_id=342)
+    assert resident_plan(cfg).weight_blocks_in_registers == 48
+    inp = li.make_inputs(cfg, random_state=True)
+    say("resident two layers H=4096 B=24, determinism")
+    prob = run(inp, dev)
+    first = [t.clone() for t in (prob.y, prob.hT, prob.cT)]
+    y, hT, cT = prob.outputs_f32()
+    c = np.array([2, 23])
+    ref = orc.forward_inputs(inp.batch_subset(c))
+    check((y[:, c], hT[:, c], cT[:, c]), ref, "resident two layers")
+    for _ in range(2):
+        prob.ws.fill_(0x5A)
+        prob.run()
+        for a, b in zip(first, (prob.y, prob.hT, prob.cT)):
+            va = a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32)
+            vb = b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32)
+            assert torch.equal(va, vb)
