@@ -245,6 +245,7 @@ lstm_status_t lstm_fwd_ex(const lstm_desc_t* d, const void* x, const void* h0, c
     RecParams rp;
     rp.nlayers = lp.nlayers;
     rp.slot = (long long)slot;
+    rp.fslot = (long long)p.xf_slot_elems;
     rp.T = T, rp.B = B, rp.H = H, rp.Mt = p.Mt, rp.ncnt = p.ncnt;
     rp.cell = p.cell;
     rp.ks = lp.ks;
@@ -270,6 +271,7 @@ lstm_status_t lstm_fwd_ex(const lstm_desc_t* d, const void* x, const void* h0, c
       r.U = pl.hoisted ? nullptr : (l == 0 ? x : xbuf(l - 1));
       r.u_slot = pl.hoisted ? 0 : (l == 0 ? (long long)B * I : (long long)slot);
       r.X = xbuf(l);
+      r.Xf = lp.res_nrb > 0 ? static_cast<void*>(wsb + p.xf_off) : nullptr;
       r.Yout = (l == L - 1) ? y : nullptr;
       r.h0 = state(h0, l, ds);
       r.c0 = static_cast<const float*>(state(c0, l, sizeof(float)));
@@ -295,7 +297,7 @@ lstm_status_t lstm_fwd_ex(const lstm_desc_t* d, const void* x, const void* h0, c
     for (int k = 0; k < lp.nlayers; ++k) vec = vec && rp.layer[k].vec_ok;
     int per_cu = 0;
     const bool res = lp.res_nrb > 0;
-    if (res && !vec) return LSTM_ERR_UNSUPPORTED;  // planned only for aligned whole-chunk rows
+    if (res && (!vec || p.xf_slot_elems == 0)) return LSTM_ERR_UNSUPPORTED;  // planned only for aligned rows
     const hipError_t pe = res ? res_prepare(bf16, lp.mw, lp.nw, lp.res_nci, lp.res_nrb, lp.lds_bytes, &per_cu)
                               : rec_prepare(bf16, lp.stream, vec, lp.nwaves, lp.mw, lp.nw, lp.lds_bytes, &per_cu);
     if (pe != hipSuccess) return LSTM_ERR_HIP;

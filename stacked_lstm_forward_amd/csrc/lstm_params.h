@@ -42,6 +42,8 @@ struct RecLayer {
   const void* U;          // fused input: step t, batch b at U + t*u_slot + b*Kin (the layer
                           // below's exchange buffer, or x for layer 0), or null
   void* X;                // this layer's exchange buffer: [T] slots of [B][H]
+  void* Xf;               // register-resident kernel only: h_t again, in the order its
+                          // readers load it (see lstm_rec_res.h), [T] slots of fslot elements
   void* Yout;             // caller's y [T][B][H] (top layer), or null
   const void* h0;         // [B][H] or null (zeros)
   const float* c0;        // [B][H] or null (zeros)
@@ -61,6 +63,7 @@ struct RecLayer {
 struct RecParams {
   RecLayer layer[kMaxLayersPerLaunch];
   long long slot;         // elements between two steps of an exchange buffer
+  long long fslot;        // elements between two steps of Xf
   int nlayers;
   int T, B, H, Mt, ncnt;  // ncnt = ceil(B/16) column tiles
   int cell;               // lstm_cell_t

@@ -82,8 +82,10 @@ int round_grid(int g) { return (g + 7) & ~7; }
 // between the registers and the LDS of each workgroup.  Only the bf16 shape
 // the kernel is instantiated for: 4 M-tiles per workgroup, 4 K-groups of
 // exactly kResNCI chunks each (H = 4096), at most two 16-column batch tiles.
+bool resident_shape(bool bf16, int nch, int ncnt) { return bf16 && nch == 4 * kResNCI && ncnt <= 2; }
+
 bool plan_resident(int m, int nch, int ncnt, bool bf16, bool aligned, const DeviceInfo& dev, LaunchPlan* lp) {
-  if (!bf16 || !aligned || m > kResMW || nch != 4 * kResNCI || ncnt > 2) return false;
+  if (!resident_shape(bf16, nch, ncnt) || !aligned || m > kResMW) return false;
   const int nlb = kResMW * kResNCI - kResNRB;  // LDS blocks per wave
   const int red = kResMW * 4 * 64 * 16;        // one 1 KiB partial per (M-tile, K-group)
   const int red_off = 4 * nlb * 64 * kFragBytes;
@@ -272,6 +274,15 @@ int make_plan(const int32_t L, const int32_t I, const int32_t H, const int32_t B
   const size_t slot_bytes = ((size_t)B * H * p.dsize + kSlotAlign - 1) / kSlotAlign * kSlotAlign;
   p.slot_elems = slot_bytes / p.dsize;
   off += (size_t)L * T * slot_bytes;
+  // the register-resident kernel's fragment-order copy of h: one layer at a
+  // time, so one set of T slots; sized from the shape alone, so the workspace
+  // does not depend on the device the plan is made for
+  p.xf_off = off;
+  if (resident_shape(p.bf16 != 0, nch_h, p.ncnt) && (H % p.KC) == 0) {
+    const size_t xf_bytes = align256((size_t)p.ncnt * 16 * H * p.dsize);
+    p.xf_slot_elems = xf_bytes / p.dsize;
+    off += (size_t)T * xf_bytes;
+  }
   p.ws_bytes = off;
   return kStatusOk;
 }

@@ -21,6 +21,17 @@
 // done one after the other (MW accumulators and one h fragment per chunk in
 // registers); after each, the four K-groups' partial sums meet in LDS and
 // K-group i finishes M-tile i of that column tile.
+//
+// Exchange layout.  A wave's load of one fragment half touches 16 batch rows
+// of h; from a row-major [B][H] buffer that is 16 pieces of 64 bytes 2H bytes
+// apart, which the vector memory path serves several times slower than 1 KiB
+// of contiguous memory.  So h_t also goes to Xf in exactly the order its
+// readers load it: for column tile j and chunk c a 2 KiB block, half h at
+// +1 KiB, lane l's 16 bytes at +16 l:
+//     Xf[t][((j * nch + c) * 2 + h) * 64 + lane][8 bf16]
+// and every load instruction of a step reads 1 KiB in one piece.  The row-major
+// copy (the next layer's input, or y) is still written; step 0 reads the
+// caller's row-major h0.
 // The step protocol (write-through stores, step counters, bounded waits) is the
 // one of lstm_rec_kernel.
 #pragma once
@@ -55,6 +66,9 @@ lstm_rec_res_kernel(const RecParams P) {
   const int q = lane >> 4;
   const int H = P.H, B = P.B, T_ = P.T, cell = P.cell;
   const long slot = P.slot;
+  constexpr int NCH = KS * NCI;           // chunks of a row of h
+  constexpr int FB = 2048 / Dt<BF16>::SZ;  // elements of one 2 KiB fragment block
+  constexpr int EPH = 16 / Dt<BF16>::SZ;   // elements of one lane's 16-byte half
   const int mt0 = v * Lr.mt_per_wg;
   const int mcnt = min(Lr.mt_per_wg, P.Mt - mt0);
   uint4* As = reinterpret_cast<uint4*>(smem) + (long)kg * NLB * 128;  // this wave's LDS blocks
@@ -63,7 +77,9 @@ lstm_rec_res_kernel(const RecParams P) {
   bool mval[MW];
   long arow[MW];
   uint32_t mr_[MW];
-  int boff[NW];  // element offset of this lane's h row plus the wave's first chunk
+  // element offsets of this lane's two fragment halves of its first chunk:
+  // row-major (h0) and fragment order (Xf); chunk ci adds ci * KS * KC, resp. ci * KS * FB
+  uint32_t hrm[NW][2], hfr[NW][2];
 #pragma unroll
   for (int i = 0; i < MW; ++i) {
     mval[i] = i < mcnt;
@@ -73,7 +89,11 @@ lstm_rec_res_kernel(const RecParams P) {
   }
 #pragma unroll
   for (int j = 0; j < NW; ++j) {
-    boff[j] = min(16 * j + (lane & 15), B - 1) * H + kg * KC;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      hrm[j][hh] = min(16 * j + (lane & 15), B - 1) * H + kg * KC + frag_col<BF16>(q, hh);
+      hfr[j][hh] = (j * NCH + kg) * FB + hh * (FB / 2) + lane * EPH;
+    }
   }
 
   // ---- this wave's weight blocks: registers for b < NRB, LDS for the rest
@@ -93,6 +113,14 @@ lstm_rec_res_kernel(const RecParams P) {
   // ---- per column tile j: this wave finishes M-tile kg (if it exists)
   const bool fm = kg < mcnt;
   const int funit = cell >= kCellRnnTanh ? 16 * (mt0 + kg) + 4 * q : 4 * (mt0 + kg) + q;
+  // Xf position of this lane's unit in column tile 0 (the simple RNN's four
+  // units funit..funit+3 share one 16-byte group, so they follow it)
+  uint32_t fpos;
+  {
+    const int c = funit / KC, kc = funit % KC;
+    const int hh = kc / (KC / 2), qq = (kc % (KC / 2)) / EPH, e = kc % EPH;
+    fpos = c * FB + hh * (FB / 2) + (qq * 16 + (lane & 15)) * EPH + e;
+  }
   bool flive[NW];
   long fgoff[NW];
   float st[NW];
@@ -121,6 +149,7 @@ lstm_rec_res_kernel(const RecParams P) {
   };
 
   T* Xp = reinterpret_cast<T*>(Lr.X);
+  T* Xf = reinterpret_cast<T*>(Lr.Xf);
   const float* Gp = Lr.G;
 
   for (int t = 0; t < T_; ++t) {
@@ -144,9 +173,12 @@ lstm_rec_res_kernel(const RecParams P) {
     stamp(t, 1);
 
     // a null h_{t-1} (t = 0 without h0) is zero: nothing to multiply
-    const T* hsrc = t > 0 ? Xp + (long)(t - 1) * slot : h0p;
-    T* xout = Xp + (long)t * slot;
-    T* yout = Lr.Yout ? reinterpret_cast<T*>(Lr.Yout) + (long)t * B * H : nullptr;
+    const bool fr = t > 0;
+    const T* hsrc = fr ? Xf + (long)(t - 1) * P.fslot : h0p;
+    const long cstride = fr ? KS * FB : KS * KC;
+    T* fout = Xf + (long)t * P.fslot;
+    // row-major copy: y for the top layer, else the next layer's input
+    T* rout = Lr.Yout ? reinterpret_cast<T*>(Lr.Yout) + (long)t * B * H : Xp + (long)t * slot;
     const bool last = (t == T_ - 1);
 
 #pragma unroll
@@ -156,7 +188,12 @@ lstm_rec_res_kernel(const RecParams P) {
       for (int i = 0; i < MW; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (hsrc) {
         Frag rb[PD];
-        auto issue = [&](Frag& dst, int ci) { dst = load_frag_vec<BF16>(hsrc + boff[j] + ci * KS * KC, q); };
+        const uint32_t o0 = fr ? hfr[j][0] : hrm[j][0], o1 = fr ? hfr[j][1] : hrm[j][1];
+        auto issue = [&](Frag& dst, int ci) {
+          const T* pc = hsrc + ci * cstride;
+          dst.v[0] = *reinterpret_cast<const uint4*>(pc + o0);
+          dst.v[1] = *reinterpret_cast<const uint4*>(pc + o1);
+        };
         // LDS blocks are read one block ahead into the other of two buffers
         Frag al[2];
 #pragma unroll
@@ -195,10 +232,11 @@ lstm_rec_res_kernel(const RecParams P) {
 #pragma unroll
         for (int r = 0; r < KS; ++r) p += red[(kg * KS + r) * 64 + lane];
         const long o = (long)(16 * j + (lane & 15)) * H + funit;
+        const long fo = (long)j * NCH * FB + fpos;
         cell_update(cell, p, st[j], H - funit, [&](int u, float h) {
           const T hv = from_float<BF16>(h);
-          store_coherent<BF16>(xout + o + u, hv);
-          if (yout) yout[o + u] = hv;
+          store_coherent<BF16>(fout + fo + u, hv);
+          rout[o + u] = hv;
           if (last && Lr.hT) reinterpret_cast<T*>(Lr.hT)[o + u] = hv;
         });
         if (cell == kCellLstm && last && Lr.cT) Lr.cT[o] = st[j];

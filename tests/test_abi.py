@@ -83,6 +83,10 @@ def test_workspace_size_formula():
         mt = (c.H + 3) // 4
         slot = -(-c.B * c.H * ds // 256) * 256  # exchange slots start on 256-byte boundaries
         expect = 256 + c.L * 1024 * 128 + c.T * mt * c.B * 16 * 4 + c.L * c.T * slot
+        if c.dtype == "bf16" and c.H == 4096 and c.B <= 32:
+            # the register-resident kernel's copy of h in load order: T slots of
+            # (B rounded up to 16) x H
+            expect += c.T * (-(-c.B // 16) * 16 * c.H * ds)
         assert expect <= n <= expect + 4 * 256, (name, n, expect)
 
 
