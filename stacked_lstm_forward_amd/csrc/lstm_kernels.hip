@@ -181,9 +181,9 @@ __global__ void __launch_bounds__(kGemmThreads) lstm_input_gemm(const GemmParams
 // 16-byte aligned, no rows without input weights): a 256 x 256 workgroup
 // tile, 4 waves of 128 x 128 (8 x 8 MFMA tiles, accumulators in the
 // accumulation registers).  Operands go from global memory straight into LDS
-// with the gfx950 direct-to-LDS loads (each wave-wide 16-byte load fills one
-// 1 KiB half of a fragment block, lane l at byte 16*l -- the half-major block
-// layout), two stages deep: chunk c+1 streams in while chunk c is multiplied.
+// with the gfx950 direct-to-LDS loads (a wave-wide 16-byte load lands lane l
+// at byte 16*l of its LDS destination), two stages deep: chunk c+1 streams in
+// while chunk c is multiplied.
 // Per chunk a wave reads 32 KiB from LDS for 128 MFMAs (2 per tile, chained on
 // one accumulator, which keeps the matrix pipe issuing back to back).
 constexpr int kDmaTiles = 16;                    // M-tiles and column tiles per workgroup
@@ -228,32 +228,54 @@ __global__ void __launch_bounds__(kGemmThreads) lstm_input_gemm_dma(const GemmPa
   const int nch = P.K / KC;
 
   // staging: wave w fills fragment blocks 8w .. 8w+7 of every stage (blocks
-  // 0-15: the A tiles, W rows; 16-31: the B tiles, columns of U), both halves.
-  // Rows and columns past the end are clamped to valid ones (results unused).
+  // 0-15: the A tiles, W rows; 16-31: the B tiles, columns of U).  A block
+  // holds its 16 rows' 128-byte chunks row by row, 8 pieces of 16 bytes each,
+  // piece p of row r in slot p ^ ((r >> 1) & 7).  One wave-wide load fills half
+  // a block: 8 whole rows, lane l row 8i + l/8, slot l%8, so every load reads
+  // whole 128-byte lines (a load of 16 rows x 64 bytes costs the texture path
+  // several times more), and the swizzle keeps the fragment reads below free
+  // of bank conflicts.  Rows and columns past the end are clamped to valid
+  // ones (results unused).
+  constexpr int EPH = 16 / Dt<BF16>::SZ;  // elements of one 16-byte piece
   const T* gbase = reinterpret_cast<const T*>(wave < 2 ? P.W : P.U);
-  long src[8];
+  long src[8][2];
 #pragma unroll
   for (int s8 = 0; s8 < 8; ++s8) {
     const int blk = 8 * wave + s8;
-    if (wave < 2) {
-      const int mt = mtb + blk;
-      long r = mt < P.Mt ? cell_row(P.cell, mt, lane & 15, P.H).w : -1;
-      src[s8] = (r < 0 ? 0 : r) * P.K;
-    } else {
-      long col = n0 + 16 * (blk - kDmaTiles) + (lane & 15);
-      col = col < P.N ? col : P.N - 1;
-      src[s8] = (col / P.B) * P.u_slot + (col % P.B) * P.K;  // column n: step n / B, sequence n % B
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = 8 * i + (lane >> 3);
+      const long piece = (lane & 7) ^ ((r >> 1) & 7);
+      if (wave < 2) {
+        const int mt = mtb + blk;
+        long row = mt < P.Mt ? cell_row(P.cell, mt, r, P.H).w : -1;
+        src[s8][i] = (row < 0 ? 0 : row) * P.K + piece * EPH;
+      } else {
+        long col = n0 + 16 * (blk - kDmaTiles) + r;
+        col = col < P.N ? col : P.N - 1;
+        // column n: step n / B, sequence n % B
+        src[s8][i] = (col / P.B) * P.u_slot + (col % P.B) * P.K + piece * EPH;
+      }
     }
   }
   auto stage_load = [&](int c, int buf) {
 #pragma unroll
     for (int s8 = 0; s8 < 8; ++s8)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const T* g = gbase + src[s8] + (long)c * KC + frag_col<BF16>(q, h);
-        uint4* l = lds + buf * kDmaStage + (8 * wave + s8) * 128 + h * 64;
+      for (int i = 0; i < 2; ++i) {
+        const T* g = gbase + src[s8][i] + (long)c * KC;
+        uint4* l = lds + buf * kDmaStage + (8 * wave + s8) * 128 + i * 64;
         __builtin_amdgcn_global_load_lds((gptr_t)g, (lptr_t)l, 16, 0, 0);
       }
+  };
+  // this lane's two fragment halves (row lane%16, pieces 4h + lane/16) in a block
+  const int fr_ = lane & 15, fsw = (fr_ >> 1) & 7;
+  const int foff0 = fr_ * 8 + ((0 + q) ^ fsw), foff1 = fr_ * 8 + ((4 + q) ^ fsw);
+  auto frag_at = [&](const uint4* blk) {
+    Frag f;
+    f.v[0] = blk[foff0];
+    f.v[1] = blk[foff1];
+    return f;
   };
 
   const int wm = wave & 1, wn = wave >> 1;
@@ -276,13 +298,13 @@ __global__ void __launch_bounds__(kGemmThreads) lstm_input_gemm_dma(const GemmPa
     const uint4* st = lds + (c & 1) * kDmaStage;
     Frag a[8], b[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) b[j] = lds_get(st + (kDmaTiles + 8 * wn + j) * 128, lane);
-    a[0] = lds_get(st + (8 * wm + 0) * 128, lane);
-    a[1] = lds_get(st + (8 * wm + 1) * 128, lane);
+    for (int j = 0; j < 8; ++j) b[j] = frag_at(st + (kDmaTiles + 8 * wn + j) * 128);
+    a[0] = frag_at(st + (8 * wm + 0) * 128);
+    a[1] = frag_at(st + (8 * wm + 1) * 128);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      if (i + 2 < 8) a[i + 2] = lds_get(st + (8 * wm + i + 2) * 128, lane);
+      if (i + 2 < 8) a[i + 2] = frag_at(st + (8 * wm + i + 2) * 128);
 #pragma unroll
       for (int j = 0; j < 8; ++j) mfma_frag<BF16>(acc[i][j], a[i], b[j]);
       __builtin_amdgcn_sched_barrier(0);
