@@ -17,10 +17,11 @@
 
 namespace lstm {
 hipError_t launch_input_gemm(bool bf16, const GemmParams& p, hipStream_t s);
-hipError_t rec_prepare(bool bf16, bool stream, bool vec, int nwv, int mw, int nw, int lds_bytes, int* max_blocks_per_cu);
+hipError_t rec_prepare(bool bf16, bool stream, bool vec, bool frag, int nwv, int mw, int nw, int lds_bytes,
+                       int* max_blocks_per_cu);
 hipError_t launch_clear(int* p, long long n, hipStream_t s);
-hipError_t launch_rec(bool bf16, bool stream, bool vec, int nwv, const RecParams& p, int lds_bytes, bool plain,
-                      hipStream_t s);
+hipError_t launch_rec(bool bf16, bool stream, bool vec, bool frag, int nwv, const RecParams& p, int lds_bytes,
+                      bool plain, hipStream_t s);
 hipError_t res_prepare(bool bf16, int mw, int nw, int nci, int nrb, int lds_bytes, int* max_blocks_per_cu);
 hipError_t launch_rec_res(bool bf16, int nci, int nrb, const RecParams& p, int lds_bytes, bool plain, hipStream_t s);
 }  // namespace lstm
@@ -240,12 +241,34 @@ lstm_status_t lstm_fwd_ex(const lstm_desc_t* d, const void* x, const void* h0, c
     return LSTM_OK;
   };
 
+  // 16-byte loads allowed for every operand row of layer pl (the aligned path)
+  auto layer_vec = [&](const LayerPlan& pl) -> bool {
+    const int l = pl.layer;
+    const void* Wl = pl.hoisted ? nullptr : W_l(l);
+    const void* Ul = pl.hoisted ? nullptr : (l == 0 ? x : static_cast<const void*>(xbuf(l - 1)));
+    const long long us = pl.hoisted ? 0 : (l == 0 ? (long long)B * I : (long long)slot);
+    return ((size_t)H * ds) % 16 == 0 && aligned16(R_l(l)) && aligned16(xbuf(l)) && (!Wl || aligned16(Wl)) &&
+           (!Ul || aligned16(Ul)) && (!state(h0, l, ds) || aligned16(state(h0, l, ds))) && (pl.Kin % p.KC) == 0 &&
+           ((size_t)us * ds) % 16 == 0;
+  };
+  auto launch_vec = [&](const LaunchPlan& lp) -> bool {
+    bool v = (H % p.KC) == 0;
+    for (int k = 0; k < lp.nlayers; ++k) v = v && layer_vec(lp.layers[k]);
+    return v;
+  };
+  // Wavefront launches read each other's exchange buffers (the first layer of
+  // a launch reads the last layer of the one before), so they use the
+  // load-order exchange only if every one of them is on the aligned path.
+  bool wave_vec = true;
+  if (p.regime == LSTM_REGIME_WAVEFRONT)
+    for (int r = 0; r < p.nrec; ++r) wave_vec = wave_vec && launch_vec(p.rec[r]);
+
   bool traced = false;  // only the first recurrent launch is traced
   auto rec = [&](const LaunchPlan& lp) -> lstm_status_t {
     RecParams rp;
     rp.nlayers = lp.nlayers;
     rp.slot = (long long)slot;
-    rp.fslot = (long long)p.xf_slot_elems;
+    rp.fslot = (long long)slot;
     rp.T = T, rp.B = B, rp.H = H, rp.Mt = p.Mt, rp.ncnt = p.ncnt;
     rp.cell = p.cell;
     rp.ks = lp.ks;
@@ -271,7 +294,8 @@ lstm_status_t lstm_fwd_ex(const lstm_desc_t* d, const void* x, const void* h0, c
       r.U = pl.hoisted ? nullptr : (l == 0 ? x : xbuf(l - 1));
       r.u_slot = pl.hoisted ? 0 : (l == 0 ? (long long)B * I : (long long)slot);
       r.X = xbuf(l);
-      r.Xf = lp.res_nrb > 0 ? static_cast<void*>(wsb + p.xf_off) : nullptr;
+      r.F = nullptr;
+      r.ufrag = 0;
       r.Yout = (l == L - 1) ? y : nullptr;
       r.h0 = state(h0, l, ds);
       r.c0 = static_cast<const float*>(state(c0, l, sizeof(float)));
@@ -286,26 +310,46 @@ lstm_status_t lstm_fwd_ex(const lstm_desc_t* d, const void* x, const void* h0, c
       r.wg_count = pl.wg_count;
       r.mt_per_wg = pl.mt_per_wg;
       r.staged = pl.staged;
-      const size_t row_bytes = (size_t)H * ds;
-      r.vec_ok = (row_bytes % 16 == 0) && aligned16(r.R) && aligned16(r.X) && (!r.W || aligned16(r.W)) &&
-                 (!r.U || aligned16(r.U)) && (!r.h0 || aligned16(r.h0)) && (r.Kin % p.KC) == 0 &&
-                 ((size_t)r.u_slot * ds) % 16 == 0;
+      r.vec_ok = layer_vec(pl) ? 1 : 0;
     }
     for (int k = lp.nlayers; k < kMaxLayersPerLaunch; ++k) rp.layer[k] = RecLayer();
     // aligned fast path: whole chunks and 16-byte aligned rows in every layer of the launch
-    bool vec = (H % p.KC) == 0;
-    for (int k = 0; k < lp.nlayers; ++k) vec = vec && rp.layer[k].vec_ok;
+    const bool vec = launch_vec(lp);
+    // On the aligned path h_t is exchanged in load order when the batch fills
+    // at least one 16-column tile (below that a load-order read would fetch
+    // mostly padding; the register-resident kernel always uses it).
+    // Wavefront: each layer's exchange buffer holds it (read by the layer
+    // itself and, as its fused input, by the layer above).  Layerwise: the
+    // one-layer load-order region holds it, and the row-major slots keep a
+    // copy for the next layer's input GEMM (none for the top layer, whose
+    // copy is y).
+    const bool frag = vec && (p.regime != LSTM_REGIME_WAVEFRONT || wave_vec) && (B >= 16 || lp.res_nrb > 0);
+    if (frag) {
+      for (int k = 0; k < lp.nlayers; ++k) {
+        RecLayer& r = rp.layer[k];
+        const LayerPlan& pl = lp.layers[k];
+        const int l = pl.layer;
+        if (p.regime == LSTM_REGIME_WAVEFRONT) {
+          r.F = xbuf(l);
+          r.X = nullptr;
+          if (!pl.hoisted && l > 0) r.ufrag = 1;  // U = xbuf(l - 1), now in load order
+        } else {
+          r.F = static_cast<void*>(wsb + p.xf_off);
+          r.X = (l < L - 1) ? xbuf(l) : nullptr;
+        }
+      }
+    }
     int per_cu = 0;
     const bool res = lp.res_nrb > 0;
-    if (res && (!vec || p.xf_slot_elems == 0)) return LSTM_ERR_UNSUPPORTED;  // planned only for aligned rows
+    if (res && !vec) return LSTM_ERR_UNSUPPORTED;  // planned only for aligned rows
     const hipError_t pe = res ? res_prepare(bf16, lp.mw, lp.nw, lp.res_nci, lp.res_nrb, lp.lds_bytes, &per_cu)
-                              : rec_prepare(bf16, lp.stream, vec, lp.nwaves, lp.mw, lp.nw, lp.lds_bytes, &per_cu);
+                              : rec_prepare(bf16, lp.stream, vec, frag, lp.nwaves, lp.mw, lp.nw, lp.lds_bytes, &per_cu);
     if (pe != hipSuccess) return LSTM_ERR_HIP;
     if ((long long)per_cu * dev.info.num_cus < lp.grid) return LSTM_ERR_UNSUPPORTED;  // not co-resident
     if (!before(LSTM_KERNEL_RECURRENT)) return LSTM_ERR_HIP;
     const bool plain = opts && opts->plain_launch;
     const hipError_t le = res ? launch_rec_res(bf16, lp.res_nci, lp.res_nrb, rp, lp.lds_bytes, plain, stream)
-                              : launch_rec(bf16, lp.stream, vec, lp.nwaves, rp, lp.lds_bytes, plain, stream);
+                              : launch_rec(bf16, lp.stream, vec, frag, lp.nwaves, rp, lp.lds_bytes, plain, stream);
     if (le != hipSuccess) return LSTM_ERR_HIP;
     if (!after()) return LSTM_ERR_HIP;
     return LSTM_OK;

@@ -346,7 +346,7 @@ __global__ void __launch_bounds__(256) lstm_clear(int* p, long long n) {
 // touches them).  The recurrent kernel's instantiations live in
 // lstm_rec_inst.hip, compiled once per (dtype, weight source).
 // ----------------------------------------------------------------------------
-#define LSTM_DECL(d, s, w) const void* rec_kernel_ptr_##d##_##s##_w##w(int mw, int nw, bool vec);
+#define LSTM_DECL(d, s, w) const void* rec_kernel_ptr_##d##_##s##_w##w(int mw, int nw, bool vec, bool frag);
 LSTM_DECL(f32, lds, 4) LSTM_DECL(f32, stream, 4) LSTM_DECL(bf16, lds, 4) LSTM_DECL(bf16, stream, 4)
 LSTM_DECL(f32, lds, 8) LSTM_DECL(f32, stream, 8) LSTM_DECL(bf16, lds, 8) LSTM_DECL(bf16, stream, 8)
 #undef LSTM_DECL
@@ -354,13 +354,15 @@ LSTM_DECL(f32, lds, 8) LSTM_DECL(f32, stream, 8) LSTM_DECL(bf16, lds, 8) LSTM_DE
 const void* rec_res_kernel_ptr(bool bf16, int mw, int nw, int nci, int nrb);
 
 namespace {
-const void* rec_kernel_fn(bool bf16, bool stream, bool vec, int nwv, int mw, int nw) {
+const void* rec_kernel_fn(bool bf16, bool stream, bool vec, int nwv, int mw, int nw, bool frag) {
   if (nwv == 8) {
-    if (bf16) return stream ? rec_kernel_ptr_bf16_stream_w8(mw, nw, vec) : rec_kernel_ptr_bf16_lds_w8(mw, nw, vec);
-    return stream ? rec_kernel_ptr_f32_stream_w8(mw, nw, vec) : rec_kernel_ptr_f32_lds_w8(mw, nw, vec);
+    if (bf16)
+      return stream ? rec_kernel_ptr_bf16_stream_w8(mw, nw, vec, frag) : rec_kernel_ptr_bf16_lds_w8(mw, nw, vec, frag);
+    return stream ? rec_kernel_ptr_f32_stream_w8(mw, nw, vec, frag) : rec_kernel_ptr_f32_lds_w8(mw, nw, vec, frag);
   }
-  if (bf16) return stream ? rec_kernel_ptr_bf16_stream_w4(mw, nw, vec) : rec_kernel_ptr_bf16_lds_w4(mw, nw, vec);
-  return stream ? rec_kernel_ptr_f32_stream_w4(mw, nw, vec) : rec_kernel_ptr_f32_lds_w4(mw, nw, vec);
+  if (bf16)
+    return stream ? rec_kernel_ptr_bf16_stream_w4(mw, nw, vec, frag) : rec_kernel_ptr_bf16_lds_w4(mw, nw, vec, frag);
+  return stream ? rec_kernel_ptr_f32_stream_w4(mw, nw, vec, frag) : rec_kernel_ptr_f32_lds_w4(mw, nw, vec, frag);
 }
 }  // namespace
 
@@ -404,8 +406,9 @@ hipError_t launch_clear(int* p, long long n, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t rec_prepare(bool bf16, bool stream, bool vec, int nwv, int mw, int nw, int lds_bytes, int* max_blocks_per_cu) {
-  const void* fn = rec_kernel_fn(bf16, stream, vec, nwv, mw, nw);
+hipError_t rec_prepare(bool bf16, bool stream, bool vec, bool frag, int nwv, int mw, int nw, int lds_bytes,
+                       int* max_blocks_per_cu) {
+  const void* fn = rec_kernel_fn(bf16, stream, vec, nwv, mw, nw, frag);
   if (!fn) return hipErrorInvalidValue;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
   if (e != hipSuccess) return e;
@@ -428,9 +431,9 @@ hipError_t launch_rec_res(bool bf16, int nci, int nrb, const RecParams& p, int l
   return hipLaunchCooperativeKernel(fn, dim3(p.grid), dim3(64 * 4), args, (unsigned)lds_bytes, s);
 }
 
-hipError_t launch_rec(bool bf16, bool stream, bool vec, int nwv, const RecParams& p, int lds_bytes, bool plain,
-                      hipStream_t s) {
-  const void* fn = rec_kernel_fn(bf16, stream, vec, nwv, p.mw, p.nw);
+hipError_t launch_rec(bool bf16, bool stream, bool vec, bool frag, int nwv, const RecParams& p, int lds_bytes,
+                      bool plain, hipStream_t s) {
+  const void* fn = rec_kernel_fn(bf16, stream, vec, nwv, p.mw, p.nw, frag);
   if (!fn) return hipErrorInvalidValue;
   void* args[] = {const_cast<RecParams*>(&p)};
   if (plain) return hipLaunchKernel(fn, dim3(p.grid), dim3(64 * nwv), args, (unsigned)lds_bytes, s);

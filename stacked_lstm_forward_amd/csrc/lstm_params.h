@@ -41,9 +41,10 @@ struct RecLayer {
   const float* G;         // hoisted pre-activations [T][Mt][B][16], or null
   const void* U;          // fused input: step t, batch b at U + t*u_slot + b*Kin (the layer
                           // below's exchange buffer, or x for layer 0), or null
-  void* X;                // this layer's exchange buffer: [T] slots of [B][H]
-  void* Xf;               // register-resident kernel only: h_t again, in the order its
-                          // readers load it (see lstm_rec_res.h), [T] slots of fslot elements
+  void* X;                // row-major h_t, [T] slots of [B][H]: the exchange buffer itself
+                          // when F is null, else a copy for a later input GEMM, or null
+  void* F;                // aligned path: h_t in load order (fragment blocks, see
+                          // lstm_rec.h), [T] slots of fslot elements, or null
   void* Yout;             // caller's y [T][B][H] (top layer), or null
   const void* h0;         // [B][H] or null (zeros)
   const float* c0;        // [B][H] or null (zeros)
@@ -53,6 +54,7 @@ struct RecLayer {
   const int* dep_flags;   // step counters of the producer of U in this launch, or null
   int dep_count;          // workgroups of that producer
   long long u_slot;       // elements between two steps of U
+  int ufrag;              // 1: U is the layer below's F (load order), else row-major
   int Kin;                // fused input width (0 when hoisted)
   int wg_begin, wg_count; // virtual workgroup ids owned by this layer
   int mt_per_wg;          // M-tiles per workgroup
@@ -63,7 +65,7 @@ struct RecLayer {
 struct RecParams {
   RecLayer layer[kMaxLayersPerLaunch];
   long long slot;         // elements between two steps of an exchange buffer
-  long long fslot;        // elements between two steps of Xf
+  long long fslot;        // elements between two steps of F
   int nlayers;
   int T, B, H, Mt, ncnt;  // ncnt = ceil(B/16) column tiles
   int cell;               // lstm_cell_t

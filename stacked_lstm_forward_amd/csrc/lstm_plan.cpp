@@ -221,6 +221,8 @@ int make_plan(const int32_t L, const int32_t I, const int32_t H, const int32_t B
   if (p.ncnt > 16) return kUnsupported;                     // B > 256
   if ((long long)L > 64) return kUnsupported;
   if ((long long)T * B > (1LL << 31) / 16 || (long long)H * 4 > (1LL << 30)) return kUnsupported;
+  // one step's h (a row-major exchange slot) stays below 4 GiB: kernels address it with 32-bit byte offsets
+  if ((long long)B * H * 4 >= (1LL << 32) || (long long)B * I * 4 >= (1LL << 32)) return kUnsupported;
 
   const int nch_h = cdiv(H, p.KC);
   const int nch_x = cdiv(I, p.KC);
@@ -270,19 +272,18 @@ int make_plan(const int32_t L, const int32_t I, const int32_t H, const int32_t B
   p.zero_ints = off / sizeof(int);
   p.G_off = off;
   off += align256((size_t)T * p.Mt * B * 16 * sizeof(float));
+  // exchange slots hold h_t of one step either row-major ([B][H]) or in load
+  // order (ncnt column tiles x nch chunks of 16 x KC), whichever is larger
   p.hist_off = off;
-  const size_t slot_bytes = ((size_t)B * H * p.dsize + kSlotAlign - 1) / kSlotAlign * kSlotAlign;
+  const size_t slot_raw = std::max((size_t)B * H, (size_t)p.ncnt * 16 * nch_h * p.KC) * p.dsize;
+  const size_t slot_bytes = (slot_raw + kSlotAlign - 1) / kSlotAlign * kSlotAlign;
   p.slot_elems = slot_bytes / p.dsize;
   off += (size_t)L * T * slot_bytes;
-  // the register-resident kernel's fragment-order copy of h: one layer at a
-  // time, so one set of T slots; sized from the shape alone, so the workspace
-  // does not depend on the device the plan is made for
+  // one layer's load-order exchange for layerwise runs (the row-major slots
+  // above then feed the next layer's input GEMM); one set of T slots, reused
+  // layer after layer
   p.xf_off = off;
-  if (resident_shape(p.bf16 != 0, nch_h, p.ncnt) && (H % p.KC) == 0) {
-    const size_t xf_bytes = align256((size_t)p.ncnt * 16 * H * p.dsize);
-    p.xf_slot_elems = xf_bytes / p.dsize;
-    off += (size_t)T * xf_bytes;
-  }
+  off += (size_t)T * slot_bytes;
   p.ws_bytes = off;
   return kStatusOk;
 }

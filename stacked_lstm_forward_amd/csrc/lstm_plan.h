@@ -52,7 +52,7 @@ struct Plan {
   // workspace layout (bytes)
   size_t err_off = 0, flags_off = 0, G_off = 0, hist_off = 0, ws_bytes = 0;
   size_t slot_elems = 0;  // elements between two steps of an exchange buffer
-  size_t xf_off = 0, xf_slot_elems = 0;  // fragment-order exchange buffer of the resident kernel
+  size_t xf_off = 0;    // one layer's load-order exchange (layerwise runs), T slots of slot_elems
   size_t zero_ints = 0; // ints zeroed at the start (error word + all step counters)
 };
 

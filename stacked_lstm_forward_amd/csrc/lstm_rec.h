@@ -129,8 +129,11 @@ struct RecShape {
   static constexpr int PD = kFit < 2 ? 2 : (kFit > 8 ? 8 : (kFit & ~1));
 };
 
-template <bool BF16, int MW, int NW, bool STREAM, bool VEC, int NWV>
+// FRAG (aligned path only): h_t is exchanged in load order through the F
+// buffers (see the addressing note below) instead of the row-major slots.
+template <bool BF16, int MW, int NW, bool STREAM, bool VEC, int NWV, bool FRAG>
 __global__ void __launch_bounds__(64 * NWV) lstm_rec_kernel(const RecParams P) {
+  static_assert(VEC || !FRAG, "the load-order exchange needs the aligned path");
   typedef typename Dt<BF16>::T T;
   constexpr int KC = Dt<BF16>::KC;
   constexpr int PD = RecShape<MW, NW, STREAM>::PD;
@@ -199,8 +202,19 @@ __global__ void __launch_bounds__(64 * NWV) lstm_rec_kernel(const RecParams P) {
   long arow[MW];  // caller weight row this lane loads for M-tile i (streamed weights; clamped)
   uint32_t mw_[MW], mr_[MW];  // 0 where that row has no input / recurrent weights (streamed fragment zeroed)
   int unit[MW], bcol[NW];     // first unit of this lane's rows; batch column
-  long boff[NW];  // element offset of this lane's row of h (clamped to a valid row)
-  long uoff[NW];  // ... and of its row of the fused input u (rows of Kin elements)
+  // B-operand (h, u) addressing.  A row-major source (x, h0, and every source
+  // off the aligned path): lane offset row * K + q * KC/8, chunk stride KC,
+  // half 1 at +KC/2.  A load-order source (the F buffers): lane offset
+  // lane * EPH, column tile n's blocks from n * nch_part * FB, chunk stride FB,
+  // half 1 at +FB/2 -- one load reads 1 KiB in one piece.
+  constexpr int FB = 2048 / Dt<BF16>::SZ;  // elements of one 2 KiB fragment block
+  constexpr int EPH = 16 / Dt<BF16>::SZ;   // elements of one lane's 16-byte half
+  // row-major byte offsets of this lane's two halves in h and u (rows clamped
+  // to valid ones; the planner keeps a slot below 4 GiB)
+  uint32_t hrow0[NW], hrow1[NW], urow0[NW], urow1[NW];
+  long boff[NW], uoff[NW];  // row-major element offsets of this lane's rows of h and u (!FRAG)
+  int nlc[NW];              // column tile of j, clamped (wave-uniform)
+  int fpos[MW];             // load-order position of this lane's unit in column tile 0
 #pragma unroll
   for (int i = 0; i < MW; ++i) {
     mloc[i] = gm + i * P.ntgm;
@@ -214,12 +228,21 @@ __global__ void __launch_bounds__(64 * NWV) lstm_rec_kernel(const RecParams P) {
     // LSTM / GRU: the lane's four rows are the four rows of unit 4*mt + q;
     // simple RNN: they are units 16*mt + 4*q + k, k = 0..3
     unit[i] = cell >= kCellRnnTanh ? 16 * (mt0 + mloc[i]) + 4 * q : 4 * (mt0 + mloc[i]) + q;
+    // (the simple RNN's four units share one 16-byte group and follow it)
+    const int kc = unit[i] % KC;
+    fpos[i] = (unit[i] / KC) * FB + (kc / (KC / 2)) * (FB / 2) + (((kc % (KC / 2)) / EPH) * 16 + (lane & 15)) * EPH +
+              kc % EPH;
   }
 #pragma unroll
   for (int j = 0; j < NW; ++j) {
     const int nloc = gn + j * P.ntgn;
     nval[j] = j < P.nw && nloc < P.ncnt;
     bcol[j] = 16 * nloc + (lane & 15);
+    nlc[j] = min(nloc, P.ncnt - 1);
+    hrow0[j] = (uint32_t)(min(bcol[j], B - 1) * H + q * (KC / 8)) * (uint32_t)Dt<BF16>::SZ;
+    hrow1[j] = hrow0[j] + (KC / 2) * Dt<BF16>::SZ;
+    urow0[j] = (uint32_t)(min(bcol[j], B - 1) * Kin + q * (KC / 8)) * (uint32_t)Dt<BF16>::SZ;
+    urow1[j] = urow0[j] + (KC / 2) * Dt<BF16>::SZ;
     boff[j] = (long)min(bcol[j], B - 1) * H;
     uoff[j] = (long)min(bcol[j], B - 1) * Kin;
   }
@@ -268,6 +291,15 @@ __global__ void __launch_bounds__(64 * NWV) lstm_rec_kernel(const RecParams P) {
   const T* Wp = reinterpret_cast<const T*>(LY(W));
   const T* Rp = reinterpret_cast<const T*>(LY(R));
   T* Xp = reinterpret_cast<T*>(LY(X));
+  T* Fp = FRAG ? reinterpret_cast<T*>(LY(F)) : nullptr;
+  const bool ufrag = FRAG && LY(ufrag);
+  // u's byte offsets for the whole launch (u's layout is fixed)
+  uint32_t ulo0[NW], ulo1[NW];
+#pragma unroll
+  for (int j = 0; j < NW; ++j) {
+    ulo0[j] = ufrag ? (uint32_t)(lane * 16) : urow0[j];
+    ulo1[j] = ufrag ? (uint32_t)(lane * 16 + 1024) : urow1[j];
+  }
   const T* Up = reinterpret_cast<const T*>(LY(U));
   const float* Gp = LY(G);
   // G offsets of this lane's tiles (clamped so every load is valid)
@@ -311,8 +343,18 @@ __global__ void __launch_bounds__(64 * NWV) lstm_rec_kernel(const RecParams P) {
 #pragma unroll
       for (int j = 0; j < NW; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const T* hsrc = t > 0 ? Xp + (long)(t - 1) * slot : reinterpret_cast<const T*>(LY(h0));
+    // h_{t-1}: the load-order buffer on the aligned path, else the row-major
+    // slot; at t = 0 the caller's row-major h0 (null: zero, no h part)
+    const bool hfrag = FRAG && t > 0;
+    const T* hsrc = t > 0 ? (hfrag ? Fp + (long)(t - 1) * P.fslot : Xp + (long)(t - 1) * slot)
+                          : reinterpret_cast<const T*>(LY(h0));
     const T* usrc = Kin ? Up + (long)t * LY(u_slot) : nullptr;
+    uint32_t hlo0[NW], hlo1[NW];
+#pragma unroll
+    for (int j = 0; j < NW; ++j) {
+      hlo0[j] = hfrag ? (uint32_t)(lane * 16) : hrow0[j];
+      hlo1[j] = hfrag ? (uint32_t)(lane * 16 + 1024) : hrow1[j];
+    }
 
     Frag rb[PD][NW];
     Frag ra[STREAM ? PD : 1][MW];
@@ -323,9 +365,24 @@ __global__ void __launch_bounds__(64 * NWV) lstm_rec_kernel(const RecParams P) {
       const int kk = (is_u ? c : c - nch_u) * KC;  // first column of the chunk
       const T* bsrc = is_u ? usrc : hsrc;
       const T* asrc = is_u ? Wp : Rp;
-      if (VEC) {
+      if (VEC && !FRAG) {
 #pragma unroll
         for (int j = 0; j < NW; ++j) b[j] = load_frag_vec<BF16>(bsrc + (is_u ? uoff[j] : boff[j]) + kk, q);
+      } else if (VEC) {
+        // a wave-uniform base per column tile plus per-lane byte offsets, so
+        // each half is one 16-byte load (base in scalar registers)
+        const bool fr = is_u ? ufrag : hfrag;
+        const int cc = is_u ? c : c - nch_u;
+        const int npart = is_u ? nch_u : nch_h;
+#pragma unroll
+        for (int j = 0; j < NW; ++j) {
+          const char* pj = reinterpret_cast<const char*>(bsrc + (fr ? (long)(nlc[j] * npart + cc) * FB : (long)kk));
+          const uint32_t o0 = is_u ? ulo0[j] : hlo0[j], o1 = is_u ? ulo1[j] : hlo1[j];
+          b[j].v[0] = *reinterpret_cast<const uint4*>(pj + o0);
+          b[j].v[1] = *reinterpret_cast<const uint4*>(pj + o1);
+        }
+      }
+      if (VEC) {
         if (STREAM) {
 #pragma unroll
           for (int i = 0; i < MW; ++i) {
@@ -435,7 +492,10 @@ __global__ void __launch_bounds__(64 * NWV) lstm_rec_kernel(const RecParams P) {
     stamp(t, 3);
 
     // ---- gates, cell update, outputs
-    T* xout = Xp + (long)t * slot;
+    // the exchange: the load-order buffer (plus the row-major copy when a
+    // later input GEMM reads it), else the row-major slot itself
+    T* fout = Fp ? Fp + (long)t * P.fslot : nullptr;
+    T* xout = FRAG ? (Xp ? Xp + (long)t * slot : nullptr) : Xp + (long)t * slot;
     T* yout = LY(Yout) ? reinterpret_cast<T*>(LY(Yout)) + (long)t * B * H : nullptr;
     const bool last = (t == T_ - 1);
 #pragma unroll
@@ -445,13 +505,18 @@ __global__ void __launch_bounds__(64 * NWV) lstm_rec_kernel(const RecParams P) {
         if (!live(i, j)) continue;
         const f32x4 p = acc[i][j] + (Gp ? gq[i][j] : breg[i]);
         const long o = (long)bcol[j] * H + unit[i];
-        auto emit = [&](long oo, float h) {  // h_t to the exchange slot, y and (last step) hT
+        // the exchange (write-through) and, beside a load-order exchange, the
+        // row-major copy a later input GEMM reads
+        T* const dst = FRAG ? fout + (long)(bcol[j] >> 4) * nch_h * FB + fpos[i] : xout + o;
+        T* const cpy = FRAG ? xout : nullptr;
+        auto emit = [&](int k, float h) {  // h_t to the exchange, y and (last step) hT
           const T hv = from_float<BF16>(h);
-          store_coherent<BF16>(xout + oo, hv);
-          if (yout) yout[oo] = hv;
-          if (last && LY(hT)) reinterpret_cast<T*>(LY(hT))[oo] = hv;
+          store_coherent<BF16>(dst + k, hv);
+          if (cpy) cpy[o + k] = hv;
+          if (yout) yout[o + k] = hv;
+          if (last && LY(hT)) reinterpret_cast<T*>(LY(hT))[o + k] = hv;
         };
-        cell_update(cell, p, creg[i][j], H - unit[i], [&](int k, float h) { emit(o + k, h); });
+        cell_update(cell, p, creg[i][j], H - unit[i], emit);
         if (cell == kCellLstm && last && LY(cT)) LY(cT)[o] = creg[i][j];
       }
     stamp(t, 4);

@@ -149,7 +149,7 @@ lstm_rec_res_kernel(const RecParams P) {
   };
 
   T* Xp = reinterpret_cast<T*>(Lr.X);
-  T* Xf = reinterpret_cast<T*>(Lr.Xf);
+  T* Xf = reinterpret_cast<T*>(Lr.F);
   const float* Gp = Lr.G;
 
   for (int t = 0; t < T_; ++t) {
@@ -179,6 +179,7 @@ lstm_rec_res_kernel(const RecParams P) {
     T* fout = Xf + (long)t * P.fslot;
     // row-major copy: y for the top layer, else the next layer's input
     T* rout = Lr.Yout ? reinterpret_cast<T*>(Lr.Yout) + (long)t * B * H : Xp + (long)t * slot;
+    // (the host gives every resident layer either y or a row-major X)
     const bool last = (t == T_ - 1);
 
 #pragma unroll

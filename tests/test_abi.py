@@ -81,12 +81,13 @@ def test_workspace_size_formula():
         n = sl.lstm_fwd_workspace_size(d)
         ds = 2 if c.dtype == "bf16" else 4
         mt = (c.H + 3) // 4
-        slot = -(-c.B * c.H * ds // 256) * 256  # exchange slots start on 256-byte boundaries
-        expect = 256 + c.L * 1024 * 128 + c.T * mt * c.B * 16 * 4 + c.L * c.T * slot
-        if c.dtype == "bf16" and c.H == 4096 and c.B <= 32:
-            # the register-resident kernel's copy of h in load order: T slots of
-            # (B rounded up to 16) x H
-            expect += c.T * (-(-c.B // 16) * 16 * c.H * ds)
+        kc = 64 if c.dtype == "bf16" else 32
+        # an exchange slot holds h_t row-major ([B][H]) or in load order (16-column
+        # tiles x 16 x KC chunks), whichever is larger, from a 256-byte boundary
+        elems = max(c.B * c.H, -(-c.B // 16) * 16 * -(-c.H // kc) * kc)
+        slot = -(-elems * ds // 256) * 256
+        # L x T exchange slots, plus T slots of one layer's load-order exchange
+        expect = 256 + c.L * 1024 * 128 + c.T * mt * c.B * 16 * 4 + c.L * c.T * slot + c.T * slot
         assert expect <= n <= expect + 4 * 256, (name, n, expect)
 
 

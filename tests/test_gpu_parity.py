@@ -79,6 +79,34 @@ def test_tiny_shapes(dev, shape, dtype, regime):
     check_close(got, ref, TOL[dtype], f"tiny {shape} {dtype} r{regime}")
 
 
+# ----------------------------------------------------------------------------- load-order exchange
+# Aligned shapes (H a multiple of the chunk width) with B >= 16 exchange h in
+# load order: ragged last column tile (B = 40), layerwise runs whose next layer's
+# input GEMM reads the row-major copy, a wavefront of 18 layers in two launches
+# (layer 16 reads layer 15's load-order buffer), and B = 8, which keeps the
+# row-major exchange on the aligned path.
+ALIGNED = [
+    # L, I, H, B, T
+    (3, 64, 128, 40, 5),
+    (2, 96, 64, 16, 4),
+    (18, 32, 64, 16, 3),
+    (2, 64, 128, 8, 5),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", ALIGNED)
+@pytest.mark.parametrize("regime", [1, 2])
+def test_aligned_exchange(dev, shape, dtype, regime):
+    L, I, H, B, T = shape
+    cfg = li.custom_config(L, I, H, B, T, dtype, cfg_id=200 + L + B)
+    inp = li.make_inputs(cfg, random_state=True)
+    say(f"aligned {shape} {dtype} regime={regime}")
+    got = run_gpu(inp, dev, regime=regime)
+    ref = orc.lstm_forward_inputs(inp)
+    check_close(got, ref, TOL[dtype], f"aligned {shape} {dtype} r{regime}")
+
+
 # ----------------------------------------------------------------------------- the five workloads
 @pytest.mark.parametrize("name", ["c1", "c2", "c3", "c5"])
 def test_workload_full(dev, name):
