@@ -178,7 +178,7 @@ __global__ void __launch_bounds__(kGemmThreads) lstm_input_gemm(const GemmParams
 }
 
 // Fast path of the input projection (K a whole number of chunks, every row
-// 16-byte aligned, no rows without input weights): a 256 x 256 workgroup
+// 16-byte aligned): a 256 x 256 workgroup
 // tile, 4 waves of 128 x 128 (8 x 8 MFMA tiles, accumulators in the
 // accumulation registers).  Operands go from global memory straight into LDS
 // with the gfx950 direct-to-LDS loads (a wave-wide 16-byte load lands lane l
@@ -317,11 +317,14 @@ __global__ void __launch_bounds__(kGemmThreads) lstm_input_gemm_dma(const GemmPa
   for (int i = 0; i < 8; ++i) {
     const int mt = mtb + 8 * wm + i;
     if (mt >= P.Mt) continue;
-    f32x4 bv;  // this lane's four rows 4*(lane/16) + k of the tile (rows past H are never read)
+    f32x4 bv;       // this lane's four rows 4*(lane/16) + k of the tile (rows past H are never read)
+    bool wrow[4];   // false: the row has no input weights (the GRU's recurrent half of n), so its
+                    // product (of a clamped stand-in row) is dropped and G holds the bias alone
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const int bi = cell_row(P.cell, mt, 4 * q + k, P.H).bi;
-      bv[k] = bi >= 0 ? to_float(bias[bi]) : 0.f;
+      const CellRow cr = cell_row(P.cell, mt, 4 * q + k, P.H);
+      bv[k] = cr.bi >= 0 ? to_float(bias[cr.bi]) : 0.f;
+      wrow[k] = cr.w >= 0;
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -329,7 +332,10 @@ __global__ void __launch_bounds__(kGemmThreads) lstm_input_gemm_dma(const GemmPa
       if (col >= P.N) continue;
       const long t = col / P.B, bb = col % P.B;
       float* dst = P.G + ((t * P.Mt + mt) * P.B + bb) * 16 + 4 * q;
-      *reinterpret_cast<f32x4*>(dst) = acc[i][j] + bv;
+      f32x4 g;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) g[k] = wrow[k] ? acc[i][j][k] + bv[k] : bv[k];
+      *reinterpret_cast<f32x4*>(dst) = g;
     }
   }
 }
@@ -372,7 +378,7 @@ hipError_t launch_input_gemm(bool bf16, const GemmParams& p, hipStream_t s) {
   // the 256 x 256 direct-to-LDS kernel pays off on long K (measured: 0.45 vs
   // 0.53 ms at K = 4096, 0.33 vs 0.35 ms at K = 1536); short K keeps the
   // register-staged 256 x 128 kernel, whose smaller tiles fill more CUs
-  if (p.vec_ok_w && p.vec_ok_u && whole && p.cell != kCellGru && p.K >= 1024) {
+  if (p.vec_ok_w && p.vec_ok_u && whole && p.K >= 1024) {
     const unsigned lds = 2 * kDmaStage * sizeof(uint4);
     const void* fn = bf16 ? reinterpret_cast<const void*>(&lstm_input_gemm_dma<true>)
                           : reinterpret_cast<const void*>(&lstm_input_gemm_dma<false>);

@@ -80,7 +80,7 @@ def test_cells_workload_shapes(dev, cell, name):
 
 @pytest.mark.parametrize("cell", CELLS)
 def test_cells_large_hidden_sampled(dev, cell):
-    """c4 shapes (H = 4096, weights streamed): the oracle runs on 4 sampled sequences."""
+    """c4 shapes (H = 4096, recurrent weights in registers and LDS): the oracle runs on 4 sampled sequences."""
     cfg = li.with_cell(li.CONFIGS["c4"], cell)
     cfg = li.Config(cfg.name + "-T12", cfg.cfg_id, cfg.L, cfg.I, cfg.H, cfg.B, 12, cfg.dtype, cell)
     inp = li.make_inputs(cfg)
