@@ -291,25 +291,27 @@ __global__ void __launch_bounds__(kGemmThreads) lstm_input_gemm_dma(const GemmPa
     // after the barrier everybody's have, and nobody still reads buffer (c+1)&1
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (c + 1 < nch) stage_load(c + 1, (c + 1) & 1);
-    // operand reads from LDS run two tile rows ahead of the MFMAs that use
-    // them (the scheduling barriers keep that order), so the matrix pipe starts
-    // after the B fragments and two A fragments instead of after all sixteen
+    // Every operand of chunk c is read from LDS before chunk c+1's loads are
+    // issued: the compiler cannot tell that those loads fill the other buffer,
+    // and an LDS read issued after them would first wait for all of them,
+    // which would serialise each chunk's loads with the previous chunk's MFMAs.
     const uint4* st = lds + (c & 1) * kDmaStage;
     Frag a[8], b[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) b[j] = frag_at(st + (kDmaTiles + 8 * wn + j) * 128);
-    a[0] = frag_at(st + (8 * wm + 0) * 128);
-    a[1] = frag_at(st + (8 * wm + 1) * 128);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = frag_at(st + (8 * wm + i) * 128);
+    // (unconditional, so no branch separates the reads from the MFMAs: the last
+    // iteration loads its own chunk again into the idle buffer)
+    __builtin_amdgcn_sched_barrier(0);
+    stage_load(min(c + 1, nch - 1), (c + 1) & 1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (i + 2 < 8) a[i + 2] = frag_at(st + (8 * wm + i + 2) * 128);
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int j = 0; j < 8; ++j) mfma_frag<BF16>(acc[i][j], a[i], b[j]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
   }
+  __builtin_amdgcn_s_waitcnt(0);  // the last (redundant) loads have landed
 
   // epilogue: add bias, write [T][Mt][B][16]
   const T* bias = reinterpret_cast<const T*>(P.bias);
