@@ -107,6 +107,29 @@ def test_aligned_exchange(dev, shape, dtype, regime):
     check_close(got, ref, TOL[dtype], f"aligned {shape} {dtype} r{regime}")
 
 
+# ----------------------------------------------------------------------------- direct-to-LDS input GEMM
+# K >= 1024 with aligned rows takes the 256 x 256 direct-to-LDS GEMM: a partial
+# M-block (H = 40: 10 M-tiles of 16), a ragged column tile (T * B = 15) and,
+# for the GRU, rows without input weights dropped in its epilogue.
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("cell", ["lstm", "gru"])
+def test_input_gemm_direct_to_lds_ragged(dev, dtype, cell):
+    cfg = li.custom_config(1, 1024, 40, 3, 5, dtype, cfg_id=61, cell=cell)
+    inp = li.make_inputs(cfg, random_state=True)
+    say(f"input GEMM K=1024 H=40 B=3 T=5 {dtype} {cell}")
+    got = run_gpu(inp, dev)
+    ref = orc.forward_inputs(inp)
+    if cell != "lstm":
+        got, ref = got[:2] + (None,), ref[:2] + (None,)
+    names = ("y", "hT", "cT")
+    for n, g, r in zip(names, got, ref):
+        if r is None:
+            continue
+        e = rel_err(g, r)
+        say(f"  {n}={e:.2e}")
+        assert np.all(np.isfinite(g)) and e <= TOL[dtype], (cell, dtype, n, e)
+
+
 # ----------------------------------------------------------------------------- the five workloads
 @pytest.mark.parametrize("name", ["c1", "c2", "c3", "c5"])
 def test_workload_full(dev, name):
