@@ -202,6 +202,10 @@ typedef struct {
                                 input product W_l u_t is fused into its recurrent steps          */
   int32_t weight_blocks_in_registers; /* 2 KiB weight blocks each wave of the first recurrent
                                 launch keeps in registers (0: weights in LDS only, or streamed) */
+  int32_t data_valid_exchange; /* 1 if the first recurrent launch exchanges h_t without step
+                                counters: its slots start filled with all-ones words and readers
+                                re-read h_{t-1} until no element holds that pattern (small
+                                single-layer grids; assumes 16-byte aligned caller buffers)     */
 } lstm_plan_info_t;
 
 /*

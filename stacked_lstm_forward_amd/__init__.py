@@ -59,7 +59,7 @@ class PlanInfo(ctypes.Structure):
                 ("tile_groups_m", ctypes.c_int32), ("tile_groups_n", ctypes.c_int32),
                 ("wave_tiles_m", ctypes.c_int32), ("wave_tiles_n", ctypes.c_int32),
                 ("weights_streamed", ctypes.c_int32), ("input_gemms", ctypes.c_int32),
-                ("weight_blocks_in_registers", ctypes.c_int32)]
+                ("weight_blocks_in_registers", ctypes.c_int32), ("data_valid_exchange", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
         n = self.layers_per_launch
@@ -71,7 +71,8 @@ class PlanInfo(ctypes.Structure):
                 "tile_groups": [self.tile_groups_m, self.tile_groups_n],
                 "wave_tiles": [self.wave_tiles_m, self.wave_tiles_n],
                 "weights_streamed": bool(self.weights_streamed), "input_gemms": self.input_gemms,
-                "weight_blocks_in_registers": self.weight_blocks_in_registers}
+                "weight_blocks_in_registers": self.weight_blocks_in_registers,
+                "data_valid_exchange": bool(self.data_valid_exchange)}
 
 
 class LstmError(RuntimeError):

@@ -214,11 +214,57 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// ---------------------------------------------------------------------------
+// Data-valid exchange: a slot starts as all-ones words, which no stored value
+// can equal once NaNs are canonical, so a reader knows an element has been
+// written when it no longer holds the all-ones pattern.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kSentinelWord = 0xffffffffu;
+
+// A raw buffer over `bytes` bytes at p (loads past the end return zeros).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
+}
+
+// 16 bytes at byte offset `off` of the buffer with the agent-coherence bit
+// (sc1), the cache policy of agent-scope atomic loads: a re-read sees the
+// writers' later stores instead of a stale cached copy.  One wave-wide load
+// of contiguous lanes is still coalesced.
+__device__ __forceinline__ uint4 load16_coherent(__amdgpu_buffer_rsrc_t r, int off) {
+  constexpr int kSc1 = 16;  // cache-policy operand bit of sc1
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kSc1));
+}
+
+// 1 if no element of the 16 bytes still holds the unwritten pattern
+template <bool BF16>
+__device__ __forceinline__ int written16(const uint4 v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  int ok = 1;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (BF16)
+      ok &= ((w[e] & 0xffffu) != 0xffffu && (w[e] >> 16) != 0xffffu) ? 1 : 0;
+    else
+      ok &= (w[e] != kSentinelWord) ? 1 : 0;
+  }
+  return ok;
+}
+
 template <bool BF16>
 __device__ __forceinline__ typename Dt<BF16>::T from_float(float f);
 template <>
 __device__ __forceinline__ float from_float<false>(float f) { return f; }
 template <>
 __device__ __forceinline__ uint16_t from_float<true>(float f) { return f32_to_bf16(f); }
+
+// the value with any NaN replaced by the canonical quiet NaN (never all ones)
+template <bool BF16>
+__device__ __forceinline__ typename Dt<BF16>::T canon_nan(typename Dt<BF16>::T v);
+template <>
+__device__ __forceinline__ float canon_nan<false>(float v) { return v == v ? v : __uint_as_float(0x7fc00000u); }
+template <>
+__device__ __forceinline__ uint16_t canon_nan<true>(uint16_t v) {
+  return (v & 0x7fffu) > 0x7f80u ? (uint16_t)0x7fc0u : v;
+}
 
 }  // namespace lstm

@@ -129,6 +129,7 @@ lstm_status_t lstm_fwd_plan(const lstm_desc_t* d, int32_t force_regime, int32_t 
   out->weights_streamed = p.rec[0].stream;
   out->input_gemms = p.ngemm;
   out->weight_blocks_in_registers = p.rec[0].res_nrb;
+  out->data_valid_exchange = data_valid_lds(p, p.rec[0], d->H, d->B, info) > 0 ? 1 : 0;
   return LSTM_OK;
 }
 
@@ -218,7 +219,7 @@ lstm_status_t lstm_fwd_ex(const lstm_desc_t* d, const void* x, const void* h0, c
     return true;
   };
 
-  auto gemm = [&](int l, const void* U, long long u_slot, int K, bool zero) -> lstm_status_t {
+  auto gemm = [&](int l, const void* U, long long u_slot, int K, bool zero, void* fill) -> lstm_status_t {
     GemmParams gp;
     gp.W = W_l(l);
     gp.U = U;
@@ -227,6 +228,8 @@ lstm_status_t lstm_fwd_ex(const lstm_desc_t* d, const void* x, const void* h0, c
     gp.G = G;
     gp.zero_ptr = zero ? reinterpret_cast<int*>(wsb) : nullptr;
     gp.zero_count = zero ? (int)p.zero_ints : 0;
+    gp.fill_ptr = static_cast<unsigned*>(fill);
+    gp.fill_count = fill ? (long long)((size_t)T * slot * ds / 4) : 0;
     gp.K = K;
     gp.H = H;
     gp.Mt = p.Mt;
@@ -263,6 +266,13 @@ lstm_status_t lstm_fwd_ex(const lstm_desc_t* d, const void* x, const void* h0, c
   if (p.regime == LSTM_REGIME_WAVEFRONT)
     for (int r = 0; r < p.nrec; ++r) wave_vec = wave_vec && launch_vec(p.rec[r]);
 
+  // Data-valid exchange (lstm_rec.h, data_valid_lds in lstm_plan.h) when the
+  // launch's buffers allow it: its LDS bytes, or 0.
+  auto sent_lds = [&](const LaunchPlan& lp) -> int {
+    const int need = data_valid_lds(p, lp, H, B, dev.info);
+    return (need && launch_vec(lp) && (size_t)slot * ds < (1u << 31)) ? need : 0;
+  };
+
   bool traced = false;  // only the first recurrent launch is traced
   auto rec = [&](const LaunchPlan& lp) -> lstm_status_t {
     RecParams rp;
@@ -283,6 +293,12 @@ lstm_status_t lstm_fwd_ex(const lstm_desc_t* d, const void* x, const void* h0, c
     rp.trace_wgs = tr ? opts->trace_wgs : 0;
     rp.trace_stride = (tr && opts->trace_stride > 0) ? opts->trace_stride : 1;
     traced = traced || tr;
+    int lds = lp.lds_bytes;
+    rp.sent = 0, rp.red_stride = 0;
+    if (const int need = sent_lds(lp)) {
+      rp.sent = 1, rp.red_stride = ((lp.lds_bytes - lp.red_off) + 255) & ~255;
+      lds = need;
+    }
     for (int k = 0; k < lp.nlayers; ++k) {
       const LayerPlan& pl = lp.layers[k];
       const int l = pl.layer;
@@ -342,14 +358,20 @@ lstm_status_t lstm_fwd_ex(const lstm_desc_t* d, const void* x, const void* h0, c
     int per_cu = 0;
     const bool res = lp.res_nrb > 0;
     if (res && !vec) return LSTM_ERR_UNSUPPORTED;  // planned only for aligned rows
-    const hipError_t pe = res ? res_prepare(bf16, lp.mw, lp.nw, lp.res_nci, lp.res_nrb, lp.lds_bytes, &per_cu)
-                              : rec_prepare(bf16, lp.stream, vec, frag, lp.nwaves, lp.mw, lp.nw, lp.lds_bytes, &per_cu);
+    hipError_t pe = res ? res_prepare(bf16, lp.mw, lp.nw, lp.res_nci, lp.res_nrb, lp.lds_bytes, &per_cu)
+                        : rec_prepare(bf16, lp.stream, vec, frag, lp.nwaves, lp.mw, lp.nw, lds, &per_cu);
+    if (pe == hipSuccess && rp.sent && (long long)per_cu * dev.info.num_cus < lp.grid) {
+      // the second reduction area costs co-residency: step counters instead
+      // (the filled slots are then simply overwritten)
+      rp.sent = 0, rp.red_stride = 0, lds = lp.lds_bytes;
+      pe = rec_prepare(bf16, lp.stream, vec, frag, lp.nwaves, lp.mw, lp.nw, lds, &per_cu);
+    }
     if (pe != hipSuccess) return LSTM_ERR_HIP;
     if ((long long)per_cu * dev.info.num_cus < lp.grid) return LSTM_ERR_UNSUPPORTED;  // not co-resident
     if (!before(LSTM_KERNEL_RECURRENT)) return LSTM_ERR_HIP;
     const bool plain = opts && opts->plain_launch;
     const hipError_t le = res ? launch_rec_res(bf16, lp.res_nci, lp.res_nrb, rp, lp.lds_bytes, plain, stream)
-                              : launch_rec(bf16, lp.stream, vec, frag, lp.nwaves, rp, lp.lds_bytes, plain, stream);
+                              : launch_rec(bf16, lp.stream, vec, frag, lp.nwaves, rp, lds, plain, stream);
     if (le != hipSuccess) return LSTM_ERR_HIP;
     if (!after()) return LSTM_ERR_HIP;
     return LSTM_OK;
@@ -357,7 +379,7 @@ lstm_status_t lstm_fwd_ex(const lstm_desc_t* d, const void* x, const void* h0, c
 
   if (p.ngemm > 0) {
     // layer 0 input projection (+ zeroing of the error word and step counters)
-    st = gemm(0, x, (long long)B * I, I, true);
+    st = gemm(0, x, (long long)B * I, I, true, (p.regime != LSTM_REGIME_WAVEFRONT && sent_lds(p.rec[0])) ? xbuf(0) : nullptr);
     if (st != LSTM_OK) return st;
   } else {
     // every input product is fused into the steps: only the counters need clearing
@@ -373,7 +395,7 @@ lstm_status_t lstm_fwd_ex(const lstm_desc_t* d, const void* x, const void* h0, c
   } else {
     for (int l = 0; l < L; ++l) {
       if (l > 0) {
-        st = gemm(l, xbuf(l - 1), (long long)slot, H, false);
+        st = gemm(l, xbuf(l - 1), (long long)slot, H, false, sent_lds(p.rec[l]) ? xbuf(l) : nullptr);
         if (st != LSTM_OK) return st;
       }
       st = rec(p.rec[l]);

@@ -70,6 +70,11 @@ __global__ void __launch_bounds__(kGemmThreads) lstm_input_gemm(const GemmParams
     const long wg = (long)blockIdx.y * gridDim.x + blockIdx.x;
     for (long i = wg * kGemmThreads + tid; i < P.zero_count; i += nwg * kGemmThreads) P.zero_ptr[i] = 0;
   }
+  if (P.fill_ptr) {  // grid-stride: the unwritten pattern of a data-valid exchange
+    const long nwg = (long)gridDim.x * gridDim.y;
+    const long wg = (long)blockIdx.y * gridDim.x + blockIdx.x;
+    for (long i = wg * kGemmThreads + tid; i < P.fill_count; i += nwg * kGemmThreads) P.fill_ptr[i] = kSentinelWord;
+  }
   const int mtb = blockIdx.y * MTW;        // first M-tile of this workgroup
   const int n0 = blockIdx.x * kGemmTileN;  // first column
   const int nch = (P.K + KC - 1) / KC;
@@ -204,6 +209,11 @@ __global__ void __launch_bounds__(kGemmThreads) lstm_input_gemm_dma(const GemmPa
     const long nwg = (long)gridDim.x * gridDim.y;
     const long wg = (long)blockIdx.y * gridDim.x + blockIdx.x;
     for (long i = wg * kGemmThreads + tid; i < P.zero_count; i += nwg * kGemmThreads) P.zero_ptr[i] = 0;
+  }
+  if (P.fill_ptr) {  // grid-stride: the unwritten pattern of a data-valid exchange
+    const long nwg = (long)gridDim.x * gridDim.y;
+    const long wg = (long)blockIdx.y * gridDim.x + blockIdx.x;
+    for (long i = wg * kGemmThreads + tid; i < P.fill_count; i += nwg * kGemmThreads) P.fill_ptr[i] = kSentinelWord;
   }
   // Tile order: the 1-D grid (a multiple of 8) goes round-robin over the 8
   // XCDs, so workgroup ids are first regrouped into one contiguous range per

@@ -26,6 +26,8 @@ struct GemmParams {
   const void* bias;  // [4H]
   float* G;          // [T][Mt][B][16]
   int* zero_ptr;     // if non-null: workgroup 0 zeroes zero_count ints first (flags, error word)
+  unsigned* fill_ptr;     // if non-null: fill_count words set to all ones first (the exchange
+  long long fill_count;   // slots of the data-valid recurrent launch that follows)
   long long u_slot;  // elements between two steps of U
   int zero_count;
   int K, H, Mt, B, N;  // N = T*B
@@ -79,6 +81,10 @@ struct RecParams {
   long long timeout_ticks;  // per-wait limit in wall-clock ticks
   long long* trace;       // optional per-step phase timestamps (see lstm_fwd_opts_t), or null
   int trace_wgs, trace_stride;
+  int sent;               // 1: data-valid exchange (single hoisted layer, row-major slots): the
+                          // slots start filled with all-ones words, h_t is written without a step
+                          // counter and readers poll the data itself (see lstm_rec.h)
+  int red_stride;         // bytes between the two step-parity copies of the reduction area (sent)
 };
 
 }  // namespace lstm

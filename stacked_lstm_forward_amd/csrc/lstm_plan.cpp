@@ -288,4 +288,15 @@ int make_plan(const int32_t L, const int32_t I, const int32_t H, const int32_t B
   return kStatusOk;
 }
 
+int data_valid_lds(const Plan& p, const LaunchPlan& lp, int H, int B, const DeviceInfo& dev) {
+  if (p.regime == kRegimeWavefront || lp.nlayers != 1 || lp.res_nrb > 0 || lp.stream || lp.ks < 2) return 0;
+  if (lp.nwaves != 4 || lp.mw != 1 || lp.nw != 1) return 0;  // the one instantiation that has it
+  const LayerPlan& pl = lp.layers[0];
+  if (!pl.hoisted || !pl.staged || B >= 16 || pl.wg_count > kSentMaxWgs) return 0;
+  if (H % p.KC != 0 || ((size_t)H * p.dsize) % 16 != 0 || cdiv(pl.nch, lp.ks) > 6) return 0;
+  const int red = lp.lds_bytes - lp.red_off;
+  const int need = lp.red_off + ((red + 255) & ~255) + red;
+  return need + kLdsReserve <= dev.lds_per_block ? need : 0;
+}
+
 }  // namespace lstm

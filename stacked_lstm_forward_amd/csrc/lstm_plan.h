@@ -56,6 +56,19 @@ struct Plan {
   size_t zero_ints = 0; // ints zeroed at the start (error word + all step counters)
 };
 
+// Data-valid exchange (lstm_rec.h): recurrent launch `lp` qualifies when it
+// runs one hoisted layer whose weight rows stay in LDS, splits the K range
+// over waves (the split's barrier is the step's only one), loads all of a
+// wave's chunks at once (at most 6 per wave with one column tile), exchanges
+// h in row-major slots (batch below one 16-column tile, whole 16-byte rows)
+// and has at most kSentMaxWgs workgroups: every reader re-reads the whole
+// slot until it is complete, which measured faster than step counters up to
+// 64 workgroups and slower from 128 (one layer, B = 4 and 8, bf16 and fp32).
+// Returns the launch's LDS bytes (its reduction area once per step parity) or
+// 0.  The caller adds the conditions on its buffers (16-byte aligned rows).
+constexpr int kSentMaxWgs = 64;
+int data_valid_lds(const Plan& p, const LaunchPlan& lp, int H, int B, const DeviceInfo& dev);
+
 // Returns 0 on success, else an lstm_status_t.
 // `aligned`: the caller's R (and h0) allow 16-byte loads; the register-resident
 // kernel needs it.

@@ -139,6 +139,7 @@ __global__ void __launch_bounds__(64 * NWV) lstm_rec_kernel(const RecParams P) {
   constexpr int PD = RecShape<MW, NW, STREAM>::PD;
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int s_ok;
+  __shared__ int s_abort[2];  // data-valid exchange: a wave gave up waiting in a step of this parity
 
   // The layer table is read in place from the kernel-argument segment with a
   // wave-uniform index (scalar loads); copying one entry out of the by-value
@@ -174,6 +175,16 @@ __global__ void __launch_bounds__(64 * NWV) lstm_rec_kernel(const RecParams P) {
   const int q = lane >> 4;
   const int cell = P.cell;
   uint4* As = reinterpret_cast<uint4*>(smem);  // fragment block (m, c) at As + (m * nch + c) * 128
+  // Data-valid exchange (one hoisted layer, row-major slots, every chunk of a
+  // wave loaded at once): no step counters.  The host fills the slots with
+  // all-ones words; a reader re-reads its chunks of h_{t-1} with coherent
+  // loads until none holds that pattern, a writer stores h_t (NaNs made
+  // canonical) and moves on without waiting for its stores.  The K-split
+  // partial sums alternate between two LDS areas by step parity, so no
+  // barrier closes a step.
+  constexpr bool kSentCode = VEC && !STREAM && !FRAG && NWV == 4 && MW == 1 && NW == 1;
+  const bool sent = kSentCode && P.sent && ks > 1 && Kin == 0 && LY(staged) && (nch + ks - 1) / ks <= PD;
+  if (tid == 0) s_abort[0] = s_abort[1] = 0;
 
   // ---- keep this workgroup's weight rows on chip for the whole sequence
   if (!STREAM && LY(staged)) {
@@ -324,7 +335,7 @@ __global__ void __launch_bounds__(64 * NWV) lstm_rec_kernel(const RecParams P) {
     }
 
     // ---- wait for h^l_{t-1} (own layer) and h^{l-1}_t (producer in this launch)
-    const int* own = t > 0 ? LY(flags) : nullptr;
+    const int* own = (t > 0 && !sent) ? LY(flags) : nullptr;
     const int* dep = LY(dep_flags);
     if (own || dep) {
       if (wave == 0) {
@@ -460,14 +471,68 @@ __global__ void __launch_bounds__(64 * NWV) lstm_rec_kernel(const RecParams P) {
 
     // a null h_{t-1} (t = 0 without h0) is zero: only the input chunks remain
     const int c_end = hsrc ? nch : nch_u;
-    products(kg, c_end > kg ? (c_end - kg + ks - 1) / ks : 0);
+    if (kSentCode && sent && t > 0) {
+      // this wave's chunks c = kg + s * ks, s < n (n <= PD), re-read until
+      // every element of every one has been written, then multiplied
+      const int n = nch > kg ? (nch - kg + ks - 1) / ks : 0;
+      Frag hb[PD][NW];
+      if (n > 0) {
+        const long long t0 = wall_clock64();
+        const __amdgpu_buffer_rsrc_t hb_rsrc = raw_buffer(hsrc, (int)(slot * (long)sizeof(T)));
+        while (true) {
+#pragma unroll
+          for (int s = 0; s < PD; ++s)
+            if (s < n) {
+              const int c = kg + s * ks;
+#pragma unroll
+              for (int j = 0; j < NW; ++j) {
+                const int e = (int)boff[j] + c * KC;  // element offset of the chunk in this lane's row
+                hb[s][j].v[0] = load16_coherent(hb_rsrc, (e + frag_col<BF16>(q, 0)) * (int)sizeof(T));
+                hb[s][j].v[1] = load16_coherent(hb_rsrc, (e + frag_col<BF16>(q, 1)) * (int)sizeof(T));
+              }
+            }
+          int ok = 1;
+#pragma unroll
+          for (int s = 0; s < PD; ++s)
+            if (s < n) {
+#pragma unroll
+              for (int j = 0; j < NW; ++j) ok &= written16<BF16>(hb[s][j].v[0]) & written16<BF16>(hb[s][j].v[1]);
+            }
+          if (__all(ok)) break;
+          if (__hip_atomic_load(P.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0 ||
+              wall_clock64() - t0 > P.timeout_ticks) {
+            // give up: the workgroup leaves together after the combine barrier
+            if (lane == 0) {
+              __hip_atomic_store(P.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              s_abort[t & 1] = 1;
+            }
+            break;
+          }
+        }
+#pragma unroll
+        for (int s = 0; s < PD; ++s)
+          if (s < n) {
+            const int c = kg + s * ks;
+            Frag a[MW];
+#pragma unroll
+            for (int i = 0; i < MW; ++i) a[i] = lds_get(As + (mblk[i] * nch + c) * 128, lane);
+#pragma unroll
+            for (int i = 0; i < MW; ++i)
+#pragma unroll
+              for (int j = 0; j < NW; ++j)
+                if (mval[i] && nval[j]) mfma_frag<BF16>(acc[i][j], a[i], hb[s][j]);
+          }
+      }
+    } else {
+      products(kg, c_end > kg ? (c_end - kg + ks - 1) / ks : 0);
+    }
     stamp(t, 2);
     stamp_clk(t, 7);
 
     // ---- combine the K-split partial sums: tile e is finalised by K-group
     // e % ks; every other K-group of its tile group leaves one partial in LDS
     if (ks > 1) {
-      f32x4* red = reinterpret_cast<f32x4*>(smem + P.red_off);
+      f32x4* red = reinterpret_cast<f32x4*>(smem + P.red_off + (sent ? (t & 1) * P.red_stride : 0));
       const int tpg = P.mw * P.nw;
 #pragma unroll
       for (int i = 0; i < MW; ++i)
@@ -480,6 +545,7 @@ __global__ void __launch_bounds__(64 * NWV) lstm_rec_kernel(const RecParams P) {
           red[((tg * tpg + e) * (ks - 1) + slot_r) * 64 + lane] = acc[i][j];
         }
       __syncthreads();
+      if (sent && s_abort[t & 1]) return;
 #pragma unroll
       for (int i = 0; i < MW; ++i)
 #pragma unroll
@@ -510,7 +576,7 @@ __global__ void __launch_bounds__(64 * NWV) lstm_rec_kernel(const RecParams P) {
         T* const dst = FRAG ? fout + (long)(bcol[j] >> 4) * nch_h * FB + fpos[i] : xout + o;
         T* const cpy = FRAG ? xout : nullptr;
         auto emit = [&](int k, float h) {  // h_t to the exchange, y and (last step) hT
-          const T hv = from_float<BF16>(h);
+          const T hv = sent ? canon_nan<BF16>(from_float<BF16>(h)) : from_float<BF16>(h);
           store_coherent<BF16>(dst + k, hv);
           if (cpy) cpy[o + k] = hv;
           if (yout) yout[o + k] = hv;
@@ -521,12 +587,15 @@ __global__ void __launch_bounds__(64 * NWV) lstm_rec_kernel(const RecParams P) {
       }
     stamp(t, 4);
 
-    // ---- publish step t: stores complete, then the step counter
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tid == 0)
-      __hip_atomic_store(LY(flags) + (long)wl * kFlagStride, t + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // ---- publish step t: stores complete, then the step counter (the
+    // data-valid exchange publishes by the stores themselves)
+    if (!sent) {
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (tid == 0)
+        __hip_atomic_store(LY(flags) + (long)wl * kFlagStride, t + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     stamp(t, 5);
   }
 #undef LY

@@ -139,3 +139,20 @@ def test_planner_forced_regimes_and_small_devices():
     assert info.grid <= 8
     with pytest.raises(sl.LstmError):
         sl.lstm_fwd_plan(sl.make_desc(1, 4, 4, 4, 4, "f32"), 9, 256, 160 * 1024)
+
+
+def test_planner_data_valid_exchange_only_on_small_single_layer_grids():
+    """Counter-free exchange: single hoisted layers with B < 16 and at most 64 workgroups."""
+    expect = {"c1": True, "c2": False, "c3": False, "c4": False, "c5": False}
+    for name, want in expect.items():
+        c = li.CONFIGS[name]
+        info = sl.lstm_fwd_plan(sl.make_desc(c.L, c.I, c.H, c.B, c.T, c.dtype), 0, 256, 160 * 1024)
+        assert bool(info.data_valid_exchange) == want, name
+    for (H, B, dt), want in {(256, 4, "bf16"): True, (256, 8, "f32"): True, (512, 4, "bf16"): False,
+                             (128, 16, "bf16"): False, (128, 8, "f32"): True}.items():
+        info = sl.lstm_fwd_plan(sl.make_desc(2, H, H, B, 10, dt), 1, 256, 160 * 1024)
+        assert info.grid <= 64 or not want
+        assert bool(info.data_valid_exchange) == want, (H, B, dt)
+    # the wavefront never uses it
+    info = sl.lstm_fwd_plan(sl.make_desc(2, 128, 128, 8, 10, "bf16"), 2, 256, 160 * 1024)
+    assert not info.data_valid_exchange

@@ -361,3 +361,71 @@ def test_gpu_wavefront_with_hoisted_first_layer(dev):
     assert plan["regime"] == "wavefront" and plan["input_gemms"] == 1
     got = run_gpu(inp, dev, regime=2)
     check_close(got, orc.lstm_forward_inputs(inp), TOL["f32"], "wavefront hoisted layer 0")
+
+
+# ----------------------------------------------------------------------------- counter-free exchange
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("H,B", [(128, 8), (256, 4)])
+def test_gpu_data_valid_exchange_parity(dev, H, B, dtype):
+    """Small single-layer grids exchange h_t without step counters (readers re-read
+    the slot until no element holds the unwritten pattern): same results."""
+    import stacked_lstm_forward_amd as sl
+    cfg = li.custom_config(2, H, H, B, 40, dtype, cfg_id=90)
+    d = sl.make_desc(cfg.L, cfg.I, cfg.H, cfg.B, cfg.T, cfg.dtype)
+    assert sl.lstm_fwd_plan(d, 1).as_dict()["data_valid_exchange"]
+    inp = li.make_inputs(cfg, random_state=True)
+    say(f"data-valid exchange H={H} B={B} {dtype}")
+    check_close(run_gpu(inp, dev, regime=1), orc.lstm_forward_inputs(inp), TOL[dtype], f"dv H{H} B{B} {dtype}")
+
+
+def test_gpu_data_valid_exchange_forced_timeout(dev):
+    """A zero wait limit makes the first incomplete re-read give up: every workgroup
+    leaves the kernel, the error word reports the timeout and the next call is clean."""
+    import stacked_lstm_forward_amd as sl
+    from stacked_lstm_forward_amd import runner
+    cfg = li.custom_config(2, 256, 256, 8, 6, "bf16", cfg_id=91)
+    d = sl.make_desc(cfg.L, cfg.I, cfg.H, cfg.B, cfg.T, cfg.dtype)
+    assert sl.lstm_fwd_plan(d, 1).as_dict()["data_valid_exchange"]
+    inp = li.make_inputs(cfg)
+    prob = runner.prepare(inp, dev)
+    say("data-valid exchange forced timeout")
+    opts = sl.LstmOpts()
+    opts.force_regime = 1
+    opts.wait_timeout_us = -1
+    prob.run(opts=opts)
+    assert sl.lstm_fwd_last_error(prob.ws) == sl.LSTM_ERR_BARRIER_TIMEOUT
+    prob.run()
+    assert sl.lstm_fwd_last_error(prob.ws) == sl.LSTM_OK
+    ref = orc.lstm_forward_inputs(inp)
+    assert rel_err(prob.y.float().cpu().numpy(), ref[0]) < TOL["bf16"]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_gpu_data_valid_exchange_nan_input(dev, dtype):
+    """An input element with every bit set (a NaN, and the exchange's unwritten
+    pattern) makes that sequence's h NaN from then on; stored NaNs are canonical,
+    so no reader mistakes them for unwritten slots and the call ends normally."""
+    import warnings
+    import dataclasses
+    import stacked_lstm_forward_amd as sl
+    cfg = li.custom_config(1, 128, 128, 8, 5, dtype, cfg_id=92)
+    d = sl.make_desc(cfg.L, cfg.I, cfg.H, cfg.B, cfg.T, cfg.dtype)
+    assert sl.lstm_fwd_plan(d, 0).as_dict()["data_valid_exchange"]
+    inp = li.make_inputs(cfg)
+    x = inp.x.copy()
+    if dtype == "bf16":
+        x[1, 0, 3] = 0xFFFF
+    else:
+        x.view(np.uint32)[1, 0, 3] = 0xFFFFFFFF
+    inp = dataclasses.replace(inp, x=x)
+    say(f"all-ones NaN input {dtype}")
+    got = run_gpu(inp, dev)
+    with warnings.catch_warnings():
+        warnings.simplefilter("ignore", RuntimeWarning)
+        ref = orc.lstm_forward_inputs(inp)
+    for g, r, what in zip(got, ref, ("y", "hT", "cT")):
+        assert np.array_equal(np.isnan(g), np.isnan(r)), what
+        fin = ~np.isnan(r)
+        assert np.isnan(r).any() and fin.any(), what
+        err = np.max(np.abs(g[fin] - r[fin])) / np.max(np.abs(r[fin]))
+        assert err <= TOL[dtype], (what, err)
