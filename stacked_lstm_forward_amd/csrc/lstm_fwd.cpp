@@ -129,7 +129,9 @@ lstm_status_t lstm_fwd_plan(const lstm_desc_t* d, int32_t force_regime, int32_t 
   out->weights_streamed = p.rec[0].stream;
   out->input_gemms = p.ngemm;
   out->weight_blocks_in_registers = p.rec[0].res_nrb;
-  out->data_valid_exchange = data_valid_lds(p, p.rec[0], d->H, d->B, info) > 0 ? 1 : 0;
+  const int dv_lds = data_valid_lds(p, p.rec[0], d->H, d->B, info);
+  out->data_valid_exchange = dv_lds > 0 ? 1 : 0;
+  if (dv_lds > 0) out->lds_bytes = dv_lds;  // two reduction areas
   return LSTM_OK;
 }
 
