@@ -137,8 +137,8 @@ def main() -> int:
         return 0
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: the forward pass here runs on a single MI355X and this build "
-              "has no multi-GPU path (sharding is described in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the forward pass runs on a single MI355X and the library "
+              "has no multi-GPU path. Run with --gpus 1.", file=sys.stderr)
         return 2
 
     import torch
