@@ -156,3 +156,14 @@ def test_planner_data_valid_exchange_only_on_small_single_layer_grids():
     # the wavefront never uses it
     info = sl.lstm_fwd_plan(sl.make_desc(2, 128, 128, 8, 10, "bf16"), 2, 256, 160 * 1024)
     assert not info.data_valid_exchange
+
+
+def test_planner_keeps_four_chunks_per_wave_in_8_wave_launches():
+    """8-wave launches take the widest K split that leaves every wave >= 4 chunks:
+    the 8-layer bf16 H=256 stack (8 chunks per tile row) splits 2 ways, the 4-layer
+    fp32 H=512 stack (32 chunks) 4 ways; 4-wave single-layer launches are unchanged."""
+    want = {"c2": (4, [2, 2]), "c3": (2, [2, 1]), "c5": (4, [2, 1]), "c1": (4, [1, 1])}
+    for name, (ks, tiles) in want.items():
+        c = li.CONFIGS[name]
+        info = sl.lstm_fwd_plan(sl.make_desc(c.L, c.I, c.H, c.B, c.T, c.dtype), 0, 256, 160 * 1024).as_dict()
+        assert (info["ksplit"], info["wave_tiles"]) == (ks, tiles), name
