@@ -28,8 +28,9 @@ namespace lstm {
 // ----------------------------------------------------------------------------
 // Input projection GEMM
 // ----------------------------------------------------------------------------
-// Workgroup tile: kGemmTileM rows (16 M-tiles) x kGemmTileN columns (8 column
-// tiles); wave (wm, wn) of the 2 x 2 waves computes 8 M-tiles x 4 column tiles.
+// Workgroup tile: MTW M-tiles x NTW column tiles (kGemmTileM x kGemmTileN, or
+// 64 x 64 when the large tile would leave most CUs idle); wave (wm, wn) of the
+// 2 x 2 waves computes MTW/2 M-tiles x NTW/2 column tiles.
 // Per K chunk (128 bytes of every row) the workgroup stages 24 fragment blocks
 // of 2 KiB in LDS, double-buffered (one barrier per chunk), while the next
 // chunk's global loads are already in registers.
@@ -52,13 +53,13 @@ __device__ __forceinline__ Frag gemm_load_b(const GemmParams& P, long boff, bool
   return bval ? load_frag_off<BF16>(P.U, boff, k0, q, P.K, P.vec_ok_u) : zero_frag();
 }
 
-template <bool BF16, bool VEC>
+template <bool BF16, bool VEC, int MTW, int NTW>
 __global__ void __launch_bounds__(kGemmThreads) lstm_input_gemm(const GemmParams P) {
   constexpr int KC = Dt<BF16>::KC;
-  constexpr int MTW = kGemmTileM / 16;  // M-tiles per workgroup (16)
-  constexpr int NTW = kGemmTileN / 16;  // column tiles per workgroup (8)
-  constexpr int NA = MTW * 64 / kGemmThreads;  // A fragments staged per thread per chunk (4)
-  constexpr int NB = NTW * 64 / kGemmThreads;  // B fragments staged per thread per chunk (2)
+  static_assert(MTW % 4 == 0 && NTW % 4 == 0, "every thread stages whole fragments");
+  constexpr int WM = MTW / 2, WN = NTW / 2;    // M-tiles and column tiles per wave
+  constexpr int NA = MTW * 64 / kGemmThreads;  // A fragments staged per thread per chunk
+  constexpr int NB = NTW * 64 / kGemmThreads;  // B fragments staged per thread per chunk
   constexpr int STAGE = (MTW + NTW) * 128;     // 16-byte halves per LDS stage
   extern __shared__ __align__(16) unsigned char gsmem[];
   uint4* lds = reinterpret_cast<uint4*>(gsmem);
@@ -76,7 +77,7 @@ __global__ void __launch_bounds__(kGemmThreads) lstm_input_gemm(const GemmParams
     for (long i = wg * kGemmThreads + tid; i < P.fill_count; i += nwg * kGemmThreads) P.fill_ptr[i] = kSentinelWord;
   }
   const int mtb = blockIdx.y * MTW;        // first M-tile of this workgroup
-  const int n0 = blockIdx.x * kGemmTileN;  // first column
+  const int n0 = blockIdx.x * NTW * 16;    // first column
   const int nch = (P.K + KC - 1) / KC;
   const int q = lane >> 4;                 // same for every staging slot (256 is a multiple of 64)
 
@@ -104,11 +105,11 @@ __global__ void __launch_bounds__(kGemmThreads) lstm_input_gemm(const GemmParams
   }
 
   const int wm = wave & 1, wn = wave >> 1;
-  f32x4 acc[8][4];
+  f32x4 acc[WM][WN];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < WM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < WN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   Frag ra[NA], rb[NB];
   if (nch > 0) {
@@ -135,14 +136,14 @@ __global__ void __launch_bounds__(kGemmThreads) lstm_input_gemm(const GemmParams
     for (int s = 0; s < NB; ++s) rb[s] = gemm_load_b<BF16, VEC>(P, boff[s], bval[s], cn * KC, q);
     __builtin_amdgcn_sched_barrier(0);
     const uint4* st = lds + (c & 1) * STAGE;
-    Frag b[4];
+    Frag b[WN];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = lds_get(st + (MTW + 4 * wn + j) * 128, lane);
+    for (int j = 0; j < WN; ++j) b[j] = lds_get(st + (MTW + WN * wn + j) * 128, lane);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const Frag a = lds_get(st + (8 * wm + i) * 128, lane);
+    for (int i = 0; i < WM; ++i) {
+      const Frag a = lds_get(st + (WM * wm + i) * 128, lane);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) mfma_frag<BF16>(acc[i][j], a, b[j]);
+      for (int j = 0; j < WN; ++j) mfma_frag<BF16>(acc[i][j], a, b[j]);
     }
     if (c + 1 < nch) {
       uint4* nx = lds + ((c + 1) & 1) * STAGE;
@@ -162,8 +163,8 @@ __global__ void __launch_bounds__(kGemmThreads) lstm_input_gemm(const GemmParams
   typedef typename Dt<BF16>::T T;
   const T* bias = reinterpret_cast<const T*>(P.bias);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int mt = mtb + 8 * wm + i;
+  for (int i = 0; i < WM; ++i) {
+    const int mt = mtb + WM * wm + i;
     if (mt >= P.Mt) continue;
     f32x4 bv;  // this lane's four rows 4*(lane/16) + k of the tile (rows past H are never read)
 #pragma unroll
@@ -172,8 +173,8 @@ __global__ void __launch_bounds__(kGemmThreads) lstm_input_gemm(const GemmParams
       bv[k] = bi >= 0 ? to_float(bias[bi]) : 0.f;
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const long col = n0 + 16 * (4 * wn + j) + (lane & 15);
+    for (int j = 0; j < WN; ++j) {
+      const long col = n0 + 16 * (WN * wn + j) + (lane & 15);
       if (col >= P.N) continue;
       const long t = col / P.B, bb = col % P.B;
       float* dst = P.G + ((t * P.Mt + mt) * P.B + bb) * 16 + 4 * (lane >> 4);
@@ -384,6 +385,15 @@ const void* rec_kernel_fn(bool bf16, bool stream, bool vec, int nwv, int mw, int
 }
 }  // namespace
 
+template <int MTW, int NTW>
+const void* input_gemm_fn(bool bf16, bool vec) {
+  if (bf16)
+    return vec ? reinterpret_cast<const void*>(&lstm_input_gemm<true, true, MTW, NTW>)
+               : reinterpret_cast<const void*>(&lstm_input_gemm<true, false, MTW, NTW>);
+  return vec ? reinterpret_cast<const void*>(&lstm_input_gemm<false, true, MTW, NTW>)
+             : reinterpret_cast<const void*>(&lstm_input_gemm<false, false, MTW, NTW>);
+}
+
 hipError_t launch_input_gemm(bool bf16, const GemmParams& p, hipStream_t s) {
   constexpr int kMTW = kGemmTileM / 16, kNTW = kGemmTileN / 16;
   const bool whole = (p.K % (bf16 ? Dt<true>::KC : Dt<false>::KC)) == 0;
@@ -401,16 +411,18 @@ hipError_t launch_input_gemm(bool bf16, const GemmParams& p, hipStream_t s) {
     void* args[] = {const_cast<GemmParams*>(&p)};
     return hipLaunchKernel(fn, grid, dim3(kGemmThreads), args, lds, s);
   }
-  const unsigned lds = 2 * (kMTW + kNTW) * 64 * sizeof(Frag);
-  const dim3 grid((p.N + kGemmTileN - 1) / kGemmTileN, (p.Mt + kMTW - 1) / kMTW);
   const bool vec = p.vec_ok_w && p.vec_ok_u && (p.K % (bf16 ? Dt<true>::KC : Dt<false>::KC)) == 0;
-  const void* fn;
-  if (bf16)
-    fn = vec ? reinterpret_cast<const void*>(&lstm_input_gemm<true, true>)
-             : reinterpret_cast<const void*>(&lstm_input_gemm<true, false>);
-  else
-    fn = vec ? reinterpret_cast<const void*>(&lstm_input_gemm<false, true>)
-             : reinterpret_cast<const void*>(&lstm_input_gemm<false, false>);
+  // A problem the 256 x 128 tile covers with fewer than kGemmSmallGrid
+  // workgroups (a short sequence, a small batch) leaves most CUs idle while
+  // each workgroup runs its whole K loop: 64 x 64 tiles spread it further
+  // (1-layer H = 128, B = 8, T = 16, fp32: 2 workgroups and 33 us, 16).
+  constexpr int kGemmSmallGrid = 64;
+  const int big = ((p.N + kGemmTileN - 1) / kGemmTileN) * ((p.Mt + kMTW - 1) / kMTW);
+  const bool small = big < kGemmSmallGrid;
+  const int mtw = small ? 4 : kMTW, ntw = small ? 4 : kNTW;
+  const unsigned lds = 2 * (mtw + ntw) * 64 * sizeof(Frag);
+  const dim3 grid((p.N + ntw * 16 - 1) / (ntw * 16), (p.Mt + mtw - 1) / mtw);
+  const void* fn = small ? input_gemm_fn<4, 4>(bf16, vec) : input_gemm_fn<kMTW, kNTW>(bf16, vec);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   void* args[] = {const_cast<GemmParams*>(&p)};
