@@ -167,3 +167,13 @@ def test_planner_keeps_four_chunks_per_wave_in_8_wave_launches():
         c = li.CONFIGS[name]
         info = sl.lstm_fwd_plan(sl.make_desc(c.L, c.I, c.H, c.B, c.T, c.dtype), 0, 256, 160 * 1024).as_dict()
         assert (info["ksplit"], info["wave_tiles"]) == (ks, tiles), name
+
+
+def test_planner_refuses_past_the_limits():
+    """B > 256 (16 column tiles) and L > 64 are refused before any launch."""
+    for d in (sl.make_desc(2, 64, 64, 257, 3, "f32"), sl.make_desc(65, 32, 32, 4, 3, "bf16")):
+        with pytest.raises(sl.LstmError) as ei:
+            sl.lstm_fwd_plan(d, 0, 256, 160 * 1024)
+        assert ei.value.status == sl.LSTM_ERR_UNSUPPORTED
+    for d in (sl.make_desc(2, 64, 64, 256, 3, "f32"), sl.make_desc(64, 32, 32, 4, 3, "bf16")):
+        assert sl.lstm_fwd_plan(d, 0, 256, 160 * 1024).grid > 0

@@ -429,3 +429,19 @@ def test_gpu_data_valid_exchange_nan_input(dev, dtype):
         assert np.isnan(r).any() and fin.any(), what
         err = np.max(np.abs(g[fin] - r[fin])) / np.max(np.abs(r[fin]))
         assert err <= TOL[dtype], (what, err)
+
+
+# ----------------------------------------------------------------------------- size limits
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("regime", [1, 2])
+@pytest.mark.parametrize("shape", [(64, 32, 32, 4, 3), (2, 64, 64, 256, 3)])
+def test_gpu_size_limits(dev, shape, dtype, regime):
+    """The largest stack (64 layers: four 16-layer wavefront launches) and the
+    largest batch (256 = 16 column tiles) the library accepts."""
+    L, I, H, B, T = shape
+    cfg = li.custom_config(L, I, H, B, T, dtype, cfg_id=95 + L)
+    inp = li.make_inputs(cfg, random_state=True)
+    say(f"limits {shape} {dtype} regime={regime}")
+    got = run_gpu(inp, dev, regime=regime)
+    ref = orc.lstm_forward_inputs(inp)
+    check_close(got, ref, TOL[dtype], f"limits {shape} {dtype} r{regime}")
