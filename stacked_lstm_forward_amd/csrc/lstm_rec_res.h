@@ -164,7 +164,7 @@ lstm_rec_res_kernel(const RecParams P) {
 
     if (t > 0) {
       if (kg == 0) {
-        const bool ok = wait_counts(Lr.flags, Lr.wg_count, t, nullptr, 0, 0, P.err, P.timeout_ticks);
+        const bool ok = wait_counts_serial(Lr.flags, Lr.wg_count, t, nullptr, 0, 0, P.err, P.timeout_ticks);
         if (lane == 0) s_ok = ok ? 1 : 0;
       }
       __syncthreads();
