@@ -48,7 +48,8 @@
  * gate k of hidden unit j.  "dtype" is LSTM_F32 (IEEE fp32) or LSTM_BF16
  * (bfloat16 bits); arithmetic is fp32 (fp32 accumulation and cell state) in
  * both cases.  With LSTM_BF16 the h that feeds the next step is the bf16 value
- * stored in y / the layer-to-layer buffers.
+ * stored in y / the layer-to-layer buffers.  A NaN in h may come back as the
+ * canonical quiet NaN (its payload is not kept).
  *
  * Ownership: every tensor pointer is a device pointer owned by the caller.  The
  * library allocates no device memory and keeps no state between calls outside
