@@ -303,6 +303,15 @@ __global__ void __launch_bounds__(64 * NWV) lstm_rec_kernel(const RecParams P) {
     uoff[j] = (long)min(bcol[j], B - 1) * Kin;
   }
   auto fin = [&](int i, int j) { return ((i * P.nw + j) % ks) == kg; };
+  // Branch-free MFMA chains on the aligned path with two waves per SIMD: a
+  // tile the wave does not own (past the layer's last M-tile or column tile,
+  // or beyond mw x nw when the instantiation rounds up) multiplies clamped
+  // rows and its sum is never used.  Measured: the 4-layer fp32 H = 512
+  // wavefront 1.297 -> 1.272 ms, the 8-layer bf16 H = 256 one 0.853 -> 0.835.
+  // One wave per SIMD keeps the branches (the single-layer bf16 H = 1536
+  // launch was 0.7% slower without them), and so does choosing between both
+  // forms at run time (2-3% slower: the loop then carries both).
+  constexpr bool dense = VEC && NWV == 8;
   auto live = [&](int i, int j) { return mval[i] && nval[j] && fin(i, j) && unit[i] < H && bcol[j] < B; };
 
   // per-lane state in registers, fp32: the LSTM's cell state c, the GRU's
@@ -476,11 +485,21 @@ __global__ void __launch_bounds__(64 * NWV) lstm_rec_kernel(const RecParams P) {
       auto compute = [&](int s, int ci) {
         if (!STREAM) lds_a(al[STREAM ? 0 : ((s + 1) & 1)], ci + 1);
         Frag (&a)[MW] = STREAM ? ra[STREAM ? s : 0] : al[STREAM ? 0 : (s & 1)];
+        if (dense) {
+          // every tile of the instantiation is one of the wave's (a tile past
+          // the layer's last M-tile multiplies clamped rows; its sum is never
+          // used): no branch between the MFMA chains
 #pragma unroll
-        for (int i = 0; i < MW; ++i)
+          for (int i = 0; i < MW; ++i)
 #pragma unroll
-          for (int j = 0; j < NW; ++j)
-            if (mval[i] && nval[j]) mfma_frag<BF16>(acc[i][j], a[i], rb[s][j]);
+            for (int j = 0; j < NW; ++j) mfma_frag<BF16>(acc[i][j], a[i], rb[s][j]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < MW; ++i)
+#pragma unroll
+            for (int j = 0; j < NW; ++j)
+              if (mval[i] && nval[j]) mfma_frag<BF16>(acc[i][j], a[i], rb[s][j]);
+        }
       };
       if (n > 0 && n <= PD) {
         // burst: every chunk of this wave in flight at once
