@@ -91,6 +91,8 @@ __device__ bool wait_counts_serial(const int* a, int na, int ta, const int* b, i
   while (true) {
     int ok = 1;
     const int n = max(na, b ? nb : 0);
+    // the error word is read with the first batch of counters, not after them
+    const int e = __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     for (int base = 0; base < n; base += 256) {
       int va[4], vb[4];
       if (base < na) poll_issue(a + (long)base * kFlagStride, na - base, va);
@@ -102,7 +104,7 @@ __device__ bool wait_counts_serial(const int* a, int na, int ta, const int* b, i
       }
     }
     if (__all(ok)) return true;
-    if (__hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return false;
+    if (e != 0) return false;
     if (wall_clock64() - start > timeout) {
       if (lane == 0) __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       return false;
