@@ -445,3 +445,21 @@ def test_gpu_size_limits(dev, shape, dtype, regime):
     got = run_gpu(inp, dev, regime=regime)
     ref = orc.lstm_forward_inputs(inp)
     check_close(got, ref, TOL[dtype], f"limits {shape} {dtype} r{regime}")
+
+
+@pytest.mark.parametrize("shape,dtype", [((2, 64, 64, 80, 4), "f32"), ((2, 192, 192, 80, 4), "bf16"),
+                                         ((3, 128, 128, 48, 4), "bf16")])
+def test_gpu_wavefront_padding_tiles(dev, shape, dtype):
+    """Two-waves-per-SIMD launches multiply every tile of their instantiation
+    without branches: here a wave owns 3 column tiles of a 4-wide instantiation
+    (B = 48, 80), and with B = 80 one tile group's third tile is past the batch.
+    Those tiles' sums must never reach the outputs."""
+    import stacked_lstm_forward_amd as sl
+    L, I, H, B, T = shape
+    d = sl.make_desc(L, I, H, B, T, dtype)
+    plan = sl.lstm_fwd_plan(d, 2).as_dict()
+    assert plan["block"] == 512 and plan["wave_tiles"][1] == 3, plan
+    cfg = li.custom_config(L, I, H, B, T, dtype, cfg_id=97)
+    inp = li.make_inputs(cfg, random_state=True)
+    say(f"padding tiles {shape} {dtype}")
+    check_close(run_gpu(inp, dev, regime=2), orc.lstm_forward_inputs(inp), TOL[dtype], f"pad {shape} {dtype}")
