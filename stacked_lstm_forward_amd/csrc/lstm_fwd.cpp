@@ -240,6 +240,7 @@ lstm_status_t lstm_fwd_ex(const lstm_desc_t* d, const void* x, const void* h0, c
     gp.vec_ok_w = aligned16(gp.W) && ((size_t)K * ds) % 16 == 0;
     gp.vec_ok_u = aligned16(U) && ((size_t)K * ds) % 16 == 0 && ((size_t)u_slot * ds) % 16 == 0;
     gp.cell = p.cell;
+    gp.num_cus = dev.info.num_cus;
     if (!before(LSTM_KERNEL_INPUT_GEMM)) return LSTM_ERR_HIP;
     if (launch_input_gemm(bf16, gp, stream) != hipSuccess) return LSTM_ERR_HIP;
     if (!after()) return LSTM_ERR_HIP;

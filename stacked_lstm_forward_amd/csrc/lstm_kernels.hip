@@ -192,11 +192,16 @@ __global__ void __launch_bounds__(kGemmThreads) lstm_input_gemm(const GemmParams
 // while chunk c is multiplied.
 // Per chunk a wave reads 32 KiB from LDS for 128 MFMAs (2 per tile, chained on
 // one accumulator, which keeps the matrix pipe issuing back to back).
-constexpr int kDmaTiles = 16;                    // M-tiles and column tiles per workgroup
+constexpr int kDmaTiles = 16;                    // M-tiles (and at most column tiles) per workgroup
 constexpr int kDmaStage = 2 * kDmaTiles * 128;   // 16-byte units per LDS stage (64 KiB)
 
-template <bool BF16>
+// NT column tiles per workgroup (16, or 14 when that packs the columns into
+// fewer rounds of workgroups than 16 would: see launch_input_gemm); each of
+// the two column-halves of waves takes NT / 2.
+template <bool BF16, int NT>
 __global__ void __launch_bounds__(kGemmThreads) lstm_input_gemm_dma(const GemmParams P) {
+  static_assert(NT % 2 == 0 && NT <= kDmaTiles, "column tiles per workgroup");
+  constexpr int WN = NT / 2;  // column tiles per wave
   typedef typename Dt<BF16>::T T;
   typedef __attribute__((address_space(1))) const void* gptr_t;
   typedef __attribute__((address_space(3))) void* lptr_t;
@@ -223,7 +228,7 @@ __global__ void __launch_bounds__(kGemmThreads) lstm_input_gemm_dma(const GemmPa
   // rows and 8 blocks of U columns through their L2 instead of each pulling
   // its own from memory.
   const int nM = (P.Mt + kDmaTiles - 1) / kDmaTiles;
-  const int nN = (P.N + kDmaTiles * 16 - 1) / (kDmaTiles * 16);
+  const int nN = (P.N + NT * 16 - 1) / (NT * 16);
   const int total = nM * nN;
   const int per_xcd = (int)gridDim.x >> 3;
   const int v = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
@@ -235,7 +240,7 @@ __global__ void __launch_bounds__(kGemmThreads) lstm_input_gemm_dma(const GemmPa
   const int mblk = first_m + (v % in_group) % gsize;
   const int nblk = (v % in_group) / gsize;
   const int mtb = mblk * kDmaTiles;                  // first M-tile
-  const long n0 = (long)nblk * kDmaTiles * 16;       // first column
+  const long n0 = (long)nblk * NT * 16;              // first column
   const int nch = P.K / KC;
 
   // staging: wave w fills fragment blocks 8w .. 8w+7 of every stage (blocks
@@ -271,13 +276,15 @@ __global__ void __launch_bounds__(kGemmThreads) lstm_input_gemm_dma(const GemmPa
   }
   auto stage_load = [&](int c, int buf) {
 #pragma unroll
-    for (int s8 = 0; s8 < 8; ++s8)
+    for (int s8 = 0; s8 < 8; ++s8) {
+      if (8 * wave + s8 >= kDmaTiles + NT) continue;  // a column block past NT (wave-uniform)
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const T* g = gbase + src[s8][i] + (long)c * KC;
         uint4* l = lds + buf * kDmaStage + (8 * wave + s8) * 128 + i * 64;
         __builtin_amdgcn_global_load_lds((gptr_t)g, (lptr_t)l, 16, 0, 0);
       }
+    }
   };
   // this lane's two fragment halves (row lane%16, pieces 4h + lane/16) in a block
   const int fr_ = lane & 15, fsw = (fr_ >> 1) & 7;
@@ -290,11 +297,11 @@ __global__ void __launch_bounds__(kGemmThreads) lstm_input_gemm_dma(const GemmPa
   };
 
   const int wm = wave & 1, wn = wave >> 1;
-  f32x4 acc[8][8];
+  f32x4 acc[8][WN];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < WN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   if (nch > 0) stage_load(0, 0);
   for (int c = 0; c < nch; ++c) {
@@ -307,9 +314,9 @@ __global__ void __launch_bounds__(kGemmThreads) lstm_input_gemm_dma(const GemmPa
     // and an LDS read issued after them would first wait for all of them,
     // which would serialise each chunk's loads with the previous chunk's MFMAs.
     const uint4* st = lds + (c & 1) * kDmaStage;
-    Frag a[8], b[8];
+    Frag a[8], b[WN];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) b[j] = frag_at(st + (kDmaTiles + 8 * wn + j) * 128);
+    for (int j = 0; j < WN; ++j) b[j] = frag_at(st + (kDmaTiles + WN * wn + j) * 128);
 #pragma unroll
     for (int i = 0; i < 8; ++i) a[i] = frag_at(st + (8 * wm + i) * 128);
     // (unconditional, so no branch separates the reads from the MFMAs: the last
@@ -320,7 +327,7 @@ __global__ void __launch_bounds__(kGemmThreads) lstm_input_gemm_dma(const GemmPa
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) mfma_frag<BF16>(acc[i][j], a[i], b[j]);
+      for (int j = 0; j < WN; ++j) mfma_frag<BF16>(acc[i][j], a[i], b[j]);
   }
   __builtin_amdgcn_s_waitcnt(0);  // the last (redundant) loads have landed
 
@@ -340,8 +347,8 @@ __global__ void __launch_bounds__(kGemmThreads) lstm_input_gemm_dma(const GemmPa
       wrow[k] = cr.w >= 0;
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const long col = n0 + 16 * (8 * wn + j) + (lane & 15);
+    for (int j = 0; j < WN; ++j) {
+      const long col = n0 + 16 * (WN * wn + j) + (lane & 15);
       if (col >= P.N) continue;
       const long t = col / P.B, bb = col % P.B;
       float* dst = P.G + ((t * P.Mt + mt) * P.B + bb) * 16 + 4 * q;
@@ -402,11 +409,24 @@ hipError_t launch_input_gemm(bool bf16, const GemmParams& p, hipStream_t s) {
   // register-staged 256 x 128 kernel, whose smaller tiles fill more CUs
   if (p.vec_ok_w && p.vec_ok_u && whole && p.K >= 1024) {
     const unsigned lds = 2 * kDmaStage * sizeof(uint4);
-    const void* fn = bf16 ? reinterpret_cast<const void*>(&lstm_input_gemm_dma<true>)
-                          : reinterpret_cast<const void*>(&lstm_input_gemm_dma<false>);
+    // 14 column tiles per workgroup instead of 16 when that needs no more
+    // rounds of one workgroup per CU: each round then loads 30 fragment
+    // blocks per chunk instead of 32 (the 16384 x 1600 projection of a
+    // 4096-wide bf16 layer at B = 32, T = 50: 448 tiles in 2 rounds become 512
+    // in 2 rounds)
+    const int nM = (p.Mt + kDmaTiles - 1) / kDmaTiles;
+    auto rounds = [&](int nt) {
+      const int cus = p.num_cus > 0 ? p.num_cus : 256;
+      return (nM * ((p.N + nt * 16 - 1) / (nt * 16)) + cus - 1) / cus;
+    };
+    const int nt = rounds(14) * (kDmaTiles + 14) < rounds(16) * (kDmaTiles + 16) ? 14 : 16;
+    const void* fn = nt == 14 ? (bf16 ? reinterpret_cast<const void*>(&lstm_input_gemm_dma<true, 14>)
+                                      : reinterpret_cast<const void*>(&lstm_input_gemm_dma<false, 14>))
+                              : (bf16 ? reinterpret_cast<const void*>(&lstm_input_gemm_dma<true, 16>)
+                                      : reinterpret_cast<const void*>(&lstm_input_gemm_dma<false, 16>));
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    const int tiles = ((p.N + kDmaTiles * 16 - 1) / (kDmaTiles * 16)) * ((p.Mt + kDmaTiles - 1) / kDmaTiles);
+    const int tiles = ((p.N + nt * 16 - 1) / (nt * 16)) * nM;
     const dim3 grid((tiles + 7) & ~7);  // a multiple of the 8 XCDs (extra workgroups only help zeroing)
     void* args[] = {const_cast<GemmParams*>(&p)};
     return hipLaunchKernel(fn, grid, dim3(kGemmThreads), args, lds, s);

@@ -33,6 +33,7 @@ struct GemmParams {
   int K, H, Mt, B, N;  // N = T*B
   int vec_ok_w, vec_ok_u;
   int cell;            // lstm_cell_t
+  int num_cus;         // compute units of the device (tile-shape choice; 0: 256)
 };
 
 // One layer of a recurrent launch.
