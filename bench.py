@@ -283,6 +283,11 @@ def main() -> int:
                      "gflop_per_launch": round(dom_flops / 1e9, 3)},
         "whole_step_frac_of_mfma_peak": round(value / peak, 4),
         "kernels_ms_per_launch": {kname.get(kk, str(kk)): round(sum(v) / len(v), 5) for kk, v in per_kind.items()},
+        # every kernel that does arithmetic, not only the dominant one (the
+        # input GEMMs and the recurrence of a layerwise run bind differently)
+        "kernels_mfma_frac": {
+            kname.get(kk, str(kk)): round(sum(flops_kind[kk]) / (sum(v) * 1e-3) / 1e12 / peak, 4)
+            for kk, v in per_kind.items() if sum(flops_kind[kk]) > 0},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
