@@ -19,6 +19,8 @@
 //    step counters (agent-scope release/acquire), polled with a time limit so a
 //    wait can never hang.
 #include <algorithm>
+#include <mutex>
+#include <vector>
 
 #include "lstm_common.h"
 #include "lstm_params.h"
@@ -392,6 +394,52 @@ const void* rec_kernel_fn(bool bf16, bool stream, bool vec, int nwv, int mw, int
 }
 }  // namespace
 
+// A kernel's dynamic-LDS limit and its occupancy for a given LDS size and
+// block do not change between calls: set and query them once per process and
+// device instead of on every forward call (each is a runtime call on the host
+// path of every launch).  The limit only ever grows, to the largest size any
+// launch of that kernel has asked for.  blocks_per_cu may be null.
+hipError_t prepare_fn(const void* fn, int lds_bytes, int block, int* blocks_per_cu) {
+  struct Limit {
+    const void* fn;
+    int dev, lds;  // largest dynamic LDS set for fn on dev
+  };
+  struct Occ {
+    const void* fn;
+    int dev, lds, block, blocks;
+  };
+  static std::mutex mu;
+  static std::vector<Limit> limits;
+  static std::vector<Occ> occ;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  Limit* lim = nullptr;
+  for (Limit& l : limits)
+    if (l.fn == fn && l.dev == dev) lim = &l;
+  if (!lim || lim->lds < lds_bytes) {
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+    if (e != hipSuccess) return e;
+    if (lim)
+      lim->lds = lds_bytes;
+    else
+      limits.push_back(Limit{fn, dev, lds_bytes});
+  }
+  if (!blocks_per_cu) return hipSuccess;
+  for (const Occ& o : occ)
+    if (o.fn == fn && o.dev == dev && o.lds == lds_bytes && o.block == block) {
+      *blocks_per_cu = o.blocks;
+      return hipSuccess;
+    }
+  int b = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, fn, block, lds_bytes);
+  if (e != hipSuccess) return e;
+  occ.push_back(Occ{fn, dev, lds_bytes, block, b});
+  *blocks_per_cu = b;
+  return hipSuccess;
+}
+
 template <int MTW, int NTW>
 const void* input_gemm_fn(bool bf16, bool vec) {
   if (bf16)
@@ -424,7 +472,7 @@ hipError_t launch_input_gemm(bool bf16, const GemmParams& p, hipStream_t s) {
                                       : reinterpret_cast<const void*>(&lstm_input_gemm_dma<false, 14>))
                               : (bf16 ? reinterpret_cast<const void*>(&lstm_input_gemm_dma<true, 16>)
                                       : reinterpret_cast<const void*>(&lstm_input_gemm_dma<false, 16>));
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = prepare_fn(fn, (int)lds, kGemmThreads, nullptr);
     if (e != hipSuccess) return e;
     const int tiles = ((p.N + nt * 16 - 1) / (nt * 16)) * nM;
     const dim3 grid((tiles + 7) & ~7);  // a multiple of the 8 XCDs (extra workgroups only help zeroing)
@@ -443,7 +491,7 @@ hipError_t launch_input_gemm(bool bf16, const GemmParams& p, hipStream_t s) {
   const unsigned lds = 2 * (mtw + ntw) * 64 * sizeof(Frag);
   const dim3 grid((p.N + ntw * 16 - 1) / (ntw * 16), (p.Mt + mtw - 1) / mtw);
   const void* fn = small ? input_gemm_fn<4, 4>(bf16, vec) : input_gemm_fn<kMTW, kNTW>(bf16, vec);
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipError_t e = prepare_fn(fn, (int)lds, kGemmThreads, nullptr);
   if (e != hipSuccess) return e;
   void* args[] = {const_cast<GemmParams*>(&p)};
   return hipLaunchKernel(fn, grid, dim3(kGemmThreads), args, lds, s);
@@ -460,17 +508,13 @@ hipError_t rec_prepare(bool bf16, bool stream, bool vec, bool frag, int nwv, int
                        int* max_blocks_per_cu) {
   const void* fn = rec_kernel_fn(bf16, stream, vec, nwv, mw, nw, frag);
   if (!fn) return hipErrorInvalidValue;
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
-  if (e != hipSuccess) return e;
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(max_blocks_per_cu, fn, 64 * nwv, lds_bytes);
+  return prepare_fn(fn, lds_bytes, 64 * nwv, max_blocks_per_cu);
 }
 
 hipError_t res_prepare(bool bf16, int mw, int nw, int nci, int nrb, int lds_bytes, int* max_blocks_per_cu) {
   const void* fn = rec_res_kernel_ptr(bf16, mw, nw, nci, nrb);
   if (!fn) return hipErrorInvalidValue;
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
-  if (e != hipSuccess) return e;
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(max_blocks_per_cu, fn, 64 * 4, lds_bytes);
+  return prepare_fn(fn, lds_bytes, 64 * 4, max_blocks_per_cu);
 }
 
 hipError_t launch_rec_res(bool bf16, int nci, int nrb, const RecParams& p, int lds_bytes, bool plain, hipStream_t s) {
