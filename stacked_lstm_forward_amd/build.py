@@ -1,4 +1,7 @@
-"""Builds the gfx950 shared library ``lib/liblstm_fwd.so`` in-tree with hipcc.
+"""Builds the gfx950 shared libraries in-tree with hipcc:
+
+    lib/liblstm_fwd.so    the forward pass (include/lstm_fwd.h)
+    lib/liblstm_peaks.so  the measured-peak microbenchmarks (include/lstm_peaks.h)
 
     python -m stacked_lstm_forward_amd.build
 """
@@ -13,6 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIBDIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIBDIR, "liblstm_fwd.so")
+PEAKS_LIB = os.path.join(LIBDIR, "liblstm_peaks.so")
 ARCH = "gfx950"
 # (source, extra defines): the recurrent kernel is instantiated once per
 # (dtype, weight source, waves per workgroup) so the variants compile in parallel
@@ -20,6 +24,7 @@ UNITS = [("lstm_kernels.hip", [])] + [
     ("lstm_rec_inst.hip", [f"-DLSTM_INST_BF16={bf}", f"-DLSTM_INST_STREAM={st}", f"-DLSTM_INST_NWV={nwv}"])
     for bf in (0, 1) for st in (0, 1) for nwv in (4, 8)
 ] + [("lstm_rec_res_inst.hip", []), ("lstm_fwd.cpp", []), ("lstm_plan.cpp", [])]
+PEAK_UNITS = [("lstm_peaks.hip", [])]
 BUILD_DIR = os.path.join(HERE, "_build")
 
 
@@ -44,12 +49,13 @@ def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     cc = hipcc()
     jobs = []
-    for i, (src, defs) in enumerate(UNITS):
-        obj = os.path.join(BUILD_DIR, f"{i:02d}_{os.path.splitext(src)[0]}.o")
-        jobs.append((obj, [cc, *_flags(), *defs, "-c", os.path.join(CSRC, src), "-o", obj]))
+    for tag, units in (("fwd", UNITS), ("peaks", PEAK_UNITS)):
+        for i, (src, defs) in enumerate(units):
+            obj = os.path.join(BUILD_DIR, f"{tag}_{i:02d}_{os.path.splitext(src)[0]}.o")
+            jobs.append((tag, obj, [cc, *_flags(), *defs, "-c", os.path.join(CSRC, src), "-o", obj]))
 
     def run(job):
-        obj, cmd = job
+        _, obj, cmd = job
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)
@@ -60,14 +66,16 @@ def build(verbose: bool = False) -> str:
     workers = max(1, min(len(jobs), os.cpu_count() or 1, 8))
     with ThreadPoolExecutor(workers) as ex:
         objs = list(ex.map(run, jobs))
-    tmp = LIB + ".tmp"
-    link = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
-    if verbose:
-        print(" ".join(link), flush=True)
-    r = subprocess.run(link, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed ({r.returncode}):\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    for tag, lib in (("fwd", LIB), ("peaks", PEAKS_LIB)):
+        mine = [o for (t, _, _), o in zip(jobs, objs) if t == tag]
+        tmp = lib + ".tmp"
+        link = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *mine, "-o", tmp]
+        if verbose:
+            print(" ".join(link), flush=True)
+        r = subprocess.run(link, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed ({r.returncode}):\n{r.stdout}\n{r.stderr}")
+        os.replace(tmp, lib)
     return LIB
 
 

@@ -13,11 +13,11 @@ import stacked_lstm_forward_amd as sl
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def declared_functions():
+def declared_functions(header=None):
     names = []
     inc = os.path.join(ROOT, "include")
     for fn in sorted(os.listdir(inc)):
-        if not fn.endswith(".h"):
+        if not fn.endswith(".h") or (header and fn != header):
             continue
         text = open(os.path.join(inc, fn)).read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -28,11 +28,30 @@ def declared_functions():
 
 def test_library_loads_and_exports_all_declared_symbols():
     lib = sl.load_library()
-    names = declared_functions()
+    names = declared_functions("lstm_fwd.h")
     assert set(names) == set(sl.EXPORTED), names
     for n in names:
         assert hasattr(lib, n), n
         assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+
+
+def test_peaks_library_loads_and_exports_all_declared_symbols():
+    from stacked_lstm_forward_amd import peaks
+    lib = peaks.load_library()
+    names = declared_functions("lstm_peaks.h")
+    assert set(names) == set(peaks.EXPORTED), names
+    for n in names:
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+    # host-only sizing (no GPU call)
+    assert lib.lstm_peak_step_ws_bytes(256, 1, 1024, 10) == 256 + 256 * 128 + 10 * 256 * 1024
+    assert lib.lstm_peak_step_ws_bytes(256, 8, 384, 10) == 256 + 256 * 128 + 10 * 32 * 384
+    assert lib.lstm_peak_step_ws_bytes(256, 1, 24, 10) == 0      # slice not a multiple of 16
+    assert lib.lstm_peak_step_ws_bytes(512, 1, 16, 10) == 0      # more than 256 active workgroups
+
+
+def test_every_header_is_covered():
+    assert set(declared_functions()) == set(declared_functions("lstm_fwd.h")) | set(
+        declared_functions("lstm_peaks.h"))
 
 
 def test_status_strings():
