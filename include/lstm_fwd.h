@@ -53,7 +53,8 @@
  *
  * Ownership: every tensor pointer is a device pointer owned by the caller.  The
  * library allocates no device memory and keeps no state between calls outside
- * the caller's workspace `ws`, which must hold at least
+ * the caller's workspace `ws` (lstm_fwd_noalloc instead uses one fixed device
+ * array of the library's, described at its declaration), which must hold at least
  * lstm_fwd_workspace_size(desc) bytes, 256-byte aligned.  Its contents on entry
  * are ignored.  All work is enqueued on `stream`, asynchronously; nothing syncs
  * the host.  Concurrent calls must not share a workspace.
@@ -180,6 +181,32 @@ lstm_status_t lstm_fwd_validate(const lstm_desc_t *d, const void *x, const void 
  * lstm_fwd on workspace `ws` left (LSTM_OK or LSTM_ERR_BARRIER_TIMEOUT).
  */
 lstm_status_t lstm_fwd_last_error(const void *ws, hipStream_t stream);
+
+/*
+ * lstm_fwd without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  The workspace is a fixed device array inside the
+ * library, LSTM_FWD_NOALLOC_MAX_WORKSPACE bytes on each device the library
+ * runs on, held until the process ends.  A problem whose
+ * lstm_fwd_workspace_size exceeds it returns LSTM_ERR_WORKSPACE before
+ * anything is enqueued (64 MiB holds, e.g., a 1-layer H = 128, B = 8, T = 16
+ * problem or a 1-layer bf16 H = 1536, B = 4, T = 256 one; the 4-layer
+ * H = 512, B = 64, T = 100 problem needs 113 MiB).  The call allocates
+ * nothing; the other arguments, layouts, results and errors are lstm_fwd's.
+ * Every call on one device shares that device's array and finds the previous
+ * call's contents in it (the kernels clear what must start at zero): calls
+ * that overlap on one device -- on two streams, or from two host threads --
+ * race, and their results are undefined; calls ordered on one stream are safe.
+ * dev_status: optional device int32 (NULL: not written).  After the call's
+ * kernels it holds LSTM_OK or LSTM_ERR_BARRIER_TIMEOUT: what
+ * lstm_fwd_last_error reports for a call with a caller's workspace.
+ */
+#define LSTM_FWD_NOALLOC_MAX_WORKSPACE ((size_t)64 << 20)
+lstm_status_t lstm_fwd_noalloc(const lstm_desc_t *d,
+                               const void *x, const void *h0, const float *c0,
+                               const void *W, const void *R, const void *b,
+                               void *y, void *hT, float *cT,
+                               int32_t *dev_status, hipStream_t stream);
 
 /* What the planner decided for a problem (for logging and tests). */
 typedef struct {

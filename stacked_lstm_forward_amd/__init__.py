@@ -13,6 +13,7 @@ The functions carry the C names:
     lstm_fwd_last_error(ws, stream=None) -> status
     lstm_fwd_plan(desc, force_regime=0, num_cus=0, lds_per_cu=0) -> PlanInfo
     lstm_status_string(status) -> str
+    lstm_fwd_noalloc(desc, x, h0, c0, W, R, b, y, hT, cT, dev_status=None, stream=None) -> status
 
 Tensor arguments may be torch tensors (their ``data_ptr()``), raw integer
 device addresses, or None for the nullable ones (h0, c0, hT, cT).
@@ -35,7 +36,8 @@ CELL_IDS = {"lstm": LSTM_CELL_LSTM, "gru": LSTM_CELL_GRU, "rnn_tanh": LSTM_CELL_
             "rnn_relu": LSTM_CELL_RNN_RELU}
 
 EXPORTED = ("lstm_fwd_workspace_size", "lstm_fwd", "lstm_fwd_ex", "lstm_status_string",
-            "lstm_fwd_validate", "lstm_fwd_last_error", "lstm_fwd_plan")
+            "lstm_fwd_validate", "lstm_fwd_last_error", "lstm_fwd_plan", "lstm_fwd_noalloc")
+NOALLOC_MAX_WORKSPACE = 64 << 20  # LSTM_FWD_NOALLOC_MAX_WORKSPACE
 
 
 class LstmDesc(ctypes.Structure):
@@ -108,6 +110,8 @@ def load_library() -> ctypes.CDLL:
     lib.lstm_fwd_last_error.restype = i32
     lib.lstm_fwd_plan.argtypes = [pdesc, i32, i32, i32, ctypes.POINTER(PlanInfo)]
     lib.lstm_fwd_plan.restype = i32
+    lib.lstm_fwd_noalloc.argtypes = [pdesc, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.lstm_fwd_noalloc.restype = i32
     _lib = lib
     return lib
 
@@ -151,6 +155,12 @@ def lstm_fwd_ex(desc, x, h0, c0, W, R, b, y, hT, cT, ws, stream=None, opts: Opti
     return int(load_library().lstm_fwd_ex(ctypes.byref(desc), _ptr(x), _ptr(h0), _ptr(c0), _ptr(W), _ptr(R),
                                           _ptr(b), _ptr(y), _ptr(hT), _ptr(cT), _ptr(ws), _stream(stream),
                                           None if opts is None else ctypes.byref(opts)))
+
+
+def lstm_fwd_noalloc(desc, x, h0, c0, W, R, b, y, hT, cT, dev_status=None, stream=None) -> int:
+    return int(load_library().lstm_fwd_noalloc(None if desc is None else ctypes.byref(desc), _ptr(x), _ptr(h0),
+                                               _ptr(c0), _ptr(W), _ptr(R), _ptr(b), _ptr(y), _ptr(hT), _ptr(cT),
+                                               _ptr(dev_status), _stream(stream)))
 
 
 def lstm_fwd_validate(desc, x, W, R, b, y, ws, ws_bytes: int) -> int:

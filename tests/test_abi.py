@@ -196,3 +196,18 @@ def test_planner_refuses_past_the_limits():
         assert ei.value.status == sl.LSTM_ERR_UNSUPPORTED
     for d in (sl.make_desc(2, 64, 64, 256, 3, "f32"), sl.make_desc(64, 32, 32, 4, 3, "bf16")):
         assert sl.lstm_fwd_plan(d, 0, 256, 160 * 1024).grid > 0
+
+
+def test_noalloc_host_checks_refuse_before_any_launch():
+    """lstm_fwd_noalloc checks its arguments and the scratch limit on the host
+    before any HIP call (so this runs without a GPU)."""
+    d = sl.make_desc(4, 512, 512, 64, 100, "f32")  # needs 113 MiB, beyond the 64 MiB scratch
+    assert sl.lstm_fwd_workspace_size(d) > sl.NOALLOC_MAX_WORKSPACE
+    st = sl.lstm_fwd_noalloc(d, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, None, None, None, 0)
+    assert st == sl.LSTM_ERR_WORKSPACE
+    bad = sl.make_desc(0, 8, 8, 2, 2, "f32")
+    assert sl.lstm_fwd_noalloc(bad, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, None, None, None, 0) == \
+        sl.LSTM_ERR_INVALID_ARG
+    small = sl.make_desc(1, 8, 8, 2, 2, "f32")
+    assert sl.lstm_fwd_noalloc(small, None, None, None, FAKE, FAKE, FAKE, FAKE, None, None, None, 0) == \
+        sl.LSTM_ERR_INVALID_ARG
