@@ -10,6 +10,7 @@
 #include <hip/hip_runtime.h>
 
 #include <mutex>
+#include <vector>
 
 #include "lstm_fwd.h"  // include/ is on the include path
 #include "lstm_params.h"
@@ -276,9 +277,19 @@ lstm_status_t lstm_fwd_ex(const lstm_desc_t* d, const void* x, const void* h0, c
     return (need && launch_vec(lp) && (size_t)slot * ds < (1u << 31)) ? need : 0;
   };
 
-  bool traced = false;  // only the first recurrent launch is traced
-  auto rec = [&](const LaunchPlan& lp) -> lstm_status_t {
+  // Every recurrent launch is prepared -- parameters, kernel variant, LDS
+  // limit, co-residency -- before the first kernel is enqueued, so a refusal
+  // (LSTM_ERR_UNSUPPORTED, LSTM_ERR_HIP) leaves nothing queued.
+  struct RecLaunch {
     RecParams rp;
+    int lds = 0;
+    bool vec = false, frag = false, res = false;
+    const LaunchPlan* lp = nullptr;
+  };
+  std::vector<RecLaunch> launches(p.nrec);
+  bool traced = false;  // only the first recurrent launch is traced
+  auto rec_prepare_launch = [&](const LaunchPlan& lp, RecLaunch& out) -> lstm_status_t {
+    RecParams& rp = out.rp;
     rp.nlayers = lp.nlayers;
     rp.slot = (long long)slot;
     rp.fslot = (long long)slot;
@@ -371,18 +382,29 @@ lstm_status_t lstm_fwd_ex(const lstm_desc_t* d, const void* x, const void* h0, c
     }
     if (pe != hipSuccess) return LSTM_ERR_HIP;
     if ((long long)per_cu * dev.info.num_cus < lp.grid) return LSTM_ERR_UNSUPPORTED;  // not co-resident
+    out.lds = lds, out.vec = vec, out.frag = frag, out.res = res, out.lp = &lp;
+    return LSTM_OK;
+  };
+  for (int r = 0; r < p.nrec; ++r) {
+    st = rec_prepare_launch(p.rec[r], launches[r]);
+    if (st != LSTM_OK) return st;
+  }
+  auto rec = [&](const RecLaunch& rl) -> lstm_status_t {
+    const LaunchPlan& lp = *rl.lp;
     if (!before(LSTM_KERNEL_RECURRENT)) return LSTM_ERR_HIP;
     const bool plain = opts && opts->plain_launch;
-    const hipError_t le = res ? launch_rec_res(bf16, lp.res_nci, lp.res_nrb, rp, lp.lds_bytes, plain, stream)
-                              : launch_rec(bf16, lp.stream, vec, frag, lp.nwaves, rp, lds, plain, stream);
+    const hipError_t le = rl.res ? launch_rec_res(bf16, lp.res_nci, lp.res_nrb, rl.rp, lp.lds_bytes, plain, stream)
+                                 : launch_rec(bf16, lp.stream, rl.vec, rl.frag, lp.nwaves, rl.rp, rl.lds, plain, stream);
     if (le != hipSuccess) return LSTM_ERR_HIP;
     if (!after()) return LSTM_ERR_HIP;
     return LSTM_OK;
   };
+  // the data-valid exchange of launch r (its slots are filled by the input GEMM before it)
+  auto sent_of = [&](int r) -> bool { return launches[r].rp.sent != 0; };
 
   if (p.ngemm > 0) {
     // layer 0 input projection (+ zeroing of the error word and step counters)
-    st = gemm(0, x, (long long)B * I, I, true, (p.regime != LSTM_REGIME_WAVEFRONT && sent_lds(p.rec[0])) ? xbuf(0) : nullptr);
+    st = gemm(0, x, (long long)B * I, I, true, (p.regime != LSTM_REGIME_WAVEFRONT && sent_of(0)) ? xbuf(0) : nullptr);
     if (st != LSTM_OK) return st;
   } else {
     // every input product is fused into the steps: only the counters need clearing
@@ -392,16 +414,16 @@ lstm_status_t lstm_fwd_ex(const lstm_desc_t* d, const void* x, const void* h0, c
   }
   if (p.regime == LSTM_REGIME_WAVEFRONT) {
     for (int r = 0; r < p.nrec; ++r) {
-      st = rec(p.rec[r]);
+      st = rec(launches[r]);
       if (st != LSTM_OK) return st;
     }
   } else {
     for (int l = 0; l < L; ++l) {
       if (l > 0) {
-        st = gemm(l, xbuf(l - 1), (long long)slot, H, false, sent_lds(p.rec[l]) ? xbuf(l) : nullptr);
+        st = gemm(l, xbuf(l - 1), (long long)slot, H, false, sent_of(l) ? xbuf(l) : nullptr);
         if (st != LSTM_OK) return st;
       }
-      st = rec(p.rec[l]);
+      st = rec(launches[l]);
       if (st != LSTM_OK) return st;
     }
   }
