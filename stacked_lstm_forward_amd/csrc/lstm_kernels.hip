@@ -186,42 +186,94 @@ __global__ void __launch_bounds__(kGemmThreads) lstm_input_gemm(const GemmParams
 }
 
 // Fast path of the input projection (K a whole number of chunks, every row
-// 16-byte aligned): a 256 x 256 workgroup
-// tile, 4 waves of 128 x 128 (8 x 8 MFMA tiles, accumulators in the
-// accumulation registers).  Operands go from global memory straight into LDS
-// with the gfx950 direct-to-LDS loads (a wave-wide 16-byte load lands lane l
-// at byte 16*l of its LDS destination), two stages deep: chunk c+1 streams in
-// while chunk c is multiplied.
-// Per chunk a wave reads 32 KiB from LDS for 128 MFMAs (2 per tile, chained on
-// one accumulator, which keeps the matrix pipe issuing back to back).
-constexpr int kDmaTiles = 16;                    // M-tiles (and at most column tiles) per workgroup
-constexpr int kDmaStage = 2 * kDmaTiles * 128;   // 16-byte units per LDS stage (64 KiB)
+// 16-byte aligned, operands below 2^31 elements): a 256 x (16 NT) workgroup
+// tile, 8 waves (two per SIMD) of 64 x (8 NT) -- 4 x NT/2 MFMA tiles, the
+// accumulators in the accumulation registers.  Operands go from global memory
+// straight into LDS with gfx950's direct-to-LDS loads (a wave-wide 16-byte load
+// lands lane l at byte 16 l of its LDS destination).
+//
+// Pipeline.  The W rows (A operand) have three LDS stages and the U columns
+// (B operand) two: W comes from HBM (every layer's 128 MiB W is read once per
+// forward and does not stay in the last-level cache), U mostly from the L2 or
+// the last-level cache, so W's loads get two chunks of lead and U's one.  One
+// barrier per chunk, in its middle:
+//   1. read the fragments of the chunk's second K-half from LDS, interleaved
+//      with the MFMAs of its first half (fragments read during the previous
+//      chunk);
+//   2. wait for this wave's loads of the next chunk, and for the reads of 1;
+//   3. barrier: the next chunk is in LDS and nobody reads this chunk's stages
+//      any more;
+//   4. issue the loads of chunk c + 2 (U) and c + 3 (W) into those stages;
+//   5. read the next chunk's first-half fragments, interleaved with the MFMAs
+//      of this chunk's second half.
+// The loads are issued from inline assembly.  The compiler cannot tell which
+// LDS bytes a direct-to-LDS load writes, so after a builtin one it makes every
+// later LDS read wait for all loads in flight -- which would wait for the loads
+// just issued in 4.  Here their completion is tracked by hand (the vmcnt
+// waits in 2; loads complete in issue order).
+constexpr int kDmaTiles = 16;             // M-tiles per workgroup (and at most column tiles)
+constexpr int kDmaWaves = 8;
+constexpr int kDmaThreads = 64 * kDmaWaves;
+constexpr int kDmaAStages = 3, kDmaBStages = 2;
+constexpr int kDmaALoads = 2 * kDmaTiles / kDmaWaves;  // direct-to-LDS loads of W per wave per chunk
+constexpr int kDmaBLoads = 2 * kDmaTiles / kDmaWaves;  // ... of U (at most; NT < 16 repeats the last)
+
+__host__ __device__ constexpr unsigned dma_lds_bytes(int nt) {
+  return (kDmaAStages * kDmaTiles + kDmaBStages * nt) * 2048u;
+}
+
+// One wave-wide direct-to-LDS load of 16 bytes per lane: global `src` ->
+// LDS byte `lds_off` + 16 * lane.  M0 carries the LDS address (the kernel
+// uses M0 for nothing else); its write needs one wait state before the load
+// reads it.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_off) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_off), "v"(src)
+               : "memory");
+}
+
+template <bool BF16>
+__device__ __forceinline__ void mfma_half(f32x4& acc, const uint4& a, const uint4& b);
+template <>
+__device__ __forceinline__ void mfma_half<true>(f32x4& acc, const uint4& a, const uint4& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc, 0,
+                                                0, 0);
+}
+template <>
+__device__ __forceinline__ void mfma_half<false>(f32x4& acc, const uint4& a, const uint4& b) {
+  const float* fa = reinterpret_cast<const float*>(&a);
+  const float* fb = reinterpret_cast<const float*>(&b);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[e], fb[e], acc, 0, 0, 0);
+}
 
 // NT column tiles per workgroup (16, or 14 when that packs the columns into
 // fewer rounds of workgroups than 16 would: see launch_input_gemm); each of
 // the two column-halves of waves takes NT / 2.
 template <bool BF16, int NT>
-__global__ void __launch_bounds__(kGemmThreads) lstm_input_gemm_dma(const GemmParams P) {
+__global__ void __launch_bounds__(kDmaThreads) lstm_input_gemm_dma(const GemmParams P) {
   static_assert(NT % 2 == 0 && NT <= kDmaTiles, "column tiles per workgroup");
-  constexpr int WN = NT / 2;  // column tiles per wave
+  constexpr int WM = kDmaTiles / 4;          // M-tiles per wave (4 M-quarters x 2 column halves)
+  constexpr int WN = NT / 2;                 // column tiles per wave
   typedef typename Dt<BF16>::T T;
-  typedef __attribute__((address_space(1))) const void* gptr_t;
-  typedef __attribute__((address_space(3))) void* lptr_t;
   constexpr int KC = Dt<BF16>::KC;
+  constexpr uint32_t kABytes = kDmaTiles * 2048, kBBytes = NT * 2048;  // one stage
   extern __shared__ __align__(16) unsigned char gsmem[];
-  uint4* lds = reinterpret_cast<uint4*>(gsmem);
+  const uint4* lds = reinterpret_cast<const uint4*>(gsmem);
+  // LDS byte address of the dynamic area (M0 takes LDS addresses, not generic ones)
+  typedef __attribute__((address_space(3))) unsigned char lds_byte_t;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_byte_t*)gsmem;
 
   const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   if (P.zero_ptr) {  // grid-stride zeroing of the error word and step counters
     const long nwg = (long)gridDim.x * gridDim.y;
     const long wg = (long)blockIdx.y * gridDim.x + blockIdx.x;
-    for (long i = wg * kGemmThreads + tid; i < P.zero_count; i += nwg * kGemmThreads) P.zero_ptr[i] = 0;
+    for (long i = wg * kDmaThreads + tid; i < P.zero_count; i += nwg * kDmaThreads) P.zero_ptr[i] = 0;
   }
   if (P.fill_ptr) {  // grid-stride: the unwritten pattern of a data-valid exchange
     const long nwg = (long)gridDim.x * gridDim.y;
     const long wg = (long)blockIdx.y * gridDim.x + blockIdx.x;
-    for (long i = wg * kGemmThreads + tid; i < P.fill_count; i += nwg * kGemmThreads) P.fill_ptr[i] = kSentinelWord;
+    for (long i = wg * kDmaThreads + tid; i < P.fill_count; i += nwg * kDmaThreads) P.fill_ptr[i] = kSentinelWord;
   }
   // Tile order: the 1-D grid (a multiple of 8) goes round-robin over the 8
   // XCDs, so workgroup ids are first regrouped into one contiguous range per
@@ -245,99 +297,132 @@ __global__ void __launch_bounds__(kGemmThreads) lstm_input_gemm_dma(const GemmPa
   const long n0 = (long)nblk * NT * 16;              // first column
   const int nch = P.K / KC;
 
-  // staging: wave w fills fragment blocks 8w .. 8w+7 of every stage (blocks
-  // 0-15: the A tiles, W rows; 16-31: the B tiles, columns of U).  A block
-  // holds its 16 rows' 128-byte chunks row by row, 8 pieces of 16 bytes each,
-  // piece p of row r in slot p ^ ((r >> 1) & 7).  One wave-wide load fills half
-  // a block: 8 whole rows, lane l row 8i + l/8, slot l%8, so every load reads
-  // whole 128-byte lines (a load of 16 rows x 64 bytes costs the texture path
-  // several times more), and the swizzle keeps the fragment reads below free
-  // of bank conflicts.  Rows and columns past the end are clamped to valid
-  // ones (results unused).
+  // Staging.  A block holds its 16 rows' 128-byte chunks row by row, 8 pieces
+  // of 16 bytes each, piece p of row r in slot p ^ ((r >> 1) & 7).  One
+  // wave-wide load fills half a block: 8 whole rows, lane l row 8i + l/8, slot
+  // l%8, so every load reads whole 128-byte lines (a load of 16 rows x 64 bytes
+  // costs the texture path several times more), and the swizzle keeps the
+  // fragment reads below free of bank conflicts.  Rows and columns past the
+  // end are clamped to valid ones (results unused).
+  // Wave w loads W load-slots w*kDmaALoads + k and U load-slots w*kDmaBLoads + k
+  // (slot j: block j/2, half j%2; U slots past 2 NT repeat the last one).
   constexpr int EPH = 16 / Dt<BF16>::SZ;  // elements of one 16-byte piece
-  const T* gbase = reinterpret_cast<const T*>(wave < 2 ? P.W : P.U);
-  long src[8][2];
+  const T* Wg = reinterpret_cast<const T*>(P.W);
+  const T* Ug = reinterpret_cast<const T*>(P.U);
+  uint32_t srcA[kDmaALoads], srcB[kDmaBLoads];  // element offsets (the launcher keeps them below 2^31)
+  uint32_t dstA[kDmaALoads], dstB[kDmaBLoads];  // byte offsets inside a stage (wave-uniform)
 #pragma unroll
-  for (int s8 = 0; s8 < 8; ++s8) {
-    const int blk = 8 * wave + s8;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = 8 * i + (lane >> 3);
-      const long piece = (lane & 7) ^ ((r >> 1) & 7);
-      if (wave < 2) {
-        const int mt = mtb + blk;
-        long row = mt < P.Mt ? cell_row(P.cell, mt, r, P.H).w : -1;
-        src[s8][i] = (row < 0 ? 0 : row) * P.K + piece * EPH;
-      } else {
-        long col = n0 + 16 * (blk - kDmaTiles) + r;
-        col = col < P.N ? col : P.N - 1;
-        // column n: step n / B, sequence n % B
-        src[s8][i] = (col / P.B) * P.u_slot + (col % P.B) * P.K + piece * EPH;
-      }
-    }
+  for (int k = 0; k < kDmaALoads; ++k) {
+    const int j = wave * kDmaALoads + k, blk = j / 2, i = j % 2;
+    const int r = 8 * i + (lane >> 3);
+    const long piece = (lane & 7) ^ ((r >> 1) & 7);
+    const int mt = mtb + blk;
+    const long row = mt < P.Mt ? cell_row(P.cell, mt, r, P.H).w : -1;
+    srcA[k] = (uint32_t)((row < 0 ? 0 : row) * P.K + piece * EPH);
+    dstA[k] = blk * 2048 + i * 1024;
   }
-  auto stage_load = [&](int c, int buf) {
 #pragma unroll
-    for (int s8 = 0; s8 < 8; ++s8) {
-      if (8 * wave + s8 >= kDmaTiles + NT) continue;  // a column block past NT (wave-uniform)
+  for (int k = 0; k < kDmaBLoads; ++k) {
+    const int j = min(wave * kDmaBLoads + k, 2 * NT - 1), blk = j / 2, i = j % 2;
+    const int r = 8 * i + (lane >> 3);
+    const long piece = (lane & 7) ^ ((r >> 1) & 7);
+    long col = n0 + 16 * blk + r;
+    col = col < P.N ? col : P.N - 1;
+    // column n: step n / B, sequence n % B
+    srcB[k] = (uint32_t)((col / P.B) * P.u_slot + (col % P.B) * P.K + piece * EPH);
+    dstB[k] = blk * 2048 + i * 1024;
+  }
+  // chunk indices are clamped, so every iteration issues the same loads
+  auto load_A = [&](int c) {
+    const uint32_t st = lds_base + (uint32_t)(c % kDmaAStages) * kABytes;
+    const uint32_t ko = (uint32_t)min(c, nch - 1) * KC;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const T* g = gbase + src[s8][i] + (long)c * KC;
-        uint4* l = lds + buf * kDmaStage + (8 * wave + s8) * 128 + i * 64;
-        __builtin_amdgcn_global_load_lds((gptr_t)g, (lptr_t)l, 16, 0, 0);
-      }
-    }
+    for (int k = 0; k < kDmaALoads; ++k) dma16(Wg + (srcA[k] + ko), st + dstA[k]);
   };
-  // this lane's two fragment halves (row lane%16, pieces 4h + lane/16) in a block
-  const int fr_ = lane & 15, fsw = (fr_ >> 1) & 7;
-  const int foff0 = fr_ * 8 + ((0 + q) ^ fsw), foff1 = fr_ * 8 + ((4 + q) ^ fsw);
-  auto frag_at = [&](const uint4* blk) {
-    Frag f;
-    f.v[0] = blk[foff0];
-    f.v[1] = blk[foff1];
-    return f;
+  auto load_B = [&](int c) {
+    const uint32_t st = lds_base + kDmaAStages * kABytes + (uint32_t)(c % kDmaBStages) * kBBytes;
+    const uint32_t ko = (uint32_t)min(c, nch - 1) * KC;
+#pragma unroll
+    for (int k = 0; k < kDmaBLoads; ++k) dma16(Ug + (srcB[k] + ko), st + dstB[k]);
   };
 
-  const int wm = wave & 1, wn = wave >> 1;
-  f32x4 acc[8][WN];
+  // this lane's fragment halves (row lane%16, piece 4h + lane/16) in a block
+  const int fr_ = lane & 15, fsw = (fr_ >> 1) & 7;
+  const int foff0 = fr_ * 8 + ((0 + q) ^ fsw), foff1 = fr_ * 8 + ((4 + q) ^ fsw);
+  const int wm = wave & 3, wn = wave >> 2;
+  uint4 fa[2][WM], fb[2][WN];  // fragment halves: [K-half][tile]
+  auto read_half = [&](int c, int h) {
+    const uint4* sa = lds + (c % kDmaAStages) * (kABytes / 16);
+    const uint4* sb = lds + (kDmaAStages * kABytes + (c % kDmaBStages) * kBBytes) / 16;
+    const int fo = h ? foff1 : foff0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+    for (int j = 0; j < WN; ++j) fb[h][j] = sb[(WN * wn + j) * 128 + fo];
+#pragma unroll
+    for (int i = 0; i < WM; ++i) fa[h][i] = sa[(WM * wm + i) * 128 + fo];
+  };
+
+  f32x4 acc[WM][WN];
+#pragma unroll
+  for (int i = 0; i < WM; ++i)
 #pragma unroll
     for (int j = 0; j < WN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (nch > 0) stage_load(0, 0);
+  auto mfma_phase = [&](int h) {
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+      for (int j = 0; j < WN; ++j) mfma_half<BF16>(acc[i][j], fa[h][i], fb[h][j]);
+  };
+  // one fragment read, then a few MFMAs (the reads fill the other register
+  // set, so no wait separates them from these MFMAs)
+  constexpr int kReads = WM + WN;                       // fragment reads per K-half
+  constexpr int kMfmas = WM * WN * (BF16 ? 1 : 4);      // MFMAs per K-half
+  constexpr int kPer = kMfmas / kReads;
+  auto interleave = [&]() {
+#pragma unroll
+    for (int k = 0; k < kReads; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // one LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, kPer, 0);  // then MFMAs
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kMfmas - kPer * kReads, 0);
+  };
+
+  // prologue: W chunks 0 and 1, U chunk 0 in flight; wait for chunk 0
+  load_A(0);
+  load_B(0);
+  load_A(1);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kDmaALoads) : "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  load_B(1);
+  load_A(2);
+  read_half(0, 0);
   for (int c = 0; c < nch; ++c) {
-    // this wave's loads of chunk c have landed (nothing else is outstanding);
-    // after the barrier everybody's have, and nobody still reads buffer (c+1)&1
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    // Every operand of chunk c is read from LDS before chunk c+1's loads are
-    // issued: the compiler cannot tell that those loads fill the other buffer,
-    // and an LDS read issued after them would first wait for all of them,
-    // which would serialise each chunk's loads with the previous chunk's MFMAs.
-    const uint4* st = lds + (c & 1) * kDmaStage;
-    Frag a[8], b[WN];
-#pragma unroll
-    for (int j = 0; j < WN; ++j) b[j] = frag_at(st + (kDmaTiles + WN * wn + j) * 128);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) a[i] = frag_at(st + (8 * wm + i) * 128);
-    // (unconditional, so no branch separates the reads from the MFMAs: the last
-    // iteration loads its own chunk again into the idle buffer)
-    __builtin_amdgcn_sched_barrier(0);
-    stage_load(min(c + 1, nch - 1), (c + 1) & 1);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int j = 0; j < WN; ++j) mfma_frag<BF16>(acc[i][j], a[i], b[j]);
+    // 1. second-half fragments of chunk c while the first half multiplies
+    read_half(c, 1);
+    mfma_phase(0);
+    interleave();
+    // 2. this wave's loads of chunk c + 1 have landed (only W's chunk c + 2
+    //    may still be in flight), and so have the reads above
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(kDmaALoads) : "memory");
+    // 3. everybody's have; nobody reads chunk c's stages any more
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    // 4. refill them: U chunk c + 2, W chunk c + 3
+    load_B(c + 2);
+    load_A(c + 3);
+    // 5. first-half fragments of chunk c + 1 while the second half multiplies
+    read_half(c + 1, 0);
+    mfma_phase(1);
+    interleave();
   }
-  __builtin_amdgcn_s_waitcnt(0);  // the last (redundant) loads have landed
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the last (redundant) loads have landed
 
   // epilogue: add bias, write [T][Mt][B][16]
   const T* bias = reinterpret_cast<const T*>(P.bias);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int mt = mtb + 8 * wm + i;
+  for (int i = 0; i < WM; ++i) {
+    const int mt = mtb + WM * wm + i;
     if (mt >= P.Mt) continue;
     f32x4 bv;       // this lane's four rows 4*(lane/16) + k of the tile (rows past H are never read)
     bool wrow[4];   // false: the row has no input weights (the GRU's recurrent half of n), so its
@@ -455,8 +540,11 @@ hipError_t launch_input_gemm(bool bf16, const GemmParams& p, hipStream_t s) {
   // the 256 x 256 direct-to-LDS kernel pays off on long K (measured: 0.45 vs
   // 0.53 ms at K = 4096, 0.33 vs 0.35 ms at K = 1536); short K keeps the
   // register-staged 256 x 128 kernel, whose smaller tiles fill more CUs
-  if (p.vec_ok_w && p.vec_ok_u && whole && p.K >= 1024) {
-    const unsigned lds = 2 * kDmaStage * sizeof(uint4);
+  // element offsets of the direct-to-LDS kernel are 32-bit
+  const long long w_elems = (long long)p.Mt * 16 * p.K;  // at most G*H rows (tile rows past H are clamped)
+  const long long u_elems = (long long)((p.N - 1) / p.B) * p.u_slot + (long long)p.B * p.K;
+  const bool small_offsets = w_elems < (1LL << 31) && u_elems < (1LL << 31);
+  if (p.vec_ok_w && p.vec_ok_u && whole && p.K >= 1024 && small_offsets) {
     // 14 column tiles per workgroup instead of 16 when that needs no more
     // rounds of one workgroup per CU: each round then loads 30 fragment
     // blocks per chunk instead of 32 (the 16384 x 1600 projection of a
@@ -467,17 +555,29 @@ hipError_t launch_input_gemm(bool bf16, const GemmParams& p, hipStream_t s) {
       const int cus = p.num_cus > 0 ? p.num_cus : 256;
       return (nM * ((p.N + nt * 16 - 1) / (nt * 16)) + cus - 1) / cus;
     };
-    const int nt = rounds(14) * (kDmaTiles + 14) < rounds(16) * (kDmaTiles + 16) ? 14 : 16;
-    const void* fn = nt == 14 ? (bf16 ? reinterpret_cast<const void*>(&lstm_input_gemm_dma<true, 14>)
-                                      : reinterpret_cast<const void*>(&lstm_input_gemm_dma<false, 14>))
-                              : (bf16 ? reinterpret_cast<const void*>(&lstm_input_gemm_dma<true, 16>)
-                                      : reinterpret_cast<const void*>(&lstm_input_gemm_dma<false, 16>));
-    hipError_t e = prepare_fn(fn, (int)lds, kGemmThreads, nullptr);
+    int nt = rounds(14) * (kDmaTiles + 14) < rounds(16) * (kDmaTiles + 16) ? 14 : 16;
+    auto kernel_of = [&](int n) {
+      return n == 14 ? (bf16 ? reinterpret_cast<const void*>(&lstm_input_gemm_dma<true, 14>)
+                             : reinterpret_cast<const void*>(&lstm_input_gemm_dma<false, 14>))
+                     : (bf16 ? reinterpret_cast<const void*>(&lstm_input_gemm_dma<true, 16>)
+                             : reinterpret_cast<const void*>(&lstm_input_gemm_dma<false, 16>));
+    };
+    const void* fn = kernel_of(nt);
+    // 16 column tiles take all 160 KiB of a CU's LDS; a device that gives a
+    // workgroup less falls back to 14 (152 KiB)
+    hipError_t e = prepare_fn(fn, (int)dma_lds_bytes(nt), kDmaThreads, nullptr);
+    if (e != hipSuccess && nt == 16) {
+      (void)hipGetLastError();
+      nt = 14;
+      fn = kernel_of(nt);
+      e = prepare_fn(fn, (int)dma_lds_bytes(nt), kDmaThreads, nullptr);
+    }
     if (e != hipSuccess) return e;
+    const unsigned lds = dma_lds_bytes(nt);
     const int tiles = ((p.N + nt * 16 - 1) / (nt * 16)) * nM;
     const dim3 grid((tiles + 7) & ~7);  // a multiple of the 8 XCDs (extra workgroups only help zeroing)
     void* args[] = {const_cast<GemmParams*>(&p)};
-    return hipLaunchKernel(fn, grid, dim3(kGemmThreads), args, lds, s);
+    return hipLaunchKernel(fn, grid, dim3(kDmaThreads), args, lds, s);
   }
   const bool vec = p.vec_ok_w && p.vec_ok_u && (p.K % (bf16 ? Dt<true>::KC : Dt<false>::KC)) == 0;
   // A problem the 256 x 128 tile covers with fewer than kGemmSmallGrid
