@@ -129,6 +129,19 @@ __device__ __forceinline__ Frag load_frag(const void* base, long ld, long row, i
   return load_frag_off<BF16>(base, row * ld, k0, q, K, vec_ok);
 }
 
+// One wave-wide direct-to-LDS load of 16 bytes per lane: global
+// `base` + `voff` (base wave-uniform, in scalar registers; voff this lane's byte
+// offset) -> LDS byte `lds_off` + 16 * lane.  Written as inline assembly so
+// that the compiler, which cannot tell which LDS bytes such a load writes,
+// does not make every later LDS read wait for all of them; the kernels that
+// use it track its completion themselves (s_waitcnt vmcnt; loads complete in
+// issue order).  M0 carries the LDS address (those kernels use M0 for nothing
+// else); its write needs one wait state before the load reads it.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds_off) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_off), "v"(voff), "s"(base)
+               : "memory");
+}
+
 // f &= mask on every 32-bit word (mask 0 zeroes a fragment without a branch)
 __device__ __forceinline__ void frag_mask(Frag& f, uint32_t m) {
 #pragma unroll

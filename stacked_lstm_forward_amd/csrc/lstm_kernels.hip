@@ -222,15 +222,6 @@ __host__ __device__ constexpr unsigned dma_lds_bytes(int nt) {
   return (kDmaAStages * kDmaTiles + kDmaBStages * nt) * 2048u;
 }
 
-// One wave-wide direct-to-LDS load of 16 bytes per lane: global `src` ->
-// LDS byte `lds_off` + 16 * lane.  M0 carries the LDS address (the kernel
-// uses M0 for nothing else); its write needs one wait state before the load
-// reads it.
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds_off) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_off), "v"(src)
-               : "memory");
-}
-
 template <bool BF16>
 __device__ __forceinline__ void mfma_half(f32x4& acc, const uint4& a, const uint4& b);
 template <>
@@ -309,7 +300,7 @@ __global__ void __launch_bounds__(kDmaThreads) lstm_input_gemm_dma(const GemmPar
   constexpr int EPH = 16 / Dt<BF16>::SZ;  // elements of one 16-byte piece
   const T* Wg = reinterpret_cast<const T*>(P.W);
   const T* Ug = reinterpret_cast<const T*>(P.U);
-  uint32_t srcA[kDmaALoads], srcB[kDmaBLoads];  // element offsets (the launcher keeps them below 2^31)
+  uint32_t srcA[kDmaALoads], srcB[kDmaBLoads];  // byte offsets (the launcher keeps them below 2^32)
   uint32_t dstA[kDmaALoads], dstB[kDmaBLoads];  // byte offsets inside a stage (wave-uniform)
 #pragma unroll
   for (int k = 0; k < kDmaALoads; ++k) {
@@ -318,7 +309,7 @@ __global__ void __launch_bounds__(kDmaThreads) lstm_input_gemm_dma(const GemmPar
     const long piece = (lane & 7) ^ ((r >> 1) & 7);
     const int mt = mtb + blk;
     const long row = mt < P.Mt ? cell_row(P.cell, mt, r, P.H).w : -1;
-    srcA[k] = (uint32_t)((row < 0 ? 0 : row) * P.K + piece * EPH);
+    srcA[k] = (uint32_t)(((row < 0 ? 0 : row) * P.K + piece * EPH) * (long)sizeof(T));
     dstA[k] = blk * 2048 + i * 1024;
   }
 #pragma unroll
@@ -329,21 +320,22 @@ __global__ void __launch_bounds__(kDmaThreads) lstm_input_gemm_dma(const GemmPar
     long col = n0 + 16 * blk + r;
     col = col < P.N ? col : P.N - 1;
     // column n: step n / B, sequence n % B
-    srcB[k] = (uint32_t)((col / P.B) * P.u_slot + (col % P.B) * P.K + piece * EPH);
+    srcB[k] = (uint32_t)(((col / P.B) * P.u_slot + (col % P.B) * P.K + piece * EPH) * (long)sizeof(T));
     dstB[k] = blk * 2048 + i * 1024;
   }
   // chunk indices are clamped, so every iteration issues the same loads
+  // (the chunk's column offset goes into the scalar base address)
   auto load_A = [&](int c) {
     const uint32_t st = lds_base + (uint32_t)(c % kDmaAStages) * kABytes;
-    const uint32_t ko = (uint32_t)min(c, nch - 1) * KC;
+    const T* base = Wg + (long)min(c, nch - 1) * KC;
 #pragma unroll
-    for (int k = 0; k < kDmaALoads; ++k) dma16(Wg + (srcA[k] + ko), st + dstA[k]);
+    for (int k = 0; k < kDmaALoads; ++k) dma16(base, srcA[k], st + dstA[k]);
   };
   auto load_B = [&](int c) {
     const uint32_t st = lds_base + kDmaAStages * kABytes + (uint32_t)(c % kDmaBStages) * kBBytes;
-    const uint32_t ko = (uint32_t)min(c, nch - 1) * KC;
+    const T* base = Ug + (long)min(c, nch - 1) * KC;
 #pragma unroll
-    for (int k = 0; k < kDmaBLoads; ++k) dma16(Ug + (srcB[k] + ko), st + dstB[k]);
+    for (int k = 0; k < kDmaBLoads; ++k) dma16(base, srcB[k], st + dstB[k]);
   };
 
   // this lane's fragment halves (row lane%16, piece 4h + lane/16) in a block
@@ -540,10 +532,11 @@ hipError_t launch_input_gemm(bool bf16, const GemmParams& p, hipStream_t s) {
   // the 256 x 256 direct-to-LDS kernel pays off on long K (measured: 0.45 vs
   // 0.53 ms at K = 4096, 0.33 vs 0.35 ms at K = 1536); short K keeps the
   // register-staged 256 x 128 kernel, whose smaller tiles fill more CUs
-  // element offsets of the direct-to-LDS kernel are 32-bit
-  const long long w_elems = (long long)p.Mt * 16 * p.K;  // at most G*H rows (tile rows past H are clamped)
-  const long long u_elems = (long long)((p.N - 1) / p.B) * p.u_slot + (long long)p.B * p.K;
-  const bool small_offsets = w_elems < (1LL << 31) && u_elems < (1LL << 31);
+  // byte offsets of the direct-to-LDS kernel are 32-bit
+  const long long esz = bf16 ? 2 : 4;
+  const long long w_bytes = (long long)p.Mt * 16 * p.K * esz;  // at most G*H rows (tile rows past H are clamped)
+  const long long u_bytes = ((long long)((p.N - 1) / p.B) * p.u_slot + (long long)p.B * p.K) * esz;
+  const bool small_offsets = w_bytes < (1LL << 32) && u_bytes < (1LL << 32);
   if (p.vec_ok_w && p.vec_ok_u && whole && p.K >= 1024 && small_offsets) {
     // 14 column tiles per workgroup instead of 16 when that needs no more
     // rounds of one workgroup per CU: each round then loads 30 fragment
