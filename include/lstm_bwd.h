@@ -1,0 +1,78 @@
+/*
+ * lstm_bwd.h -- C ABI of the stacked-LSTM training passes on MI355X (gfx950):
+ * a forward pass that keeps what the backward pass needs, and the backward
+ * pass (backpropagation through time) itself.
+ *
+ * The backward pass is the chain rule through the forward definition of
+ * lstm_fwd.h (LSTM cell only).  Per layer from the top down and per step from
+ * the last to the first, with dh_rec and dc_rec the gradients reaching h_t and
+ * c_t through step t+1 (dhT and dcT at the last step):
+ *     dh    = dY[t] + dh_rec                       (dY: dy for the top layer,
+ *                                                  else the layer above's input gradient)
+ *     dc    = dh o (1 - tanh(c_t)^2) + dc_rec
+ *     dp    = [dc g i(1-i), dc c_{t-1} f(1-f), dc i (1-g^2), dh tanh(c_t) o(1-o)]
+ *     dh_rec = dp R_l ,   dc_rec = dc f
+ * and then, once the dp of every step are known, the weight and input
+ * gradients as single products over all T*B columns
+ *     dW_l = dP^T U ,  dR_l = dP^T H_prev ,  db_l = sum of dP over the columns ,
+ *     dU = dP W_l  (the layer below's dY, or dx)
+ * ("Optimizing Performance of Recurrent Neural Networks on GPUs", proposed
+ * method: the weight update done as one large product, and the layers'
+ * backward passes able to follow one another).
+ *
+ * Layouts (dense, row-major): the forward tensors as in lstm_fwd.h.
+ *   reserve  written by lstm_fwd_train, read by lstm_bwd; lstm_train_reserve_size
+ *            bytes: for every layer l, the activated gates [T][B][4H] fp32 (blocks
+ *            i, f, g, o), then for every layer c_t [T][B][H] fp32, then for every
+ *            layer h_t [T][B][H] in dtype.  Its contents are meaningful only
+ *            between an lstm_fwd_train and the lstm_bwd of the same inputs.
+ *   dy [T][B][H], dhT, dcT [L][B][H]                         fp32 (dhT, dcT: NULL = zero)
+ *   dx [T][B][I], dh0, dc0 [L][B][H]                         fp32 (NULL: not written)
+ *   dW like W, dR like R, db like b                          fp32 (required)
+ * Arithmetic: the per-step gate derivatives in fp32; every product in the
+ * workload's dtype with fp32 accumulation (bf16 workloads multiply bf16
+ * operands, as their forward does).
+ *
+ * Ownership: every pointer is a device pointer owned by the caller.  `ws` must
+ * hold lstm_bwd_workspace_size(desc) bytes, 256-byte aligned; its contents on
+ * entry are ignored.  Work is enqueued on `stream` asynchronously.
+ *
+ * Errors: status codes as in lstm_fwd.h, checked on the host before anything
+ * is enqueued; a cell other than the LSTM returns LSTM_ERR_UNSUPPORTED.
+ */
+#ifndef LSTM_BWD_H
+#define LSTM_BWD_H
+
+#include "lstm_fwd.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Bytes of the reserve buffer for `d` (0: invalid, or a cell other than the LSTM). */
+size_t lstm_train_reserve_size(const lstm_desc_t *d);
+
+/* lstm_fwd that also fills `reserve` (required); `ws` as for lstm_fwd. */
+lstm_status_t lstm_fwd_train(const lstm_desc_t *d,
+                             const void *x, const void *h0, const float *c0,
+                             const void *W, const void *R, const void *b,
+                             void *y, void *hT, float *cT,
+                             void *reserve, void *ws, hipStream_t stream);
+
+/* Bytes of the workspace lstm_bwd needs for `d` (0: invalid or unsupported). */
+size_t lstm_bwd_workspace_size(const lstm_desc_t *d);
+
+/* Backward pass: gradients of every forward input from dy, dhT and dcT. */
+lstm_status_t lstm_bwd(const lstm_desc_t *d,
+                       const void *x, const void *h0, const float *c0,
+                       const void *W, const void *R, const void *reserve,
+                       const float *dy, const float *dhT, const float *dcT,
+                       float *dx, float *dh0, float *dc0,
+                       float *dW, float *dR, float *db,
+                       void *ws, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LSTM_BWD_H */

@@ -14,6 +14,9 @@ The functions carry the C names:
     lstm_fwd_plan(desc, force_regime=0, num_cus=0, lds_per_cu=0) -> PlanInfo
     lstm_status_string(status) -> str
     lstm_fwd_noalloc(desc, x, h0, c0, W, R, b, y, hT, cT, dev_status=None, stream=None) -> status
+    lstm_train_reserve_size(desc), lstm_bwd_workspace_size(desc) -> int
+    lstm_fwd_train(desc, x, h0, c0, W, R, b, y, hT, cT, reserve, ws, stream=None) -> status
+    lstm_bwd(desc, x, h0, c0, W, R, reserve, dy, dhT, dcT, dx, dh0, dc0, dW, dR, db, ws, stream=None) -> status
 
 Tensor arguments may be torch tensors (their ``data_ptr()``), raw integer
 device addresses, or None for the nullable ones (h0, c0, hT, cT).
@@ -38,6 +41,7 @@ CELL_IDS = {"lstm": LSTM_CELL_LSTM, "gru": LSTM_CELL_GRU, "rnn_tanh": LSTM_CELL_
 EXPORTED = ("lstm_fwd_workspace_size", "lstm_fwd", "lstm_fwd_ex", "lstm_status_string",
             "lstm_fwd_validate", "lstm_fwd_last_error", "lstm_fwd_plan", "lstm_fwd_noalloc")
 NOALLOC_MAX_WORKSPACE = 64 << 20  # LSTM_FWD_NOALLOC_MAX_WORKSPACE
+EXPORTED_TRAIN = ("lstm_train_reserve_size", "lstm_fwd_train", "lstm_bwd_workspace_size", "lstm_bwd")
 
 
 class LstmDesc(ctypes.Structure):
@@ -112,6 +116,14 @@ def load_library() -> ctypes.CDLL:
     lib.lstm_fwd_plan.restype = i32
     lib.lstm_fwd_noalloc.argtypes = [pdesc, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.lstm_fwd_noalloc.restype = i32
+    lib.lstm_train_reserve_size.argtypes = [pdesc]
+    lib.lstm_train_reserve_size.restype = sz
+    lib.lstm_bwd_workspace_size.argtypes = [pdesc]
+    lib.lstm_bwd_workspace_size.restype = sz
+    lib.lstm_fwd_train.argtypes = [pdesc, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.lstm_fwd_train.restype = i32
+    lib.lstm_bwd.argtypes = [pdesc] + [vp] * 17
+    lib.lstm_bwd.restype = i32
     _lib = lib
     return lib
 
@@ -161,6 +173,27 @@ def lstm_fwd_noalloc(desc, x, h0, c0, W, R, b, y, hT, cT, dev_status=None, strea
     return int(load_library().lstm_fwd_noalloc(None if desc is None else ctypes.byref(desc), _ptr(x), _ptr(h0),
                                                _ptr(c0), _ptr(W), _ptr(R), _ptr(b), _ptr(y), _ptr(hT), _ptr(cT),
                                                _ptr(dev_status), _stream(stream)))
+
+
+def lstm_train_reserve_size(desc) -> int:
+    return int(load_library().lstm_train_reserve_size(ctypes.byref(desc)))
+
+
+def lstm_bwd_workspace_size(desc) -> int:
+    return int(load_library().lstm_bwd_workspace_size(ctypes.byref(desc)))
+
+
+def lstm_fwd_train(desc, x, h0, c0, W, R, b, y, hT, cT, reserve, ws, stream=None) -> int:
+    return int(load_library().lstm_fwd_train(ctypes.byref(desc), _ptr(x), _ptr(h0), _ptr(c0), _ptr(W), _ptr(R),
+                                             _ptr(b), _ptr(y), _ptr(hT), _ptr(cT), _ptr(reserve), _ptr(ws),
+                                             _stream(stream)))
+
+
+def lstm_bwd(desc, x, h0, c0, W, R, reserve, dy, dhT, dcT, dx, dh0, dc0, dW, dR, db, ws, stream=None) -> int:
+    return int(load_library().lstm_bwd(None if desc is None else ctypes.byref(desc), _ptr(x), _ptr(h0), _ptr(c0),
+                                       _ptr(W), _ptr(R), _ptr(reserve), _ptr(dy), _ptr(dhT), _ptr(dcT), _ptr(dx),
+                                       _ptr(dh0), _ptr(dc0), _ptr(dW), _ptr(dR), _ptr(db), _ptr(ws),
+                                       _stream(stream)))
 
 
 def lstm_fwd_validate(desc, x, W, R, b, y, ws, ws_bytes: int) -> int:

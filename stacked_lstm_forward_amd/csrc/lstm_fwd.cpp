@@ -12,7 +12,8 @@
 #include <mutex>
 #include <vector>
 
-#include "lstm_fwd.h"  // include/ is on the include path
+#include "lstm_bwd.h"  // include/ is on the include path
+#include "lstm_fwd.h"
 #include "lstm_params.h"
 #include "lstm_plan.h"
 
@@ -163,11 +164,18 @@ lstm_status_t lstm_fwd_last_error(const void* ws, hipStream_t stream) {
   return v == 0 ? LSTM_OK : LSTM_ERR_BARRIER_TIMEOUT;
 }
 
-lstm_status_t lstm_fwd_ex(const lstm_desc_t* d, const void* x, const void* h0, const float* c0, const void* W,
-                          const void* R, const void* b, void* y, void* hT, float* cT, void* ws, hipStream_t stream,
-                          const lstm_fwd_opts_t* opts) {
+}  // extern "C"
+
+namespace {
+
+// The forward pass.  `reserve` (training forward, LSTM only) receives every
+// layer's activated gates, cell states and hidden states (lstm_bwd.h layout).
+lstm_status_t fwd_impl(const lstm_desc_t* d, const void* x, const void* h0, const float* c0, const void* W,
+                       const void* R, const void* b, void* y, void* hT, float* cT, void* ws, hipStream_t stream,
+                       const lstm_fwd_opts_t* opts, void* reserve) {
   lstm_status_t st = validate(d, x, W, R, b, y, ws);
   if (st != LSTM_OK) return st;
+  if (reserve && d->cell != LSTM_CELL_LSTM) return LSTM_ERR_UNSUPPORTED;
   DevCache dev;
   st = device_info(&dev);
   if (st != LSTM_OK) return st;
@@ -341,6 +349,14 @@ lstm_status_t lstm_fwd_ex(const lstm_desc_t* d, const void* x, const void* h0, c
       r.mt_per_wg = pl.mt_per_wg;
       r.staged = pl.staged;
       r.vec_ok = layer_vec(pl) ? 1 : 0;
+      r.save_gates = nullptr, r.save_c = nullptr, r.save_h = nullptr;
+      if (reserve) {
+        const size_t tbh = (size_t)T * B * H;
+        char* rb = static_cast<char*>(reserve);
+        r.save_gates = reinterpret_cast<float*>(rb + (size_t)l * tbh * 16);
+        r.save_c = reinterpret_cast<float*>(rb + (size_t)L * tbh * 16 + (size_t)l * tbh * 4);
+        r.save_h = static_cast<void*>(rb + (size_t)L * tbh * 20 + (size_t)l * tbh * ds);
+      }
     }
     for (int k = lp.nlayers; k < kMaxLayersPerLaunch; ++k) rp.layer[k] = RecLayer();
     // aligned fast path: whole chunks and 16-byte aligned rows in every layer of the launch
@@ -429,6 +445,29 @@ lstm_status_t lstm_fwd_ex(const lstm_desc_t* d, const void* x, const void* h0, c
   }
   if (opts && opts->num_launches) *opts->num_launches = nl;
   return LSTM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+lstm_status_t lstm_fwd_ex(const lstm_desc_t* d, const void* x, const void* h0, const float* c0, const void* W,
+                          const void* R, const void* b, void* y, void* hT, float* cT, void* ws, hipStream_t stream,
+                          const lstm_fwd_opts_t* opts) {
+  return fwd_impl(d, x, h0, c0, W, R, b, y, hT, cT, ws, stream, opts, nullptr);
+}
+
+size_t lstm_train_reserve_size(const lstm_desc_t* d) {
+  if (!d || d->cell != LSTM_CELL_LSTM || lstm_fwd_workspace_size(d) == 0) return 0;
+  const size_t tbh = (size_t)d->L * d->T * d->B * d->H;
+  return (tbh * (16 + 4 + (d->dtype == LSTM_BF16 ? 2 : 4)) + 255) & ~(size_t)255;
+}
+
+lstm_status_t lstm_fwd_train(const lstm_desc_t* d, const void* x, const void* h0, const float* c0, const void* W,
+                             const void* R, const void* b, void* y, void* hT, float* cT, void* reserve, void* ws,
+                             hipStream_t stream) {
+  if (!reserve) return LSTM_ERR_INVALID_ARG;
+  return fwd_impl(d, x, h0, c0, W, R, b, y, hT, cT, ws, stream, nullptr, reserve);
 }
 
 lstm_status_t lstm_fwd(const lstm_desc_t* d, const void* x, const void* h0, const float* c0, const void* W,

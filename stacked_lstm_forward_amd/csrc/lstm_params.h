@@ -63,6 +63,12 @@ struct RecLayer {
   int mt_per_wg;          // M-tiles per workgroup
   int staged;             // 1: weight rows kept in LDS for the whole sequence
   int vec_ok;             // 16-byte loads allowed on W/R/U/X/h0 rows
+  // training forward (LSTM only; null otherwise): per step, the activated
+  // gates [T][B][4H] fp32 (blocks i, f, g, o), c_t [T][B][H] fp32 and h_t
+  // [T][B][H] (dtype) of this layer, for the backward pass
+  float* save_gates;
+  float* save_c;
+  void* save_h;
 };
 
 struct RecParams {

@@ -148,6 +148,20 @@ __device__ __forceinline__ void cell_update(int cell, const f32x4 p, float& st, 
   }
 }
 
+// Training forward: the LSTM step's activated gates (the same functions of
+// the same pre-activations as in cell_update, so the same values) and the new
+// cell state of (batch column b, unit j), saved for the backward pass.
+__device__ __forceinline__ void save_lstm_step(float* gates, float* cs, const f32x4 p, float c, int t, int B, int H,
+                                               int b, int j) {
+  const long r = (long)t * B + b;
+  float* g = gates + r * 4 * H + j;
+  g[0] = sigmoid_f(p[0]);
+  g[H] = sigmoid_f(p[1]);
+  g[2L * H] = tanh_f(p[2]);
+  g[3L * H] = sigmoid_f(p[3]);
+  cs[r * H + j] = c;
+}
+
 // ----------------------------------------------------------------------------
 // Persistent recurrence (optionally several layers as a wavefront)
 // ----------------------------------------------------------------------------
@@ -647,9 +661,11 @@ __global__ void __launch_bounds__(64 * NWV) lstm_rec_kernel(const RecParams P) {
           if (cpy) cpy[o + k] = hv;
           if (yout) yout[o + k] = hv;
           if (last && LY(hT)) reinterpret_cast<T*>(LY(hT))[o + k] = hv;
+          if (LY(save_h)) reinterpret_cast<T*>(LY(save_h))[(long)t * B * H + o + k] = hv;
         };
         cell_update(cell, p, creg[i][j], H - unit[i], emit);
         if (cell == kCellLstm && last && LY(cT)) LY(cT)[o] = creg[i][j];
+        if (cell == kCellLstm && LY(save_gates)) save_lstm_step(LY(save_gates), LY(save_c), p, creg[i][j], t, B, H, bcol[j], unit[i]);
       }
     stamp(t, 4);
 

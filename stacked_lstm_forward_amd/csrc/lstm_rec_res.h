@@ -239,8 +239,11 @@ lstm_rec_res_kernel(const RecParams P) {
           store_coherent<BF16>(fout + fo + u, hv);
           rout[o + u] = hv;
           if (last && Lr.hT) reinterpret_cast<T*>(Lr.hT)[o + u] = hv;
+          if (Lr.save_h) reinterpret_cast<T*>(Lr.save_h)[(long)t * B * H + o + u] = hv;
         });
         if (cell == kCellLstm && last && Lr.cT) Lr.cT[o] = st[j];
+        if (cell == kCellLstm && Lr.save_gates)
+          save_lstm_step(Lr.save_gates, Lr.save_c, p, st[j], t, B, H, 16 * j + (lane & 15), funit);
       }
       // the next column tile reuses the partial-sum area
       if (j + 1 < NW) __syncthreads();

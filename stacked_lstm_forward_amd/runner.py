@@ -8,8 +8,8 @@ from typing import Optional
 
 import numpy as np
 
-from . import (LSTM_BF16, LSTM_F32, LstmDesc, LstmOpts, check, lstm_fwd, lstm_fwd_ex,
-               lstm_fwd_workspace_size, make_desc)
+from . import (LSTM_BF16, LSTM_F32, LstmDesc, LstmOpts, check, lstm_bwd, lstm_bwd_workspace_size, lstm_fwd,
+               lstm_fwd_ex, lstm_fwd_train, lstm_fwd_workspace_size, lstm_train_reserve_size, make_desc)
 
 
 def _torch():
@@ -99,4 +99,73 @@ def forward(inp, device="cuda:0", opts: Optional[LstmOpts] = None):
     return prob.outputs_f32()
 
 
-__all__ = ["DeviceProblem", "prepare", "forward", "workspace", "to_device_array", "LSTM_F32", "LSTM_BF16"]
+
+
+@dataclass
+class TrainProblem:
+    """A DeviceProblem plus what one training forward and one backward call need:
+    the reserve buffer, the backward workspace, the upstream gradients and the
+    gradient outputs (all fp32)."""
+    fwd: DeviceProblem
+    reserve: object
+    bws: object
+    dy: object
+    dhT: object
+    dcT: object
+    dx: object
+    dh0: object
+    dc0: object
+    dW: object
+    dR: object
+    db: object
+
+    def forward(self, stream=None) -> None:
+        p = self.fwd
+        check(lstm_fwd_train(p.desc, p.x, p.h0, p.c0, p.W, p.R, p.b, p.y, p.hT, p.cT, self.reserve, p.ws, stream),
+              "lstm_fwd_train")
+
+    def backward(self, stream=None) -> None:
+        p = self.fwd
+        check(lstm_bwd(p.desc, p.x, p.h0, p.c0, p.W, p.R, self.reserve, self.dy, self.dhT, self.dcT, self.dx,
+                       self.dh0, self.dc0, self.dW, self.dR, self.db, self.bws, stream), "lstm_bwd")
+
+    def grads_f64(self):
+        """Gradients as float64 numpy arrays, split per layer like the oracle's (synchronises)."""
+        c = self.fwd.desc
+        L, I, H = c.L, c.I, c.H
+        dW = self.dW.double().cpu().numpy()
+        offs = [0, 4 * H * I] + [4 * H * I + k * 4 * H * H for k in range(1, L)]
+        return {"dx": self.dx.double().cpu().numpy(), "dh0": self.dh0.double().cpu().numpy(),
+                "dc0": self.dc0.double().cpu().numpy(),
+                "dW": [dW[offs[l]:offs[l] + 4 * H * (I if l == 0 else H)].reshape(4 * H, -1) for l in range(L)],
+                "dR": list(self.dR.double().cpu().numpy().reshape(L, 4 * H, H)),
+                "db": list(self.db.double().cpu().numpy().reshape(L, 4 * H))}
+
+
+def aligned_buffer(nbytes: int, device):
+    torch = _torch()
+    raw = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+    off = (-raw.data_ptr()) % 256
+    return raw[off:off + nbytes]
+
+
+def prepare_train(inp, dy, dhT=None, dcT=None, device="cuda:0") -> TrainProblem:
+    """Device buffers for lstm_fwd_train + lstm_bwd on an LSTM ``lstm_inputs.Inputs``;
+    dy [T, B, H] and dhT / dcT [L, B, H] (or None) are host arrays of upstream gradients."""
+    torch = _torch()
+    p = prepare(inp, device)
+    c = inp.cfg
+    rs = lstm_train_reserve_size(p.desc)
+    wb = lstm_bwd_workspace_size(p.desc)
+    if rs == 0 or wb == 0:
+        raise ValueError("training passes need an LSTM problem the library supports")
+    f32 = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)  # noqa: E731
+    nW = 4 * c.H * c.I + (c.L - 1) * 4 * c.H * c.H
+    z = lambda *shape: torch.zeros(shape, dtype=torch.float32, device=device)  # noqa: E731
+    return TrainProblem(p, aligned_buffer(rs, device), aligned_buffer(wb, device), f32(dy), f32(dhT), f32(dcT),
+                        z(c.T, c.B, c.I), z(c.L, c.B, c.H), z(c.L, c.B, c.H), z(nW), z(c.L, 4 * c.H, c.H),
+                        z(c.L, 4 * c.H))
+
+
+__all__ = ["DeviceProblem", "TrainProblem", "prepare", "prepare_train", "forward", "workspace", "aligned_buffer",
+           "to_device_array", "LSTM_F32", "LSTM_BF16"]

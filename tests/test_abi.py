@@ -49,9 +49,38 @@ def test_peaks_library_loads_and_exports_all_declared_symbols():
     assert lib.lstm_peak_step_ws_bytes(512, 1, 16, 10) == 0      # more than 256 active workgroups
 
 
+def test_training_entry_points_exported():
+    lib = sl.load_library()
+    names = declared_functions("lstm_bwd.h")
+    assert set(names) == set(sl.EXPORTED_TRAIN), names
+    for n in names:
+        assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
+
+
 def test_every_header_is_covered():
     assert set(declared_functions()) == set(declared_functions("lstm_fwd.h")) | set(
-        declared_functions("lstm_peaks.h"))
+        declared_functions("lstm_peaks.h")) | set(declared_functions("lstm_bwd.h"))
+
+
+def test_training_sizes_and_host_checks():
+    d = sl.make_desc(2, 24, 16, 3, 5, "f32")
+    tbh = 2 * 5 * 3 * 16
+    assert sl.lstm_train_reserve_size(d) == (tbh * (16 + 4 + 4) + 255) // 256 * 256
+    assert sl.lstm_bwd_workspace_size(d) > 0
+    g = sl.make_desc(2, 24, 16, 3, 5, "f32", "gru")
+    assert sl.lstm_train_reserve_size(g) == 0 and sl.lstm_bwd_workspace_size(g) == 0
+    # refusals happen on the host, before any launch (no GPU needed); the 15
+    # tensor arguments x .. db, then the workspace, then the stream
+    args = [FAKE] * 15
+    assert sl.lstm_bwd(g, *args, FAKE, 0) == sl.LSTM_ERR_UNSUPPORTED
+    assert sl.lstm_bwd(None, *args, FAKE, 0) == sl.LSTM_ERR_INVALID_ARG
+    assert sl.lstm_bwd(d, *args, FAKE + 16, 0) == sl.LSTM_ERR_WORKSPACE
+    assert sl.lstm_bwd(d, *args, None, 0) == sl.LSTM_ERR_WORKSPACE
+    missing = list(args)
+    missing[5] = None  # reserve
+    assert sl.lstm_bwd(d, *missing, FAKE, 0) == sl.LSTM_ERR_INVALID_ARG
+    assert sl.lstm_fwd_train(d, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, None, None, None, FAKE, 0) == \
+        sl.LSTM_ERR_INVALID_ARG
 
 
 def test_status_strings():

@@ -1,0 +1,125 @@
+"""GPU parity of the training passes: lstm_fwd_train (the forward that keeps
+gates, cell and hidden states) and lstm_bwd (backpropagation through time)
+against the fp64 backward oracle, through the C ABI.
+
+Every gradient tensor (dx, dh0, dc0, and per layer dW, dR, db) must be within
+the workload dtype's max-norm relative tolerance of the oracle: 1e-4 for fp32,
+2e-2 for bf16 (whose products take bf16 operands, like its forward).  The
+training forward's outputs must equal lstm_fwd's bit for bit.  Every case
+prints its name before touching the GPU.
+"""
+import numpy as np
+import pytest
+
+import lstm_inputs as li
+import oracle.lstm_oracle_bwd as orcb
+from tests.parity_log import record
+from tests.pins import rel_err
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    import stacked_lstm_forward_amd as sl
+    sl.load_library()
+    return "cuda:0"
+
+
+def say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+def upstream(cfg, seed, with_states=True):
+    rng = np.random.default_rng(seed)
+    dy = rng.standard_normal((cfg.T, cfg.B, cfg.H))
+    if not with_states:
+        return dy, None, None
+    return dy, rng.standard_normal((cfg.L, cfg.B, cfg.H)), rng.standard_normal((cfg.L, cfg.B, cfg.H))
+
+
+def run_and_check(inp, dy, dhT, dcT, dev, what):
+    import torch
+    import stacked_lstm_forward_amd as sl
+    from stacked_lstm_forward_amd import runner
+    tp = runner.prepare_train(inp, dy, dhT, dcT, dev)
+    tp.forward()
+    assert sl.lstm_fwd_last_error(tp.fwd.ws) == sl.LSTM_OK
+    ref_fwd = runner.prepare(inp, dev)
+    ref_fwd.run()
+    for a, b in zip((tp.fwd.y, tp.fwd.hT, tp.fwd.cT), (ref_fwd.y, ref_fwd.hT, ref_fwd.cT)):
+        va = a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32)
+        vb = b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32)
+        assert torch.equal(va, vb), "training forward must equal lstm_fwd"
+    tp.backward()
+    got = tp.grads_f64()
+    # the oracle sees the upstream gradients the GPU saw (rounded to fp32)
+    f32 = lambda a: None if a is None else np.asarray(a, dtype=np.float32).astype(np.float64)  # noqa: E731
+    ref = orcb.lstm_backward_inputs(inp, f32(dy), f32(dhT), f32(dcT))
+    tol = TOL[inp.cfg.dtype]
+    errs = {k: rel_err(got[k], ref[k]) for k in ("dx", "dh0", "dc0")}
+    for k in ("dW", "dR", "db"):
+        errs[k] = max(rel_err(g, r) for g, r in zip(got[k], ref[k]))
+    say(f"{what}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    record(what, tol, errs)
+    for k, v in errs.items():
+        assert np.isfinite(v) and v <= tol, (what, k, v)
+
+
+SHAPES = [
+    # L, I, H, B, T
+    (1, 1, 1, 1, 1),
+    (1, 3, 5, 2, 3),
+    (2, 24, 20, 3, 5),
+    (3, 33, 17, 17, 4),
+    (2, 64, 64, 16, 6),
+    (2, 130, 66, 20, 7),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", SHAPES)
+def test_gpu_backward_small(dev, shape, dtype):
+    L, I, H, B, T = shape
+    cfg = li.custom_config(L, I, H, B, T, dtype, cfg_id=800 + L + I + H)
+    inp = li.make_inputs(cfg, random_state=True)
+    dy, dhT, dcT = upstream(cfg, 801 + H)
+    say(f"backward {shape} {dtype}")
+    run_and_check(inp, dy, dhT, dcT, dev, f"bwd {shape} {dtype}")
+
+
+@pytest.mark.parametrize("name,T", [("c1", None), ("c2", 12), ("c3", 12), ("c5", 64)])
+def test_gpu_backward_workload_shapes(dev, name, T):
+    """The workloads' shapes (T cut where noted), zero initial states, dy only."""
+    cfg = li.CONFIGS[name]
+    if T is not None:
+        cfg = li.Config(f"{cfg.name}-T{T}", cfg.cfg_id, cfg.L, cfg.I, cfg.H, cfg.B, T, cfg.dtype)
+    inp = li.make_inputs(cfg)
+    dy, _, _ = upstream(cfg, 810, with_states=False)
+    say(f"backward workload {cfg.name}")
+    run_and_check(inp, dy, None, None, dev, f"bwd {cfg.name}")
+
+
+def test_gpu_backward_large_hidden(dev):
+    """H = 4096 (the forward keeps R in registers and LDS): 2 layers, T = 4, B = 32."""
+    cfg = li.custom_config(2, 4096, 4096, 32, 4, "bf16", cfg_id=820)
+    inp = li.make_inputs(cfg)
+    dy, dhT, dcT = upstream(cfg, 821)
+    say("backward H=4096 L=2 T=4 B=32 bf16")
+    run_and_check(inp, dy, dhT, dcT, dev, "bwd H4096")
+
+
+def test_gpu_backward_wavefront_and_layerwise_forward_agree(dev):
+    """The training forward saves the same activations in both schedules."""
+    import stacked_lstm_forward_amd as sl
+    cfg = li.custom_config(3, 64, 128, 16, 6, "bf16", cfg_id=830)
+    d = sl.make_desc(cfg.L, cfg.I, cfg.H, cfg.B, cfg.T, cfg.dtype)
+    assert sl.lstm_fwd_plan(d).as_dict()["regime"] == "wavefront"
+    inp = li.make_inputs(cfg, random_state=True)
+    dy, dhT, dcT = upstream(cfg, 831)
+    say("backward after a wavefront forward")
+    run_and_check(inp, dy, dhT, dcT, dev, "bwd wavefront L3 H128")
