@@ -16,8 +16,12 @@
 // so it reads a quarter of h_{t-1} and the four waves together read it once.
 // The launcher guarantees H = 4 * NCI chunks exactly (aligned rows), so every
 // wave has NCI chunks and all its offsets are compile-time constants.
-// Block b of a wave is (chunk index ci = b / MW, M-tile b % MW); blocks
-// b < NRB live in registers, the others in LDS.  The NW column tiles are
+// Block b of a wave is (chunk index ci = b / MW, M-tile b % MW).  The last
+// LPC = (NB - NRB) / NCI M-tiles of every chunk live in LDS, the others in
+// registers: a chunk's LDS blocks are read while the previous chunk's products
+// run, so LDS latency stays hidden (with all LDS blocks in the last chunks,
+// each read only one block ahead, those chunks stalled on LDS and a pass took
+// about twice its matrix-core time).  The NW column tiles are
 // done one after the other (MW accumulators and one h fragment per chunk in
 // registers); after each, the four K-groups' partial sums meet in LDS and
 // K-group i finishes M-tile i of that column tile.
@@ -41,15 +45,26 @@
 namespace lstm {
 
 constexpr int kResWaves = 4;  // waves per workgroup = K-groups
+// Register blocks defined as accumulation-register values.  Weights that only
+// outgrow the architectural VGPRs are parked in the accumulation registers as
+// spill slots and copied back before every MFMA (about four register moves per
+// product); a value that is an accumulation register from its definition is
+// read by the MFMA in place.  30 blocks (240 registers) leave room for the
+// accumulators.
+constexpr int kResAgprBlocks = 30;
 
 template <bool BF16, int MW, int NW, int NCI, int NRB>
 __global__ void __launch_bounds__(64 * kResWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
 lstm_rec_res_kernel(const RecParams P) {
+  static_assert(BF16, "the resident kernel multiplies bf16");
   typedef typename Dt<BF16>::T T;
   constexpr int KC = Dt<BF16>::KC;
   constexpr int KS = kResWaves;
   constexpr int NB = MW * NCI;     // fragment blocks per wave
   constexpr int NLB = NB - NRB;    // ... of which in LDS
+  constexpr int LPC = NLB / NCI;   // LDS M-tiles per chunk
+  constexpr int RPC = MW - LPC;    // register M-tiles per chunk
+  static_assert(NLB % NCI == 0, "LDS blocks spread evenly over the chunks");
   constexpr int PD = 4;  // chunks of h loads in flight (H = 4096, B = 32: 2 -> 0.51 ms per layer, 4 -> 0.42, 6 no better)
   static_assert(NRB >= 0 && NRB <= NB, "register blocks");
   static_assert(MW <= KS, "one finishing K-group per M-tile");
@@ -96,18 +111,28 @@ lstm_rec_res_kernel(const RecParams P) {
     }
   }
 
-  // ---- this wave's weight blocks: registers for b < NRB, LDS for the rest
+  // ---- this wave's weight blocks: M-tile i < RPC of chunk slot ci is
+  // register block ci * RPC + i, M-tile i >= RPC is LDS block ci * LPC + i - RPC
   const T* Rp = reinterpret_cast<const T*>(Lr.R) + kg * KC;
-  Frag wreg[NRB > 0 ? NRB : 1];
+  struct WB {
+    bf16x8 h[2];
+  };
+  WB wreg[NRB > 0 ? NRB : 1];
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     const int ci = b / MW, i = b % MW;
     Frag f = load_frag_vec<BF16>(Rp + arow[i] * H + ci * KS * KC, q);
     frag_mask(f, mr_[i]);
-    if (b < NRB)
-      wreg[b < NRB ? b : 0] = f;
-    else
-      lds_put(As + (b - NRB) * 128, lane, f);
+    if (i < RPC) {
+      const int r = ci * RPC + (i < RPC ? i : 0);
+      WB w{{__builtin_bit_cast(bf16x8, f.v[0]), __builtin_bit_cast(bf16x8, f.v[1])}};
+      if (r < kResAgprBlocks) {
+        asm volatile("" : "+a"(w.h[0]));
+        asm volatile("" : "+a"(w.h[1]));
+      }
+      wreg[r] = w;
+    } else
+      lds_put(As + (ci * LPC + i - RPC) * 128, lane, f);
   }
 
   // ---- per column tile j: this wave finishes M-tile kg (if it exists)
@@ -182,38 +207,64 @@ lstm_rec_res_kernel(const RecParams P) {
     // (the host gives every resident layer either y or a row-major X)
     const bool last = (t == T_ - 1);
 
+    // The h loads of the step form one stream over all column tiles, PD
+    // chunks ahead: the next tile's first chunks are in flight while this
+    // tile's sums are combined and its gates computed.  Load g is chunk slot
+    // g % NCI of column tile g / NCI.
+    Frag rb[PD];
+    // a chunk's LDS blocks are read one chunk ahead into the other of two
+    // buffers (the next tile's first chunk during this tile's last one)
+    Frag al[2][LPC > 0 ? LPC : 1];
+    auto issue = [&](Frag& dst, int g) {
+      const int jj = g / NCI, ci = g % NCI;
+      const T* pc = hsrc + ci * cstride;
+      dst.v[0] = *reinterpret_cast<const uint4*>(pc + (fr ? hfr[jj][0] : hrm[jj][0]));
+      dst.v[1] = *reinterpret_cast<const uint4*>(pc + (fr ? hfr[jj][1] : hrm[jj][1]));
+    };
+    if (hsrc) {
+#pragma unroll
+      for (int g = 0; g < PD && g < NW * NCI; ++g) issue(rb[g], g);
+#pragma unroll
+      for (int e = 0; e < LPC; ++e) al[0][e] = lds_get(As + e * 128, lane);
+    }
+
 #pragma unroll
     for (int j = 0; j < NW; ++j) {
       f32x4 acc[MW];
 #pragma unroll
       for (int i = 0; i < MW; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (hsrc) {
-        Frag rb[PD];
-        const uint32_t o0 = fr ? hfr[j][0] : hrm[j][0], o1 = fr ? hfr[j][1] : hrm[j][1];
-        auto issue = [&](Frag& dst, int ci) {
-          const T* pc = hsrc + ci * cstride;
-          dst.v[0] = *reinterpret_cast<const uint4*>(pc + o0);
-          dst.v[1] = *reinterpret_cast<const uint4*>(pc + o1);
-        };
-        // LDS blocks are read one block ahead into the other of two buffers
-        Frag al[2];
-#pragma unroll
-        for (int s = 0; s < PD; ++s) issue(rb[s], s);
-        if (NLB > 0) al[0] = lds_get(As, lane);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ci = 0; ci < NCI; ++ci) {
-          const int s = ci % PD;
+          const int g = j * NCI + ci, s = g % PD;
+          if (ci + 1 < NCI || j + 1 < NW) {
+            const int cn = (ci + 1) % NCI;
+#pragma unroll
+            for (int e = 0; e < LPC; ++e) al[cn & 1][e] = lds_get(As + (cn * LPC + e) * 128, lane);
+          }
 #pragma unroll
           for (int i = 0; i < MW; ++i) {
-            const int b = ci * MW + i;
-            if (b >= NRB && b + 1 < NB) al[(b + 1 - NRB) & 1] = lds_get(As + (b + 1 - NRB) * 128, lane);
-            const Frag& a = b < NRB ? wreg[b < NRB ? b : 0] : al[(b - NRB) & 1];
             // no branch: a missing M-tile has zero weights and a missing
             // column tile a clamped h row; their sums are never finished
-            mfma_frag<BF16>(acc[i], a, rb[s]);
+            const bf16x8 x0 = __builtin_bit_cast(bf16x8, rb[s].v[0]), x1 = __builtin_bit_cast(bf16x8, rb[s].v[1]);
+            bf16x8 a0, a1;
+            if (i < RPC) {
+              a0 = wreg[ci * RPC + (i < RPC ? i : 0)].h[0];
+              a1 = wreg[ci * RPC + (i < RPC ? i : 0)].h[1];
+            } else {
+              a0 = __builtin_bit_cast(bf16x8, al[ci & 1][i < RPC ? 0 : i - RPC].v[0]);
+              a1 = __builtin_bit_cast(bf16x8, al[ci & 1][i < RPC ? 0 : i - RPC].v[1]);
+            }
+            // the two products of one accumulator back to back: its second
+            // product takes the first's result without a register read
+            // (a pair issues every 16.9 cycles, alternating accumulators
+            // every 22.9, which the scheduler would otherwise choose)
+            acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, x0, acc[i], 0, 0, 0);
+            acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, x1, acc[i], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
           }
-          if (ci + PD < NCI) issue(rb[s], ci + PD);
+          if (g + PD < NW * NCI) issue(rb[s], g + PD);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
