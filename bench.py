@@ -201,6 +201,116 @@ def cpu_baseline(inp, cfg, min_seconds: float) -> dict:
             "ms_per_forward_extrapolated": round(el / reps * cfg.T / ts * 1e3, 1)}
 
 
+def train_bench(args, cfg, workload, inp) -> int:
+    """One training step = lstm_fwd_train (the forward that keeps gates, cell and
+    hidden states) + lstm_bwd (backpropagation through time, weight gradients as
+    single products over all T*B columns), timed with events on the stream the
+    library enqueues on.  FLOPs: the forward's, plus twice that for the backward
+    (the recurrent chain dP R, and dW, dR and the input gradient dP W)."""
+    import numpy as np
+    import torch
+    from stacked_lstm_forward_amd import runner
+    if cfg.cell != "lstm":
+        print("--train covers the LSTM cell", file=sys.stderr)
+        return 2
+    rng = np.random.default_rng(1234)
+    dy = rng.standard_normal((cfg.T, cfg.B, cfg.H)).astype(np.float32)
+    dhT = rng.standard_normal((cfg.L, cfg.B, cfg.H)).astype(np.float32)
+    dcT = rng.standard_normal((cfg.L, cfg.B, cfg.H)).astype(np.float32)
+    tp = runner.prepare_train(inp, dy, dhT, dcT, "cuda:0")
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        tp.forward(stream)
+        tp.backward(stream)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for k in range(args.steps):
+        ev[k][0].record(stream)
+        tp.forward(stream)
+        ev[k][1].record(stream)
+        tp.backward(stream)
+        ev[k][2].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    st = sl_last_error(tp.fwd)
+    if st:
+        print(f"timed training run failed: {st}", file=sys.stderr)
+        return 1
+    ms_step = t0.elapsed_time(t1) / args.steps
+    fwd = median([e[0].elapsed_time(e[1]) for e in ev])
+    bwd = median([e[1].elapsed_time(e[2]) for e in ev])
+    g = tp.grads_f64()
+    if not all(np.all(np.isfinite(v)) for v in (g["dx"], g["dh0"], g["dc0"], *g["dW"], *g["dR"], *g["db"])):
+        print("non-finite gradients", file=sys.stderr)
+        return 1
+    dt = "f32" if cfg.dtype == "f32" else "bf16"
+    peak = SPEC_PEAKS["mfma"][dt]
+    flops = 3 * cfg.flops
+    value = flops / (ms_step * 1e-3) / 1e12
+    bwd_tf = 2 * cfg.flops / (bwd * 1e-3) / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the fp64 backward oracle on the host (cpu_baseline)")
+        cpu = cpu_baseline_train(inp, cfg, dy, dhT, dcT, args.cpu_seconds)
+    out = {
+        "metric": "stacked-LSTM training step (forward keeping state + backward) TFLOPS",
+        "value": round(value, 4), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": dt, "data": "synthetic (seeded; dy, dhT, dcT ~ N(0,1))",
+        "config": {"workload": workload, "cell": cfg.cell, "L": cfg.L, "I": cfg.I, "H": cfg.H, "B": cfg.B,
+                   "T": cfg.T, "gflop_per_step": round(flops / 1e9, 3)},
+        "roofline": {"bound": "mfma", "achieved": round(bwd_tf, 3), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(bwd_tf / peak, 4), "traffic": None, "kernel": "lstm_bwd (all its kernels)",
+                     "ms_per_launch": round(bwd, 5), "algorithmic_per_launch": 2 * cfg.flops},
+        "phases": {"forward_train": {"ms_median": round(fwd, 5),
+                                     "tflops": round(cfg.flops / (fwd * 1e-3) / 1e12, 2)},
+                   "backward": {"ms_median": round(bwd, 5), "tflops": round(bwd_tf, 2),
+                                "frac_of_mfma_peak": round(bwd_tf / peak, 4)}},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def sl_last_error(prob) -> str:
+    import stacked_lstm_forward_amd as sl
+    st = sl.lstm_fwd_last_error(prob.ws, None)
+    return "" if st == sl.LSTM_OK else sl.lstm_status_string(st)
+
+
+def cpu_baseline_train(inp, cfg, dy, dhT, dcT, min_seconds: float) -> dict:
+    """The fp64 backward oracle (its forward included) on a bounded sample:
+    every layer and sequence, the first T_s steps."""
+    import dataclasses
+    import lstm_inputs as li
+    from oracle.lstm_oracle_bwd import lstm_backward_inputs
+    threads, vendor = blas_info()
+
+    def sub(ts):
+        c = li.Config(f"{cfg.name}-T{ts}", cfg.cfg_id, cfg.L, cfg.I, cfg.H, cfg.B, ts, cfg.dtype, cfg.cell)
+        return dataclasses.replace(inp, cfg=c, x=inp.x[:ts]), c
+
+    probe, _ = sub(1)
+    t0 = time.perf_counter()
+    lstm_backward_inputs(probe, dy[:1], dhT, dcT)
+    per_step = max(time.perf_counter() - t0, 1e-6)
+    ts = max(1, min(cfg.T, int(min_seconds / per_step)))
+    sample, scfg = sub(ts)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        lstm_backward_inputs(sample, dy[:ts], dhT, dcT)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds or reps >= 50:
+            break
+    return {"value": 3 * scfg.flops * reps / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"all {cfg.L} layers and {cfg.B} sequences, the first {ts} of {cfg.T} steps, forward and "
+                      f"backward ({3 * scfg.flops / 1e9:.1f} GFLOP) run {reps}x by the fp64 NumPy oracle in {el:.1f} s",
+            "blas": vendor, "host_cpus": len(os.sched_getaffinity(0)), "precision": "fp64"}
+
+
 # The pages' own figures, on other hardware: context, never a target.
 PAGES_CONTEXT = {
     "naive_rnn_tflops_m40": 0.4, "m40_peak_tflops": 5.8, "after_gate_grouping_tflops_m40": 0.8,
@@ -237,6 +347,8 @@ def main() -> int:
                     help="only run a device-to-device copy of this many MiB (calibrates HBM traffic counters)")
     ap.add_argument("--plain-launch", action="store_true",
                     help="ordinary (not cooperative) launch of the persistent kernel, for profilers")
+    ap.add_argument("--train", action="store_true",
+                    help="time a training step (lstm_fwd_train + lstm_bwd) instead of the forward")
     ap.add_argument("--source-digest", action="store_true",
                     help="print the digest of the library sources that counter summaries are keyed on")
     args = ap.parse_args()
@@ -275,6 +387,8 @@ def main() -> int:
         workload = workload.replace("LSTM", args.cell.upper().replace("_", "-"))
     log(f"workload {cfg.name}: {workload}; generating inputs")
     inp = li.make_inputs(cfg)
+    if args.train:
+        return train_bench(args, cfg, workload, inp)
     prob = runner.prepare(inp, "cuda:0")
     plan = sl.lstm_fwd_plan(prob.desc, args.regime).as_dict()
     log(f"plan {plan}")

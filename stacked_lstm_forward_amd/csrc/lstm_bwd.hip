@@ -4,10 +4,15 @@
 // Per layer, from the top:
 //   1. the recurrent chain, strictly serial in t: for t = T-1 .. 0 an
 //      elementwise kernel turns dh = dY[t] + dh_rec and dc_rec into the gate
-//      derivatives dp_t (fp32, and a copy in the workload's dtype) and the next
+//      derivatives dp_t (fp32, and copies in the workload's dtype) and the next
 //      dc_rec; then dh_rec = dp_t R_l, an MFMA product over K = 4H split across
 //      workgroups so it fills the GPU (the K-split partial sums are added by the
-//      next step's elementwise kernel, in a fixed order);
+//      next step's elementwise kernel, in a fixed order).  That product reads
+//      all of R_l every step, so it is bound by memory: R_l^T is rewritten once
+//      per layer, and dp_t every step, in the order the MFMA fragments are
+//      loaded (every wave-wide load reads 1 KiB in one piece), each workgroup
+//      keeps its slice of dp_t in LDS and streams its slice of R_l^T with eight
+//      chunks of loads in flight per wave;
 //   2. once every step's dp is known, the weight and input gradients as single
 //      MFMA products over all T*B columns -- dW_l = dP^T U, dR_l = dP^T H_prev,
 //      dU = dP W_l ("Optimizing Performance of Recurrent Neural Networks on
@@ -25,6 +30,12 @@
 #include "lstm_params.h"
 
 namespace lstm {
+
+// lstm_kernels.hip
+hipError_t prepare_fn(const void* fn, int lds_bytes, int block, int* blocks_per_cu);
+hipError_t launch_gemm_plain(bool bf16, const void* A, const void* B, float* C, long long ldc, int M, int N, int K,
+                             int num_cus, hipStream_t s);
+
 namespace {
 
 constexpr int kBwdThreads = 256;
@@ -123,6 +134,18 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_gemm_nt(const void* A, long l
     }
 }
 
+// Element offset of (row r, column k) of a matrix stored in MFMA load order
+// with nch chunks of KC columns per row tile: block (r / 16, chunk) of 2 KiB,
+// half h at +1 KiB, lane q * 16 + r % 16 at +16 bytes per lane, holding the
+// lane's fragment columns frag_col(q, h) .. + KC / 8 - 1 of that chunk.
+template <bool BF16>
+__device__ __forceinline__ long frag_off(int r, int k, int nch) {
+  constexpr int KC = Dt<BF16>::KC, EPH = KC / 8;
+  const int c = k / KC, kc = k % KC;
+  const int h = kc / (KC / 2), q = (kc % (KC / 2)) / EPH, e = kc % EPH;
+  return (((long)(r >> 4) * nch + c) * 2 + h) * (64 * EPH) + (q * 16 + (r & 15)) * EPH + e;
+}
+
 struct StepArgs {
   const float* dY;      // [B][H] gradient reaching h_t from above (dy, or the upper layer's dU)
   const float* dhp;     // [S][B][H] K-split partials of dh_rec (null at the last step)
@@ -136,8 +159,9 @@ struct StepArgs {
   float* dcrec;         // [B][H] in: dc_rec of step t+1; out: dc f
   float* dP;            // [B][4H] fp32 gate derivatives of step t
   void* dPh;            // [B][4H] the same in the workload's dtype
+  void* dPf;            // the same in MFMA load order (nch chunks per 16 rows)
   float* dc0;           // [B][H] or null: written at step 0
-  int B, H, last;
+  int B, H, last, nch;
 };
 
 // One step of the recurrent chain for every (sequence, unit).
@@ -167,10 +191,13 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_step(const StepArgs a) {
                         dh * tc * og * (1.f - og)};
     float* dp = a.dP + (long)bb * 4 * a.H + j;
     T* dph = reinterpret_cast<T*>(a.dPh) + (long)bb * 4 * a.H + j;
+    T* dpf = reinterpret_cast<T*>(a.dPf);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
+      const T v = from_float<BF16>(d[k]);
       dp[(long)k * a.H] = d[k];
-      dph[(long)k * a.H] = from_float<BF16>(d[k]);
+      dph[(long)k * a.H] = v;
+      dpf[frag_off<BF16>(bb, k * a.H + j, a.nch)] = v;
     }
     const float dcn = dc * fg;
     a.dcrec[idx] = dcn;
@@ -187,40 +214,176 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_colsum(const float* dP, int r
   db[k] = s;
 }
 
+// R_l^T in load order: element (n, k) = R_l[k][n] for n < H, k < 4H, zero in
+// the padding.  Workgroup (x, c): columns n of R 64 x .. 64 x + 63 and rows k
+// of chunk c, through an LDS tile.
+template <bool BF16>
+__global__ void __launch_bounds__(kBwdThreads) bwd_block_rt(const void* R, int H, int nch, uint4* out) {
+  typedef typename Dt<BF16>::T T;
+  constexpr int KC = Dt<BF16>::KC, EPH = KC / 8;
+  __shared__ T tile[KC][64 + 16 / sizeof(T)];
+  const int n0 = blockIdx.x * 64, c = blockIdx.y, G = 4 * H;
+  const T* Rp = static_cast<const T*>(R);
+  for (int i = threadIdx.x; i < KC * 64; i += kBwdThreads) {
+    const int kr = i / 64, nc = i % 64, k = c * KC + kr, n = n0 + nc;
+    tile[kr][nc] = (k < G && n < H) ? Rp[(long)k * H + n] : T(0);
+  }
+  __syncthreads();
+  // 4 row tiles x 2 halves x 64 lanes of 16 bytes
+  for (int i = threadIdx.x; i < 4 * 2 * 64; i += kBwdThreads) {
+    const int t16 = i / 128, h = (i / 64) % 2, lane = i % 64, q = lane >> 4;
+    const int nl = 16 * t16 + (lane & 15), n = n0 + nl;
+    if (n >= ((H + 15) & ~15)) continue;
+    T v[EPH];
+#pragma unroll
+    for (int e = 0; e < EPH; ++e) v[e] = tile[frag_col<BF16>(q, h) + e][nl];
+    out[frag_off<BF16>(n, c * KC + frag_col<BF16>(q, h), nch) / EPH] = *reinterpret_cast<const uint4*>(v);
+  }
+}
+
+// Zeroes n 16-byte words (a fill kernel, so the call stays capturable).
+__global__ void __launch_bounds__(kBwdThreads) bwd_zero(uint4* p, long n) {
+  for (long i = (long)blockIdx.x * kBwdThreads + threadIdx.x; i < n; i += (long)gridDim.x * kBwdThreads)
+    p[i] = uint4{0u, 0u, 0u, 0u};
+}
+
+// dst[i] = sum over z < S of part[z * pstride + i], in order (dh0 from the
+// K-split partial sums of step 0).
+__global__ void __launch_bounds__(kBwdThreads) bwd_sum_parts(const float* part, long pstride, int S, long n,
+                                                             float* dst) {
+  for (long i = (long)blockIdx.x * kBwdThreads + threadIdx.x; i < n; i += (long)gridDim.x * kBwdThreads) {
+    float v = 0.f;
+    for (int z = 0; z < S; ++z) v += part[z * pstride + i];
+    dst[i] = v;
+  }
+}
+
+constexpr int kRecWaves = 8;   // waves per workgroup of the per-step product: one column tile each
+constexpr int kRecDepth = 8;   // chunks of R^T loads in flight per wave
+constexpr int kRecLdsBlocks = 64;  // dp blocks (2 KiB) a workgroup stages: 128 KiB
+
+// The per-step product dh_rec partials: part[z][b][n] = sum over the chunks c
+// of split z of dp_t[b][c-th chunk] . R^T[n][c-th chunk], for b < B, n < H.
+// Workgroup (x, z, y): column tiles 8 x + w (wave w), chunks
+// [z cps, min(nch, (z + 1) cps)), batch tiles NBT y .. NBT y + NBT - 1.  Its
+// dp blocks go to LDS first; each wave then streams its R^T blocks (each
+// read once per step by one wave) kRecDepth chunks ahead.
+template <bool BF16, int NBT>
+__global__ void __launch_bounds__(64 * kRecWaves) bwd_rec_product(const uint4* RTf, const uint4* DPf, float* part,
+                                                                   long pstride, int B, int H, int nch, int cps,
+                                                                   int nbt) {
+  extern __shared__ __align__(16) uint4 sdp[];  // [NBT][cps] blocks of 128 x 16 bytes
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n16 = blockIdx.x * kRecWaves + wave, z = blockIdx.y, bt0 = blockIdx.z * NBT;
+  const int c0 = z * cps, ncs = min(nch, c0 + cps) - c0;
+  // R^T prefetch first (it comes from memory), then stage dp (mostly in L2)
+  const bool live = n16 * 16 < H && ncs > 0;
+  const uint4* rt = RTf + ((long)n16 * nch + c0) * 128 + lane;
+  Frag ring[kRecDepth];
+  if (live) {
+#pragma unroll
+    for (int s = 0; s < kRecDepth; ++s)
+      if (s < ncs) {
+        ring[s].v[0] = rt[(long)s * 128];
+        ring[s].v[1] = rt[(long)s * 128 + 64];
+      }
+  }
+  const int nblk = NBT * ncs * 128;
+  for (int i = tid; i < nblk; i += 64 * kRecWaves) {
+    const int bt = i / (ncs * 128), rem = i % (ncs * 128), cc = rem / 128, w = rem % 128;
+    sdp[(bt * cps + cc) * 128 + w] =
+        bt0 + bt < nbt ? DPf[((long)(bt0 + bt) * nch + c0 + cc) * 128 + w] : uint4{0u, 0u, 0u, 0u};
+  }
+  __syncthreads();
+  if (!live) return;
+  f32x4 acc[NBT];
+#pragma unroll
+  for (int bt = 0; bt < NBT; ++bt) acc[bt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int cb = 0; cb < ncs; cb += kRecDepth) {
+#pragma unroll
+    for (int s = 0; s < kRecDepth; ++s) {
+      const int cc = cb + s;
+      if (cc < ncs) {
+#pragma unroll
+        for (int bt = 0; bt < NBT; ++bt) {
+          const Frag d = lds_get(sdp + (bt * cps + cc) * 128, lane);
+          mfma_frag<BF16>(acc[bt], ring[s], d);
+        }
+        if (cc + kRecDepth < ncs) {
+          ring[s].v[0] = rt[(long)(cc + kRecDepth) * 128];
+          ring[s].v[1] = rt[(long)(cc + kRecDepth) * 128 + 64];
+        }
+      }
+    }
+  }
+  // acc[bt]: batch row 16 (bt0 + bt) + lane % 16, columns n .. n + 3
+  const int n = 16 * n16 + 4 * (lane >> 4);
+  float* pz = part + (long)z * pstride;
+#pragma unroll
+  for (int bt = 0; bt < NBT; ++bt) {
+    const int b = 16 * (bt0 + bt) + (lane & 15);
+    if (b >= B) continue;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (n + r < H) pz[(long)b * H + n + r] = acc[bt][r];
+  }
+}
+
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-struct BwdLayout {
-  size_t rt, wt, dp, dph, dpt, ut, ht, dy0, dy1, dhp, dcrec, total;
-  int S;  // K splits of the per-step product
+// Shape of the per-step product launch for a (B, H, dtype).
+struct RecShape {
+  int nch;      // chunks of K = 4H
+  int nt16;     // column tiles of 16 (n < H)
+  int nbt;      // batch tiles of 16
+  int NBT;      // batch tiles per workgroup (1, 2, 4 or 8)
+  int ngroups;  // workgroups across the columns (kRecWaves tiles each)
+  int bgroups;  // ... across the batch
+  int cps;      // chunks per K split
+  int S;        // K splits (partial sums the step kernel adds)
 };
 
-constexpr int kStepWM = 1, kStepWN = 4;  // per-step product tile: 32 x 128
-constexpr int kBigWM = 2, kBigWN = 2;    // weight-gradient products: 64 x 64
-
-// K splits of the per-step product: enough workgroups to fill 256 CUs.  The
-// count returned is the one the launch makes (chunks per split rounded up),
-// which the step kernel sums.
-int step_splits(int B, int H, int K, bool bf16) {
-  const int blocks = ((B + 32 * kStepWM - 1) / (32 * kStepWM)) * ((H + 32 * kStepWN - 1) / (32 * kStepWN));
-  const int nch = (K + (bf16 ? 64 : 32) - 1) / (bf16 ? 64 : 32);
-  const int want = std::max(1, std::min(nch, 256 / std::max(1, blocks)));
-  const int cps = (nch + want - 1) / want;
-  return (nch + cps - 1) / cps;
+// Enough K splits for about 256 workgroups, each staging at most
+// kRecLdsBlocks dp blocks; batch tiles go to as few workgroup groups as
+// possible, since every group streams all of R^T.
+RecShape rec_shape(int B, int H, bool bf16) {
+  RecShape r;
+  const int KC = bf16 ? 64 : 32;
+  r.nch = (4 * H + KC - 1) / KC;
+  r.nt16 = (H + 15) / 16;
+  r.nbt = (B + 15) / 16;
+  const int m = std::min(r.nbt, 8);
+  r.NBT = m <= 1 ? 1 : m <= 2 ? 2 : m <= 4 ? 4 : 8;
+  r.bgroups = (r.nbt + r.NBT - 1) / r.NBT;
+  r.ngroups = (r.nt16 + kRecWaves - 1) / kRecWaves;
+  const int want = std::max(1, 256 / (r.ngroups * r.bgroups));
+  r.cps = std::max(1, std::min((r.nch + want - 1) / want, kRecLdsBlocks / r.NBT));
+  r.S = (r.nch + r.cps - 1) / r.cps;
+  return r;
 }
+
+struct BwdLayout {
+  size_t rtf, dpf, wt, dp, dph, dpt, ut, ht, dy0, dy1, dhp, dcrec, total;
+  RecShape rs;
+};
+
+constexpr int kBigWM = 2, kBigWN = 2;  // weight-gradient products when the direct-to-LDS kernel does not fit
 
 bool bwd_layout(const lstm_desc_t* d, BwdLayout* o) {
   if (!d || d->cell != LSTM_CELL_LSTM || lstm_fwd_workspace_size(d) == 0) return false;
   const size_t s = d->dtype == LSTM_BF16 ? 2 : 4;
   const size_t H = d->H, B = d->B, TB = (size_t)d->T * d->B, G = 4 * H;
   const size_t Imax = std::max<size_t>(d->I, H);
-  o->S = step_splits(d->B, d->H, 4 * d->H, d->dtype == LSTM_BF16);
+  o->rs = rec_shape(d->B, d->H, d->dtype == LSTM_BF16);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
     off += align256(bytes);
     return at;
   };
-  o->rt = take(H * G * s);
+  o->rtf = take((size_t)o->rs.nt16 * o->rs.nch * 2048);
+  o->dpf = take((size_t)o->rs.nbt * o->rs.nch * 2048);
   o->wt = take(Imax * G * s);
   o->dp = take(TB * G * 4);
   o->dph = take(TB * G * s);
@@ -229,7 +392,7 @@ bool bwd_layout(const lstm_desc_t* d, BwdLayout* o) {
   o->ht = take(H * TB * s);
   o->dy0 = take(TB * H * 4);
   o->dy1 = take(TB * H * 4);
-  o->dhp = take((size_t)o->S * B * H * 4);
+  o->dhp = take((size_t)o->rs.S * B * H * 4);
   o->dcrec = take(B * H * 4);
   o->total = off;
   return true;
@@ -261,6 +424,37 @@ hipError_t gemm_nt(const void* A, long lda, const void* Bm, long ldb, float* C, 
   return hipGetLastError();
 }
 
+template <bool BF16, int NBT>
+const void* rec_product_fn() {
+  return reinterpret_cast<const void*>(&bwd_rec_product<BF16, NBT>);
+}
+
+template <bool BF16>
+hipError_t rec_product(const RecShape& r, const void* RTf, const void* DPf, float* part, int B, int H, hipStream_t st) {
+  const void* fn = r.NBT == 1   ? rec_product_fn<BF16, 1>()
+                   : r.NBT == 2 ? rec_product_fn<BF16, 2>()
+                   : r.NBT == 4 ? rec_product_fn<BF16, 4>()
+                                : rec_product_fn<BF16, 8>();
+  const int lds = r.NBT * r.cps * 2048;
+  hipError_t e = prepare_fn(fn, lds, 64 * kRecWaves, nullptr);
+  if (e != hipSuccess) return e;
+  const uint4* rt = static_cast<const uint4*>(RTf);
+  const uint4* dp = static_cast<const uint4*>(DPf);
+  long pstride = (long)B * H;
+  int nch = r.nch, cps = r.cps, nbt = r.nbt;
+  void* args[] = {&rt, &dp, &part, &pstride, &B, &H, &nch, &cps, &nbt};
+  return hipLaunchKernel(fn, dim3(r.ngroups, r.S, r.bgroups), dim3(64 * kRecWaves), args, (unsigned)lds, st);
+}
+
+// C = A B^T (see gemm_nt) on the direct-to-LDS kernel when the operands suit
+// it (K-contiguous rows of whole chunks, 16-byte aligned), else gemm_nt.
+template <bool BF16>
+hipError_t big_product(const void* A, const void* Bm, float* C, long ldc, int M, int N, int K, hipStream_t st) {
+  const hipError_t e = launch_gemm_plain(BF16, A, Bm, C, ldc, M, N, K, 0, st);
+  if (e != hipErrorNotSupported) return e;
+  return gemm_nt<BF16, kBigWM, kBigWN>(A, K, Bm, K, C, ldc, 0, M, N, K, 1, st);
+}
+
 template <bool BF16>
 lstm_status_t bwd_run(const lstm_desc_t* d, const void* x, const void* h0, const float* c0, const void* W,
                       const void* R, const void* reserve, const float* dy, const float* dhT, const float* dcT,
@@ -270,7 +464,9 @@ lstm_status_t bwd_run(const lstm_desc_t* d, const void* x, const void* h0, const
   const long TB = (long)T * B, G = 4L * H;
   const size_t s = BF16 ? 2 : 4;
   char* w = static_cast<char*>(ws);
-  void* RT = w + o.rt;
+  const RecShape& rs = o.rs;
+  void* RTf = w + o.rtf;
+  void* DPf = w + o.dpf;
   void* WT = w + o.wt;
   float* dP = reinterpret_cast<float*>(w + o.dp);
   void* dPh = w + o.dph;
@@ -288,6 +484,13 @@ lstm_status_t bwd_run(const lstm_desc_t* d, const void* x, const void* h0, const
   do {                                       \
     if ((e) != hipSuccess) return LSTM_ERR_HIP; \
   } while (0)
+  // the padding of dp's load-order copy (rows >= B, columns >= 4H) stays zero
+  {
+    const long n16 = (long)rs.nbt * rs.nch * 128;
+    hipLaunchKernelGGL(bwd_zero, dim3((unsigned)std::min<long>((n16 + kBwdThreads - 1) / kBwdThreads, 1024)),
+                       dim3(kBwdThreads), 0, st, static_cast<uint4*>(DPf), n16);
+    CHECK(hipGetLastError());
+  }
   for (int l = L - 1; l >= 0; --l) {
     const int Il = l == 0 ? I : H;
     const char* Wl = static_cast<const char*>(W) + (l == 0 ? 0 : (G * I + (size_t)(l - 1) * G * H)) * s;
@@ -295,14 +498,16 @@ lstm_status_t bwd_run(const lstm_desc_t* d, const void* x, const void* h0, const
     const float* gates = reinterpret_cast<const float*>(rsv + (size_t)l * tbh * 16);
     const float* cs = reinterpret_cast<const float*>(rsv + (size_t)L * tbh * 16 + (size_t)l * tbh * 4);
     const char* hs = rsv + (size_t)L * tbh * 20 + (size_t)l * tbh * s;
-    // R_l^T [H][4H]: the per-step product's second operand, K = 4H contiguous
-    CHECK(transpose<BF16>(Rl, H, nullptr, 0, 0, (int)G, H, RT, G, st));
+    // R_l^T in load order: the per-step product's streamed operand
+    hipLaunchKernelGGL(bwd_block_rt<BF16>, dim3((H + 63) / 64, rs.nch), dim3(kBwdThreads), 0, st,
+                       static_cast<const void*>(Rl), H, rs.nch, static_cast<uint4*>(RTf));
+    CHECK(hipGetLastError());
     for (int t = T - 1; t >= 0; --t) {
       StepArgs a;
       a.dY = dY + (size_t)t * B * H;
       a.dhp = t < T - 1 ? dhp : nullptr;
       a.sstride = (long)B * H;
-      a.S = o.S;
+      a.S = rs.S;
       a.dhT = dhT ? dhT + (size_t)l * B * H : nullptr;
       a.dcT = dcT ? dcT + (size_t)l * B * H : nullptr;
       a.gates = gates + (size_t)t * B * G;
@@ -311,17 +516,23 @@ lstm_status_t bwd_run(const lstm_desc_t* d, const void* x, const void* h0, const
       a.dcrec = dcrec;
       a.dP = dP + (size_t)t * B * G;
       a.dPh = static_cast<char*>(dPh) + (size_t)t * B * G * s;
+      a.dPf = DPf;
+      a.nch = rs.nch;
       a.dc0 = (t == 0 && dc0) ? dc0 + (size_t)l * B * H : nullptr;
       a.B = B, a.H = H, a.last = t == T - 1;
       const int blocks = (int)std::min<long>(((long)B * H + kBwdThreads - 1) / kBwdThreads, 1024);
       hipLaunchKernelGGL(bwd_step<BF16>, dim3(blocks), dim3(kBwdThreads), 0, st, a);
       CHECK(hipGetLastError());
-      const void* dpt = static_cast<const char*>(dPh) + (size_t)t * B * G * s;
-      if (t > 0) {
-        // dh_rec = dp_t R_l, as o.S partial sums over slices of K = 4H
-        CHECK((gemm_nt<BF16, kStepWM, kStepWN>(dpt, G, RT, G, dhp, H, (long)B * H, B, H, (int)G, o.S, st)));
-      } else if (dh0) {
-        CHECK((gemm_nt<BF16, kStepWM, kStepWN>(dpt, G, RT, G, dh0 + (size_t)l * B * H, H, 0, B, H, (int)G, 1, st)));
+      if (t > 0 || dh0) {
+        // dh_rec = dp_t R_l, as rs.S partial sums over slices of K = 4H
+        CHECK(rec_product<BF16>(rs, RTf, DPf, dhp, B, H, st));
+        if (t == 0) {
+          const long n = (long)B * H;
+          hipLaunchKernelGGL(bwd_sum_parts, dim3((unsigned)std::min<long>((n + kBwdThreads - 1) / kBwdThreads, 1024)),
+                             dim3(kBwdThreads), 0, st, static_cast<const float*>(dhp), n, rs.S, n,
+                             dh0 + (size_t)l * B * H);
+          CHECK(hipGetLastError());
+        }
       }
     }
     // db_l: column sums of dP over all steps and sequences
@@ -335,13 +546,13 @@ lstm_status_t bwd_run(const lstm_desc_t* d, const void* x, const void* h0, const
     const void* h0l = h0 ? static_cast<const char*>(h0) + (size_t)l * B * H * s : nullptr;
     CHECK(transpose<BF16>(hs, H, h0l, H, B, (int)TB, H, HT, TB, st));  // row t*B+b: h_{t-1}[b] (h0 at t = 0)
     float* dWl = dW + (l == 0 ? 0 : (G * I + (size_t)(l - 1) * G * H));
-    CHECK((gemm_nt<BF16, kBigWM, kBigWN>(dPT, TB, UT, TB, dWl, Il, 0, (int)G, Il, (int)TB, 1, st)));
-    CHECK((gemm_nt<BF16, kBigWM, kBigWN>(dPT, TB, HT, TB, dR + (size_t)l * G * H, H, 0, (int)G, H, (int)TB, 1, st)));
+    CHECK(big_product<BF16>(dPT, UT, dWl, Il, (int)G, Il, (int)TB, st));
+    CHECK(big_product<BF16>(dPT, HT, dR + (size_t)l * G * H, H, (int)G, H, (int)TB, st));
     if (l > 0 || dx) {
       // dU = dP W_l: the layer below's dY, or dx
       CHECK(transpose<BF16>(Wl, Il, nullptr, 0, 0, (int)G, Il, WT, G, st));
       float* dU = l > 0 ? dYbuf[next] : dx;
-      CHECK((gemm_nt<BF16, kBigWM, kBigWN>(dPh, G, WT, G, dU, Il, 0, (int)TB, Il, (int)G, 1, st)));
+      CHECK(big_product<BF16>(dPh, WT, dU, Il, (int)TB, Il, (int)G, st));
       dY = dU;
       next ^= 1;
     }

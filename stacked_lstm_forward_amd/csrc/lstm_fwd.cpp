@@ -231,7 +231,7 @@ lstm_status_t fwd_impl(const lstm_desc_t* d, const void* x, const void* h0, cons
   };
 
   auto gemm = [&](int l, const void* U, long long u_slot, int K, bool zero, void* fill) -> lstm_status_t {
-    GemmParams gp;
+    GemmParams gp{};  // C = null: the forward's G layout
     gp.W = W_l(l);
     gp.U = U;
     gp.u_slot = u_slot;

@@ -239,8 +239,10 @@ __device__ __forceinline__ void mfma_half<false>(f32x4& acc, const uint4& a, con
 
 // NT column tiles per workgroup (16, or 14 when that packs the columns into
 // fewer rounds of workgroups than 16 would: see launch_input_gemm); each of
-// the two column-halves of waves takes NT / 2.
-template <bool BF16, int NT>
+// the two column-halves of waves takes NT / 2.  PLAIN: rows in order (row m of
+// tile mt is 16 mt + m, rows >= H unused) and the product written to C[m][n]
+// without bias (the backward pass's gradient products).
+template <bool BF16, int NT, bool PLAIN>
 __global__ void __launch_bounds__(kDmaThreads) lstm_input_gemm_dma(const GemmParams P) {
   static_assert(NT % 2 == 0 && NT <= kDmaTiles, "column tiles per workgroup");
   constexpr int WM = kDmaTiles / 4;          // M-tiles per wave (4 M-quarters x 2 column halves)
@@ -308,7 +310,7 @@ __global__ void __launch_bounds__(kDmaThreads) lstm_input_gemm_dma(const GemmPar
     const int r = 8 * i + (lane >> 3);
     const long piece = (lane & 7) ^ ((r >> 1) & 7);
     const int mt = mtb + blk;
-    const long row = mt < P.Mt ? cell_row(P.cell, mt, r, P.H).w : -1;
+    const long row = mt >= P.Mt ? -1 : PLAIN ? (16 * mt + r < P.H ? 16 * mt + r : -1) : cell_row(P.cell, mt, r, P.H).w;
     srcA[k] = (uint32_t)(((row < 0 ? 0 : row) * P.K + piece * EPH) * (long)sizeof(T));
     dstA[k] = blk * 2048 + i * 1024;
   }
@@ -409,6 +411,24 @@ __global__ void __launch_bounds__(kDmaThreads) lstm_input_gemm_dma(const GemmPar
     interleave();
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the last (redundant) loads have landed
+
+  if constexpr (PLAIN) {
+#pragma unroll
+    for (int i = 0; i < WM; ++i) {
+      const int mt = mtb + WM * wm + i;
+#pragma unroll
+      for (int j = 0; j < WN; ++j) {
+        const long col = n0 + 16 * (WN * wn + j) + (lane & 15);
+        if (col >= P.N) continue;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int row = 16 * mt + 4 * q + k;
+          if (row < P.H) P.C[(long)row * P.ldc + col] = acc[i][j][k];
+        }
+      }
+    }
+    return;
+  }
 
   // epilogue: add bias, write [T][Mt][B][16]
   const T* bias = reinterpret_cast<const T*>(P.bias);
@@ -526,52 +546,65 @@ const void* input_gemm_fn(bool bf16, bool vec) {
              : reinterpret_cast<const void*>(&lstm_input_gemm<false, false, MTW, NTW>);
 }
 
-hipError_t launch_input_gemm(bool bf16, const GemmParams& p, hipStream_t s) {
-  constexpr int kMTW = kGemmTileM / 16, kNTW = kGemmTileN / 16;
+const void* dma_kernel(bool bf16, int nt, bool plain) {
+  if (plain)
+    return nt == 14 ? (bf16 ? reinterpret_cast<const void*>(&lstm_input_gemm_dma<true, 14, true>)
+                            : reinterpret_cast<const void*>(&lstm_input_gemm_dma<false, 14, true>))
+                    : (bf16 ? reinterpret_cast<const void*>(&lstm_input_gemm_dma<true, 16, true>)
+                            : reinterpret_cast<const void*>(&lstm_input_gemm_dma<false, 16, true>));
+  return nt == 14 ? (bf16 ? reinterpret_cast<const void*>(&lstm_input_gemm_dma<true, 14, false>)
+                          : reinterpret_cast<const void*>(&lstm_input_gemm_dma<false, 14, false>))
+                  : (bf16 ? reinterpret_cast<const void*>(&lstm_input_gemm_dma<true, 16, false>)
+                          : reinterpret_cast<const void*>(&lstm_input_gemm_dma<false, 16, false>));
+}
+
+// Byte offsets of the direct-to-LDS kernel are 32-bit: whether p's operands
+// stay below 2^32 bytes and every row is whole 16-byte pieces of whole chunks.
+bool dma_fits(bool bf16, const GemmParams& p) {
   const bool whole = (p.K % (bf16 ? Dt<true>::KC : Dt<false>::KC)) == 0;
-  // the 256 x 256 direct-to-LDS kernel pays off on long K (measured: 0.45 vs
-  // 0.53 ms at K = 4096, 0.33 vs 0.35 ms at K = 1536); short K keeps the
-  // register-staged 256 x 128 kernel, whose smaller tiles fill more CUs
-  // byte offsets of the direct-to-LDS kernel are 32-bit
   const long long esz = bf16 ? 2 : 4;
   const long long w_bytes = (long long)p.Mt * 16 * p.K * esz;  // at most G*H rows (tile rows past H are clamped)
   const long long u_bytes = ((long long)((p.N - 1) / p.B) * p.u_slot + (long long)p.B * p.K) * esz;
-  const bool small_offsets = w_bytes < (1LL << 32) && u_bytes < (1LL << 32);
-  if (p.vec_ok_w && p.vec_ok_u && whole && p.K >= 1024 && small_offsets) {
-    // 14 column tiles per workgroup instead of 16 when that needs no more
-    // rounds of one workgroup per CU: each round then loads 30 fragment
-    // blocks per chunk instead of 32 (the 16384 x 1600 projection of a
-    // 4096-wide bf16 layer at B = 32, T = 50: 448 tiles in 2 rounds become 512
-    // in 2 rounds)
-    const int nM = (p.Mt + kDmaTiles - 1) / kDmaTiles;
-    auto rounds = [&](int nt) {
-      const int cus = p.num_cus > 0 ? p.num_cus : 256;
-      return (nM * ((p.N + nt * 16 - 1) / (nt * 16)) + cus - 1) / cus;
-    };
-    int nt = rounds(14) * (kDmaTiles + 14) < rounds(16) * (kDmaTiles + 16) ? 14 : 16;
-    auto kernel_of = [&](int n) {
-      return n == 14 ? (bf16 ? reinterpret_cast<const void*>(&lstm_input_gemm_dma<true, 14>)
-                             : reinterpret_cast<const void*>(&lstm_input_gemm_dma<false, 14>))
-                     : (bf16 ? reinterpret_cast<const void*>(&lstm_input_gemm_dma<true, 16>)
-                             : reinterpret_cast<const void*>(&lstm_input_gemm_dma<false, 16>));
-    };
-    const void* fn = kernel_of(nt);
-    // 16 column tiles take all 160 KiB of a CU's LDS; a device that gives a
-    // workgroup less falls back to 14 (152 KiB)
-    hipError_t e = prepare_fn(fn, (int)dma_lds_bytes(nt), kDmaThreads, nullptr);
-    if (e != hipSuccess && nt == 16) {
-      (void)hipGetLastError();
-      nt = 14;
-      fn = kernel_of(nt);
-      e = prepare_fn(fn, (int)dma_lds_bytes(nt), kDmaThreads, nullptr);
-    }
-    if (e != hipSuccess) return e;
-    const unsigned lds = dma_lds_bytes(nt);
-    const int tiles = ((p.N + nt * 16 - 1) / (nt * 16)) * nM;
-    const dim3 grid((tiles + 7) & ~7);  // a multiple of the 8 XCDs (extra workgroups only help zeroing)
-    void* args[] = {const_cast<GemmParams*>(&p)};
-    return hipLaunchKernel(fn, grid, dim3(kDmaThreads), args, lds, s);
+  return p.vec_ok_w && p.vec_ok_u && whole && w_bytes < (1LL << 32) && u_bytes < (1LL << 32);
+}
+
+hipError_t launch_dma(bool bf16, const GemmParams& p, hipStream_t s) {
+  // 14 column tiles per workgroup instead of 16 when that needs no more
+  // rounds of one workgroup per CU: each round then loads 30 fragment
+  // blocks per chunk instead of 32 (the 16384 x 1600 projection of a
+  // 4096-wide bf16 layer at B = 32, T = 50: 448 tiles in 2 rounds become 512
+  // in 2 rounds)
+  const int nM = (p.Mt + kDmaTiles - 1) / kDmaTiles;
+  auto rounds = [&](int nt) {
+    const int cus = p.num_cus > 0 ? p.num_cus : 256;
+    return (nM * ((p.N + nt * 16 - 1) / (nt * 16)) + cus - 1) / cus;
+  };
+  int nt = rounds(14) * (kDmaTiles + 14) < rounds(16) * (kDmaTiles + 16) ? 14 : 16;
+  auto kernel_of = [&](int n) { return dma_kernel(bf16, n, p.C != nullptr); };
+  const void* fn = kernel_of(nt);
+  // 16 column tiles take all 160 KiB of a CU's LDS; a device that gives a
+  // workgroup less falls back to 14 (152 KiB)
+  hipError_t e = prepare_fn(fn, (int)dma_lds_bytes(nt), kDmaThreads, nullptr);
+  if (e != hipSuccess && nt == 16) {
+    (void)hipGetLastError();
+    nt = 14;
+    fn = kernel_of(nt);
+    e = prepare_fn(fn, (int)dma_lds_bytes(nt), kDmaThreads, nullptr);
   }
+  if (e != hipSuccess) return e;
+  const unsigned lds = dma_lds_bytes(nt);
+  const int tiles = ((p.N + nt * 16 - 1) / (nt * 16)) * nM;
+  const dim3 grid((tiles + 7) & ~7);  // a multiple of the 8 XCDs (extra workgroups only help zeroing)
+  void* args[] = {const_cast<GemmParams*>(&p)};
+  return hipLaunchKernel(fn, grid, dim3(kDmaThreads), args, lds, s);
+}
+
+hipError_t launch_input_gemm(bool bf16, const GemmParams& p, hipStream_t s) {
+  constexpr int kMTW = kGemmTileM / 16, kNTW = kGemmTileN / 16;
+  // the 256 x 256 direct-to-LDS kernel pays off on long K (measured: 0.45 vs
+  // 0.53 ms at K = 4096, 0.33 vs 0.35 ms at K = 1536); short K keeps the
+  // register-staged 256 x 128 kernel, whose smaller tiles fill more CUs
+  if (p.K >= 1024 && dma_fits(bf16, p)) return launch_dma(bf16, p, s);
   const bool vec = p.vec_ok_w && p.vec_ok_u && (p.K % (bf16 ? Dt<true>::KC : Dt<false>::KC)) == 0;
   // A problem the 256 x 128 tile covers with fewer than kGemmSmallGrid
   // workgroups (a short sequence, a small batch) leaves most CUs idle while
@@ -588,6 +621,25 @@ hipError_t launch_input_gemm(bool bf16, const GemmParams& p, hipStream_t s) {
   if (e != hipSuccess) return e;
   void* args[] = {const_cast<GemmParams*>(&p)};
   return hipLaunchKernel(fn, grid, dim3(kGemmThreads), args, lds, s);
+}
+
+// C[m][n] = sum over k of A[m][k] B[n][k] for m < M, n < N (A [M][K] and
+// B [N][K] row-major in the workload's dtype, C fp32 with row stride ldc) on
+// the direct-to-LDS kernel.  hipErrorNotSupported when the operands do not
+// suit it (the caller then uses another kernel); nothing is enqueued then.
+hipError_t launch_gemm_plain(bool bf16, const void* A, const void* B, float* C, long long ldc, int M, int N, int K,
+                             int num_cus, hipStream_t s) {
+  const long long esz = bf16 ? 2 : 4;
+  auto al16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+  GemmParams p{};
+  p.W = A, p.U = B, p.C = C, p.ldc = ldc;
+  p.K = K, p.H = M, p.Mt = (M + 15) / 16, p.B = N, p.N = N, p.u_slot = 0;
+  p.vec_ok_w = al16(A) && (K * esz) % 16 == 0;
+  p.vec_ok_u = al16(B) && (K * esz) % 16 == 0;
+  p.cell = kCellRnnTanh;
+  p.num_cus = num_cus;
+  if (M < 1 || N < 1 || K < 1 || !dma_fits(bf16, p)) return hipErrorNotSupported;
+  return launch_dma(bf16, p, s);
 }
 
 hipError_t launch_clear(int* p, long long n, hipStream_t s) {

@@ -34,6 +34,10 @@ struct GemmParams {
   int vec_ok_w, vec_ok_u;
   int cell;            // lstm_cell_t
   int num_cus;         // compute units of the device (tile-shape choice; 0: 256)
+  // plain product (the backward pass's weight and input gradients): C[m][n] =
+  // sum over k of W[m][k] U[n][k], rows m < H, fp32, row stride ldc; no bias
+  float* C;
+  long long ldc;
 };
 
 // One layer of a recurrent launch.
