@@ -75,6 +75,47 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_transpose(const S* main, long
   }
 }
 
+// The same transpose for T-typed source and destination with 16-byte global
+// loads and stores on whole 64 x 64 tiles (rows 16-byte aligned: the host
+// checks the bases and leading dimensions); partial tiles go element by element.
+template <typename T>
+__global__ void __launch_bounds__(kBwdThreads) bwd_transpose_v(const T* main, long ldm, const T* first, long ldf,
+                                                              int nfirst, int rows, int cols, T* dst, long ldd) {
+  constexpr int EPV = 16 / sizeof(T), PR = 64 / EPV;  // elements per 16 bytes, pieces per tile row
+  __shared__ __align__(16) T tile[64][64 + EPV];
+  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
+  auto src_row = [&](int r) -> const T* {
+    return r < nfirst ? (first ? first + (long)r * ldf : nullptr) : main + (long)(r - nfirst) * ldm;
+  };
+  if (r0 + 64 > rows || c0 + 64 > cols) {
+    for (int i = threadIdx.x; i < 64 * 64; i += kBwdThreads) {
+      const int r = i / 64, c = i % 64;
+      const T* row = r0 + r < rows ? src_row(r0 + r) : nullptr;
+      tile[r][c] = (row && c0 + c < cols) ? row[c0 + c] : T(0);
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < 64 * 64; i += kBwdThreads) {
+      const int c = i / 64, r = i % 64;
+      if (c0 + c < cols && r0 + r < rows) dst[(long)(c0 + c) * ldd + r0 + r] = tile[r][c];
+    }
+    return;
+  }
+  for (int i = threadIdx.x; i < 64 * PR; i += kBwdThreads) {
+    const int r = i / PR, pc = i % PR;
+    const T* row = src_row(r0 + r);
+    *reinterpret_cast<uint4*>(&tile[r][pc * EPV]) =
+        row ? *reinterpret_cast<const uint4*>(row + c0 + pc * EPV) : uint4{0u, 0u, 0u, 0u};
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * PR; i += kBwdThreads) {
+    const int c = i / PR, pr = i % PR;
+    T v[EPV];
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) v[e] = tile[pr * EPV + e][c];
+    *reinterpret_cast<uint4*>(dst + (long)(c0 + c) * ldd + r0 + pr * EPV) = *reinterpret_cast<const uint4*>(v);
+  }
+}
+
 // C[m][n] = sum over k of A[m][k] B[n][k] (fp32 accumulation), both operands
 // K-contiguous rows.  Workgroup tile (32 WM) x (32 WN): 4 waves in a 2 x 2
 // grid, each WM x WN MFMA tiles of 16 x 16.  blockIdx.z = K split z takes
@@ -205,12 +246,23 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_step(const StepArgs a) {
   }
 }
 
-// db[k] = sum over the rows r < rows of dP[r][k] (in row order).
-__global__ void __launch_bounds__(kBwdThreads) bwd_colsum(const float* dP, int rows, int cols, float* db) {
+// db[k] = sum over the rows r < rows of dP[r][k], in two passes with a fixed
+// order: slab z (rows kColSlab z .. kColSlab z + kColSlab - 1, in order) into
+// part[z][k], then the slabs in order.
+constexpr int kColSlab = 64;
+__global__ void __launch_bounds__(kBwdThreads) bwd_colsum_slab(const float* dP, int rows, int cols, float* part) {
+  const int k = blockIdx.x * kBwdThreads + threadIdx.x, z = blockIdx.y;
+  if (k >= cols) return;
+  const int r1 = min(rows, (z + 1) * kColSlab);
+  float s = 0.f;
+  for (int r = z * kColSlab; r < r1; ++r) s += dP[(long)r * cols + k];
+  part[(long)z * cols + k] = s;
+}
+__global__ void __launch_bounds__(kBwdThreads) bwd_colsum_final(const float* part, int slabs, int cols, float* db) {
   const int k = blockIdx.x * kBwdThreads + threadIdx.x;
   if (k >= cols) return;
   float s = 0.f;
-  for (int r = 0; r < rows; ++r) s += dP[(long)r * cols + k];
+  for (int z = 0; z < slabs; ++z) s += part[(long)z * cols + k];
   db[k] = s;
 }
 
@@ -364,7 +416,7 @@ RecShape rec_shape(int B, int H, bool bf16) {
 }
 
 struct BwdLayout {
-  size_t rtf, dpf, wt, dp, dph, dpt, ut, ht, dy0, dy1, dhp, dcrec, total;
+  size_t rtf, dpf, wt, dp, dph, dpt, ut, ht, dy0, dy1, dhp, dcrec, colp, total;
   RecShape rs;
 };
 
@@ -394,6 +446,7 @@ bool bwd_layout(const lstm_desc_t* d, BwdLayout* o) {
   o->dy1 = take(TB * H * 4);
   o->dhp = take((size_t)o->rs.S * B * H * 4);
   o->dcrec = take(B * H * 4);
+  o->colp = take((TB + kColSlab - 1) / kColSlab * G * 4);
   o->total = off;
   return true;
 }
@@ -405,6 +458,12 @@ hipError_t transpose(const void* main, long ldm, const void* first, long ldf, in
                      long ldd, hipStream_t s) {
   typedef typename Dt<BF16>::T T;
   const dim3 grid((cols + 63) / 64, (rows + 63) / 64);
+  const long epv = 16 / (long)sizeof(T);
+  if (aligned16(main) && aligned16(first) && aligned16(dst) && ldm % epv == 0 && ldf % epv == 0 && ldd % epv == 0) {
+    hipLaunchKernelGGL((bwd_transpose_v<T>), grid, dim3(kBwdThreads), 0, s, static_cast<const T*>(main), ldm,
+                       static_cast<const T*>(first), ldf, nfirst, rows, cols, static_cast<T*>(dst), ldd);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((bwd_transpose<T, T>), grid, dim3(kBwdThreads), 0, s, static_cast<const T*>(main), ldm,
                      static_cast<const T*>(first), ldf, nfirst, rows, cols, static_cast<T*>(dst), ldd);
   return hipGetLastError();
@@ -476,6 +535,7 @@ lstm_status_t bwd_run(const lstm_desc_t* d, const void* x, const void* h0, const
   float* dYbuf[2] = {reinterpret_cast<float*>(w + o.dy0), reinterpret_cast<float*>(w + o.dy1)};
   float* dhp = reinterpret_cast<float*>(w + o.dhp);
   float* dcrec = reinterpret_cast<float*>(w + o.dcrec);
+  float* colp = reinterpret_cast<float*>(w + o.colp);
   const char* rsv = static_cast<const char*>(reserve);
   const size_t tbh = (size_t)T * B * H;
   const float* dY = dy;
@@ -536,9 +596,15 @@ lstm_status_t bwd_run(const lstm_desc_t* d, const void* x, const void* h0, const
       }
     }
     // db_l: column sums of dP over all steps and sequences
-    hipLaunchKernelGGL(bwd_colsum, dim3((unsigned)((G + kBwdThreads - 1) / kBwdThreads)), dim3(kBwdThreads), 0, st, dP,
-                       (int)TB, (int)G, db + (size_t)l * G);
-    CHECK(hipGetLastError());
+    {
+      const int slabs = (int)((TB + kColSlab - 1) / kColSlab);
+      const unsigned gx = (unsigned)((G + kBwdThreads - 1) / kBwdThreads);
+      hipLaunchKernelGGL(bwd_colsum_slab, dim3(gx, slabs), dim3(kBwdThreads), 0, st, dP, (int)TB, (int)G, colp);
+      CHECK(hipGetLastError());
+      hipLaunchKernelGGL(bwd_colsum_final, dim3(gx), dim3(kBwdThreads), 0, st, static_cast<const float*>(colp), slabs,
+                         (int)G, db + (size_t)l * G);
+      CHECK(hipGetLastError());
+    }
     // the K = T*B contiguous operands of the weight-gradient products
     CHECK(transpose<BF16>(dPh, G, nullptr, 0, 0, (int)TB, (int)G, dPT, TB, st));
     const void* U = l == 0 ? x : static_cast<const void*>(rsv + (size_t)L * tbh * 20 + (size_t)(l - 1) * tbh * s);
