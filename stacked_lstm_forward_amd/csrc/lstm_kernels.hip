@@ -476,7 +476,20 @@ LSTM_DECL(f32, lds, 4) LSTM_DECL(f32, stream, 4) LSTM_DECL(bf16, lds, 4) LSTM_DE
 LSTM_DECL(f32, lds, 8) LSTM_DECL(f32, stream, 8) LSTM_DECL(bf16, lds, 8) LSTM_DECL(bf16, stream, 8)
 #undef LSTM_DECL
 
-const void* rec_res_kernel_ptr(bool bf16, int mw, int nw, int nci, int nrb);
+const void* rec_res_kernel_ptr_shape0(int nw);
+const void* rec_res_kernel_ptr_shape1(int nw);
+const void* rec_res_kernel_ptr_shape2(int nw);
+static_assert(kResShapes == 3, "one instantiation unit per resident shape");
+
+const void* rec_res_kernel_ptr(bool bf16, int mw, int nw, int nci, int nrb) {
+  const void* (*const per_shape[kResShapes])(int) = {rec_res_kernel_ptr_shape0, rec_res_kernel_ptr_shape1,
+                                                      rec_res_kernel_ptr_shape2};
+  for (int k = 0; k < kResShapes; ++k) {
+    const ResShape& r = kResShape[k];
+    if ((r.bf16 != 0) == bf16 && r.mw == mw && r.nci == nci && r.nrb == nrb) return per_shape[k](nw);
+  }
+  return nullptr;
+}
 
 namespace {
 const void* rec_kernel_fn(bool bf16, bool stream, bool vec, int nwv, int mw, int nw, bool frag) {

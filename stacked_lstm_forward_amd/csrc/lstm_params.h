@@ -13,9 +13,20 @@ constexpr int kGemmTileM = 256;          // rows (16 M-tiles) per input-GEMM wor
 constexpr int kGemmTileN = 128;          // columns (time x batch) per input-GEMM workgroup
 constexpr int kSlotAlign = 256;          // bytes: exchange slots never share a cache line
 // Register-resident recurrent kernel (one layer, weights in registers + LDS):
-// 4 waves = 4 K-groups, kResMW M-tiles per workgroup, kResNCI chunks per
-// K-group, kResNRB of each wave's kResMW * kResNCI blocks in registers.
-constexpr int kResMW = 4, kResNCI = 16, kResNRB = 48;
+// 4 waves = 4 K-groups; per shape the dtype, mw M-tiles per workgroup, nci
+// chunks per K-group (H = 4 nci chunks of 64 bf16 or 32 fp32 columns exactly)
+// and nrb of each wave's mw * nci weight blocks in registers, the rest in LDS;
+// up to kResMaxNW 16-column batch tiles.
+struct ResShape {
+  int bf16, mw, nci, nrb;
+};
+constexpr int kResShapes = 3;
+constexpr ResShape kResShape[kResShapes] = {
+    {1, 4, 16, 48},  // bf16 H = 4096 (R_l 128 MiB): 48 blocks in registers, 16 in LDS
+    {1, 3, 12, 36},  // bf16 H = 3072 (72 MiB): all 36 in registers
+    {0, 2, 16, 16},  // fp32 H = 2048 (64 MiB): 16 blocks in registers, 16 in LDS
+};
+constexpr int kResMaxNW = 4;
 
 // Input projection G = W_l U^T + b_l over all T*B columns (hoisted out of the recurrence).
 // Output layout [T][Mt][B][16] fp32: for step t, M-tile mt, batch b, the 16

@@ -100,19 +100,29 @@ bool choose_split(int mmax, int ncnt, int nch, int staged_bytes, int lds_limit, 
 int round_grid(int g) { return (g + 7) & ~7; }
 
 // Register-resident launch of one layer: the weight rows stay on chip, split
-// between the registers and the LDS of each workgroup.  Only the bf16 shape
-// the kernel is instantiated for: 4 M-tiles per workgroup, 4 K-groups of
-// exactly kResNCI chunks each (H = 4096), at most two 16-column batch tiles.
-bool resident_shape(bool bf16, int nch, int ncnt) { return bf16 && nch == 4 * kResNCI && ncnt <= 2; }
+// between the registers and the LDS of each workgroup.  Only the shapes the
+// kernel is instantiated for (kResShape): the workgroup's M-tiles, 4 K-groups
+// of exactly nci chunks each, at most kResMaxNW 16-column batch tiles.
+// Returns the entry of kResShape, or -1.
+int resident_shape(bool bf16, int m, int nch, int ncnt) {
+  if (ncnt > kResMaxNW) return -1;
+  for (int k = 0; k < kResShapes; ++k) {
+    const ResShape& r = kResShape[k];
+    if ((r.bf16 != 0) == bf16 && r.mw == m && 4 * r.nci == nch) return k;
+  }
+  return -1;
+}
 
 bool plan_resident(int m, int nch, int ncnt, bool bf16, bool aligned, const DeviceInfo& dev, LaunchPlan* lp) {
-  if (!resident_shape(bf16, nch, ncnt) || !aligned || m > kResMW) return false;
-  const int nlb = kResMW * kResNCI - kResNRB;  // LDS blocks per wave
-  const int red = kResMW * 4 * 64 * 16;        // one 1 KiB partial per (M-tile, K-group)
+  const int k = aligned ? resident_shape(bf16, m, nch, ncnt) : -1;
+  if (k < 0) return false;
+  const ResShape& r = kResShape[k];
+  const int nlb = r.mw * r.nci - r.nrb;  // LDS blocks per wave
+  const int red = r.mw * 4 * 64 * 16;    // one 1 KiB partial per (M-tile, K-group)
   const int red_off = 4 * nlb * 64 * kFragBytes;
   if (red_off + red + kLdsReserve > dev.lds_per_block) return false;
-  lp->res_nrb = kResNRB, lp->res_nci = kResNCI;
-  lp->nwaves = 4, lp->ks = 4, lp->ntgm = 1, lp->ntgn = 1, lp->mw = kResMW, lp->nw = ncnt;
+  lp->res_nrb = r.nrb, lp->res_nci = r.nci;
+  lp->nwaves = 4, lp->ks = 4, lp->ntgm = 1, lp->ntgn = 1, lp->mw = r.mw, lp->nw = ncnt;
   lp->red_off = red_off, lp->lds_bytes = red_off + red;
   lp->stream = 0;
   return true;

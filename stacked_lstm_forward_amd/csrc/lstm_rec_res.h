@@ -53,10 +53,36 @@ constexpr int kResWaves = 4;  // waves per workgroup = K-groups
 // accumulators.
 constexpr int kResAgprBlocks = 30;
 
+// One register weight block (a wave's fragment of 16 rows x one chunk) in the
+// MFMA operand type, and the products of one chunk into one accumulator: bf16
+// two 16x16x32 MFMAs, fp32 eight 16x16x4 MFMAs, back to back (each takes the
+// previous one's result without a register read).
+template <bool BF16>
+struct ResOps;
+template <>
+struct ResOps<true> {
+  typedef bf16x8 V;
+  static __device__ __forceinline__ V cast(const uint4& u) { return __builtin_bit_cast(bf16x8, u); }
+  static __device__ __forceinline__ void chunk(f32x4& acc, const V& a0, const V& a1, const V& x0, const V& x1) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, x0, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, x1, acc, 0, 0, 0);
+  }
+};
+template <>
+struct ResOps<false> {
+  typedef f32x4 V;
+  static __device__ __forceinline__ V cast(const uint4& u) { return __builtin_bit_cast(f32x4, u); }
+  static __device__ __forceinline__ void chunk(f32x4& acc, const V& a0, const V& a1, const V& x0, const V& x1) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[e], x0[e], acc, 0, 0, 0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a1[e], x1[e], acc, 0, 0, 0);
+  }
+};
+
 template <bool BF16, int MW, int NW, int NCI, int NRB>
 __global__ void __launch_bounds__(64 * kResWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
 lstm_rec_res_kernel(const RecParams P) {
-  static_assert(BF16, "the resident kernel multiplies bf16");
   typedef typename Dt<BF16>::T T;
   constexpr int KC = Dt<BF16>::KC;
   constexpr int KS = kResWaves;
@@ -65,7 +91,9 @@ lstm_rec_res_kernel(const RecParams P) {
   constexpr int LPC = NLB / NCI;   // LDS M-tiles per chunk
   constexpr int RPC = MW - LPC;    // register M-tiles per chunk
   static_assert(NLB % NCI == 0, "LDS blocks spread evenly over the chunks");
-  constexpr int PD = 4;  // chunks of h loads in flight (H = 4096, B = 32: 2 -> 0.51 ms per layer, 4 -> 0.42, 6 no better)
+  // chunks of h loads in flight (H = 4096, B = 32: 2 -> 0.51 ms per layer, 4 -> 0.42, 6 no better;
+  // 3 with more than two column tiles, whose per-tile state takes the registers)
+  constexpr int PD = NW <= 2 ? 4 : 3;
   static_assert(NRB >= 0 && NRB <= NB, "register blocks");
   static_assert(MW <= KS, "one finishing K-group per M-tile");
   extern __shared__ __align__(16) unsigned char smem[];
@@ -114,8 +142,10 @@ lstm_rec_res_kernel(const RecParams P) {
   // ---- this wave's weight blocks: M-tile i < RPC of chunk slot ci is
   // register block ci * RPC + i, M-tile i >= RPC is LDS block ci * LPC + i - RPC
   const T* Rp = reinterpret_cast<const T*>(Lr.R) + kg * KC;
+  typedef ResOps<BF16> Ops;
+  typedef typename Ops::V V;
   struct WB {
-    bf16x8 h[2];
+    V h[2];
   };
   WB wreg[NRB > 0 ? NRB : 1];
 #pragma unroll
@@ -125,7 +155,7 @@ lstm_rec_res_kernel(const RecParams P) {
     frag_mask(f, mr_[i]);
     if (i < RPC) {
       const int r = ci * RPC + (i < RPC ? i : 0);
-      WB w{{__builtin_bit_cast(bf16x8, f.v[0]), __builtin_bit_cast(bf16x8, f.v[1])}};
+      WB w{{Ops::cast(f.v[0]), Ops::cast(f.v[1])}};
       if (r < kResAgprBlocks) {
         asm volatile("" : "+a"(w.h[0]));
         asm volatile("" : "+a"(w.h[1]));
@@ -147,14 +177,12 @@ lstm_rec_res_kernel(const RecParams P) {
     fpos = c * FB + hh * (FB / 2) + (qq * 16 + (lane & 15)) * EPH + e;
   }
   bool flive[NW];
-  long fgoff[NW];
   float st[NW];
   const T* h0p = reinterpret_cast<const T*>(Lr.h0);
 #pragma unroll
   for (int j = 0; j < NW; ++j) {
     const int bc = 16 * j + (lane & 15);
     flive[j] = fm && j < P.ncnt && funit < H && bc < B;
-    fgoff[j] = ((long)min(mt0 + kg, P.Mt - 1) * B + min(bc, B - 1)) * 16 + 4 * q;
     st[j] = 0.f;
     if (flive[j]) {
       const long o = (long)bc * H + funit;
@@ -180,11 +208,19 @@ lstm_rec_res_kernel(const RecParams P) {
   for (int t = 0; t < T_; ++t) {
     stamp(t, 0);
     stamp_clk(t, 6);
-    f32x4 gq[NW];
-    {
-      const float* gt = Gp + (long)t * P.Mt * B * 16;
+    // hoisted pre-activations of this lane's unit in column tile j: with up
+    // to two tiles all are loaded before the wait, with more each one at the
+    // start of its pass (registers)
+    const float* gt = Gp + (long)t * P.Mt * B * 16;
+    auto gload = [&](int j) {
+      const long off = ((long)min(mt0 + kg, P.Mt - 1) * B + min(16 * j + (lane & 15), B - 1)) * 16 + 4 * q;
+      return *reinterpret_cast<const f32x4*>(gt + off);
+    };
+    constexpr bool kEarlyG = NW <= 2;
+    f32x4 gq[kEarlyG ? NW : 1];
+    if constexpr (kEarlyG) {
 #pragma unroll
-      for (int j = 0; j < NW; ++j) gq[j] = *reinterpret_cast<const f32x4*>(gt + fgoff[j]);
+      for (int j = 0; j < NW; ++j) gq[j] = gload(j);
     }
 
     if (t > 0) {
@@ -247,21 +283,19 @@ lstm_rec_res_kernel(const RecParams P) {
           for (int i = 0; i < MW; ++i) {
             // no branch: a missing M-tile has zero weights and a missing
             // column tile a clamped h row; their sums are never finished
-            const bf16x8 x0 = __builtin_bit_cast(bf16x8, rb[s].v[0]), x1 = __builtin_bit_cast(bf16x8, rb[s].v[1]);
-            bf16x8 a0, a1;
+            const V x0 = Ops::cast(rb[s].v[0]), x1 = Ops::cast(rb[s].v[1]);
+            V a0, a1;
             if (i < RPC) {
               a0 = wreg[ci * RPC + (i < RPC ? i : 0)].h[0];
               a1 = wreg[ci * RPC + (i < RPC ? i : 0)].h[1];
             } else {
-              a0 = __builtin_bit_cast(bf16x8, al[ci & 1][i < RPC ? 0 : i - RPC].v[0]);
-              a1 = __builtin_bit_cast(bf16x8, al[ci & 1][i < RPC ? 0 : i - RPC].v[1]);
+              a0 = Ops::cast(al[ci & 1][i < RPC ? 0 : i - RPC].v[0]);
+              a1 = Ops::cast(al[ci & 1][i < RPC ? 0 : i - RPC].v[1]);
             }
-            // the two products of one accumulator back to back: its second
-            // product takes the first's result without a register read
-            // (a pair issues every 16.9 cycles, alternating accumulators
-            // every 22.9, which the scheduler would otherwise choose)
-            acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, x0, acc[i], 0, 0, 0);
-            acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, x1, acc[i], 0, 0, 0);
+            // one accumulator's products back to back (bf16: a pair issues
+            // every 16.9 cycles, alternating accumulators every 22.9, which
+            // the scheduler would otherwise choose)
+            Ops::chunk(acc[i], a0, a1, x0, x1);
             __builtin_amdgcn_sched_barrier(0);
           }
           if (g + PD < NW * NCI) issue(rb[s], g + PD);
@@ -280,7 +314,7 @@ lstm_rec_res_kernel(const RecParams P) {
       __syncthreads();
       if (j == 0) stamp(t, 3);
       if (flive[j]) {
-        f32x4 p = gq[j];
+        f32x4 p = kEarlyG ? gq[kEarlyG ? j : 0] : gload(j);
 #pragma unroll
         for (int r = 0; r < KS; ++r) p += red[(kg * KS + r) * 64 + lane];
         const long o = (long)(16 * j + (lane & 15)) * H + funit;

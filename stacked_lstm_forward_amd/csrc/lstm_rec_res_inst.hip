@@ -1,16 +1,29 @@
-// Instantiations of the register-and-LDS resident recurrent kernel: bf16,
-// kResMW = 4 M-tiles per workgroup, kResNCI = 16 chunks of 64 columns per
-// K-group (H = 4096), one or two 16-column batch tiles; kResNRB = 48 of a
-// wave's 64 blocks stay in registers (384 of its 512), the other 16 per wave
-// (128 KiB per workgroup) in LDS.
+// Instantiations of the register-and-LDS resident recurrent kernel for one
+// entry of kResShape (selected by LSTM_RES_SHAPE at compile time), with 1 to
+// kResMaxNW 16-column batch tiles.
 #include "lstm_rec_res.h"
+
+#ifndef LSTM_RES_SHAPE
+#error "define LSTM_RES_SHAPE"
+#endif
+
+#define LSTM_RES_CAT2(a, b) a##b
+#define LSTM_RES_CAT(a, b) LSTM_RES_CAT2(a, b)
 
 namespace lstm {
 
-const void* rec_res_kernel_ptr(bool bf16, int mw, int nw, int nci, int nrb) {
-  if (!bf16 || mw != kResMW || nci != kResNCI || nrb != kResNRB) return nullptr;
-  if (nw == 1) return reinterpret_cast<const void*>(&lstm_rec_res_kernel<true, kResMW, 1, kResNCI, kResNRB>);
-  if (nw == 2) return reinterpret_cast<const void*>(&lstm_rec_res_kernel<true, kResMW, 2, kResNCI, kResNRB>);
+const void* LSTM_RES_CAT(rec_res_kernel_ptr_shape, LSTM_RES_SHAPE)(int nw) {
+  constexpr ResShape S = kResShape[LSTM_RES_SHAPE];
+  switch (nw) {
+    case 1:
+      return reinterpret_cast<const void*>(&lstm_rec_res_kernel<S.bf16 != 0, S.mw, 1, S.nci, S.nrb>);
+    case 2:
+      return reinterpret_cast<const void*>(&lstm_rec_res_kernel<S.bf16 != 0, S.mw, 2, S.nci, S.nrb>);
+    case 3:
+      return reinterpret_cast<const void*>(&lstm_rec_res_kernel<S.bf16 != 0, S.mw, 3, S.nci, S.nrb>);
+    case 4:
+      return reinterpret_cast<const void*>(&lstm_rec_res_kernel<S.bf16 != 0, S.mw, 4, S.nci, S.nrb>);
+  }
   return nullptr;
 }
 
