@@ -145,8 +145,7 @@ bool plan_single(int layer, int Mt, int nch, int ncnt, bool bf16, bool aligned, 
   if (choose_split(m, ncnt, nch, staged_bytes, dev.lds_per_block, 4, lp)) {
     L.staged = 1;
     lp->stream = 0;
-  } else if (wgs <= 256 && plan_resident(m, nch, ncnt, bf16, aligned, dev, lp)) {
-    // (the resident kernel polls all its counters with one wave-wide batch)
+  } else if (plan_resident(m, nch, ncnt, bf16, aligned, dev, lp)) {
     L.staged = 1;
   } else if (choose_split(m, ncnt, nch, 0, dev.lds_per_block, 4, lp)) {
     L.staged = 0;
