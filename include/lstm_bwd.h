@@ -39,6 +39,13 @@
  *
  * Errors: status codes as in lstm_fwd.h, checked on the host before anything
  * is enqueued; a cell other than the LSTM returns LSTM_ERR_UNSUPPORTED.
+ *
+ * Recurrent chain: for bf16 layers with H = 4096 and B <= 32 (when all 256 of
+ * its workgroups fit on the device at once) it runs as one persistent launch
+ * per layer that keeps R_l^T on chip and exchanges dp_t through `ws` with
+ * per-workgroup step counters; a step wait longer than 2 s sets the error word
+ * that lstm_bwd_last_error reports.  Other shapes run it as two launches per
+ * step that stream R_l^T from memory.
  */
 #ifndef LSTM_BWD_H
 #define LSTM_BWD_H
@@ -61,6 +68,11 @@ lstm_status_t lstm_fwd_train(const lstm_desc_t *d,
 
 /* Bytes of the workspace lstm_bwd needs for `d` (0: invalid or unsupported). */
 size_t lstm_bwd_workspace_size(const lstm_desc_t *d);
+
+/* Status of the last lstm_bwd on `ws`: synchronises `stream`, then reads the
+ * workspace's error word (LSTM_ERR_BARRIER_TIMEOUT if a step wait of the
+ * on-chip recurrent chain ran out).  lstm_bwd zeroes that word on entry. */
+lstm_status_t lstm_bwd_last_error(const void *ws, hipStream_t stream);
 
 /* Backward pass: gradients of every forward input from dy, dhT and dcT. */
 lstm_status_t lstm_bwd(const lstm_desc_t *d,

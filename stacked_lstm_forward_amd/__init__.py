@@ -41,7 +41,8 @@ CELL_IDS = {"lstm": LSTM_CELL_LSTM, "gru": LSTM_CELL_GRU, "rnn_tanh": LSTM_CELL_
 EXPORTED = ("lstm_fwd_workspace_size", "lstm_fwd", "lstm_fwd_ex", "lstm_status_string",
             "lstm_fwd_validate", "lstm_fwd_last_error", "lstm_fwd_plan", "lstm_fwd_noalloc")
 NOALLOC_MAX_WORKSPACE = 64 << 20  # LSTM_FWD_NOALLOC_MAX_WORKSPACE
-EXPORTED_TRAIN = ("lstm_train_reserve_size", "lstm_fwd_train", "lstm_bwd_workspace_size", "lstm_bwd")
+EXPORTED_TRAIN = ("lstm_train_reserve_size", "lstm_fwd_train", "lstm_bwd_workspace_size", "lstm_bwd",
+                  "lstm_bwd_last_error")
 
 
 class LstmDesc(ctypes.Structure):
@@ -120,6 +121,8 @@ def load_library() -> ctypes.CDLL:
     lib.lstm_train_reserve_size.restype = sz
     lib.lstm_bwd_workspace_size.argtypes = [pdesc]
     lib.lstm_bwd_workspace_size.restype = sz
+    lib.lstm_bwd_last_error.argtypes = [vp, vp]
+    lib.lstm_bwd_last_error.restype = i32
     lib.lstm_fwd_train.argtypes = [pdesc, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.lstm_fwd_train.restype = i32
     lib.lstm_bwd.argtypes = [pdesc] + [vp] * 17
@@ -177,6 +180,10 @@ def lstm_fwd_noalloc(desc, x, h0, c0, W, R, b, y, hT, cT, dev_status=None, strea
 
 def lstm_train_reserve_size(desc) -> int:
     return int(load_library().lstm_train_reserve_size(ctypes.byref(desc)))
+
+
+def lstm_bwd_last_error(ws, stream=None) -> int:
+    return int(load_library().lstm_bwd_last_error(_ptr(ws), _stream(stream)))
 
 
 def lstm_bwd_workspace_size(desc) -> int:

@@ -25,7 +25,11 @@
 
 #include <algorithm>
 
+#include <mutex>
+#include <vector>
+
 #include "lstm_bwd.h"  // include/ is on the include path
+#include "lstm_bwd_res.h"
 #include "lstm_common.h"
 #include "lstm_params.h"
 
@@ -416,9 +420,48 @@ RecShape rec_shape(int B, int H, bool bf16) {
 }
 
 struct BwdLayout {
-  size_t rtf, dpf, wt, dp, dph, dpt, ut, ht, dy0, dy1, dhp, dcrec, colp, total;
+  size_t ctl, flg, dpx, rtf, dpf, wt, dp, dph, dpt, ut, ht, dy0, dy1, dhp, dcrec, colp, total;
   RecShape rs;
+  bool resident;  // the chain runs in lstm_bwd_res_kernel
 };
+
+// The on-chip chain kernel's shape: bf16, H = 4096 (4 K-groups of 64 chunks of
+// 64 columns; 48 register and 16 LDS blocks per wave), at most two batch tiles.
+constexpr int kBwdResNCI = 64, kBwdResNRB = 48;
+bool bwd_resident_shape(const lstm_desc_t* d) {
+  return d->dtype == LSTM_BF16 && d->H == 4 * kBwdResNCI * 64 / 4 && d->B <= 32;
+}
+
+const void* bwd_res_fn(int nw) {
+  return nw == 1 ? reinterpret_cast<const void*>(&lstm_bwd_res_kernel<true, 1, kBwdResNCI, kBwdResNRB>)
+                 : reinterpret_cast<const void*>(&lstm_bwd_res_kernel<true, 2, kBwdResNCI, kBwdResNRB>);
+}
+
+// Compute units and wall-clock rate (kHz) of the current device, once per device.
+hipError_t bwd_device(int* cus, int* clk_khz) {
+  struct Info {
+    int dev, cus, clk;
+  };
+  static std::mutex mu;
+  static std::vector<Info> seen;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const Info& i : seen)
+    if (i.dev == dev) {
+      *cus = i.cus, *clk_khz = i.clk;
+      return hipSuccess;
+    }
+  Info i{dev, 0, 0};
+  if ((e = hipDeviceGetAttribute(&i.cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+  if ((e = hipDeviceGetAttribute(&i.clk, hipDeviceAttributeWallClockRate, dev)) != hipSuccess) return e;
+  seen.push_back(i);
+  *cus = i.cus, *clk_khz = i.clk;
+  return hipSuccess;
+}
+
+constexpr long long kBwdTimeoutUs = 2000000;  // 2 s per step wait
 
 constexpr int kBigWM = 2, kBigWN = 2;  // weight-gradient products when the direct-to-LDS kernel does not fit
 
@@ -428,12 +471,16 @@ bool bwd_layout(const lstm_desc_t* d, BwdLayout* o) {
   const size_t H = d->H, B = d->B, TB = (size_t)d->T * d->B, G = 4 * H;
   const size_t Imax = std::max<size_t>(d->I, H);
   o->rs = rec_shape(d->B, d->H, d->dtype == LSTM_BF16);
+  o->resident = bwd_resident_shape(d);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
     off += align256(bytes);
     return at;
   };
+  o->ctl = take(256);  // the error word first, as in the forward's workspace
+  o->flg = take(o->resident ? (size_t)o->rs.nt16 * kFlagStride * 4 : 0);
+  o->dpx = take(o->resident ? (size_t)d->T * o->rs.nbt * o->rs.nch * 2048 : 0);
   o->rtf = take((size_t)o->rs.nt16 * o->rs.nch * 2048);
   o->dpf = take((size_t)o->rs.nbt * o->rs.nch * 2048);
   o->wt = take(Imax * G * s);
@@ -544,6 +591,25 @@ lstm_status_t bwd_run(const lstm_desc_t* d, const void* x, const void* h0, const
   do {                                       \
     if ((e) != hipSuccess) return LSTM_ERR_HIP; \
   } while (0)
+  // the on-chip chain needs every workgroup resident at once: checked (and
+  // the kernel's LDS limit set) before anything is enqueued, else the
+  // streamed chain runs
+  int cus = 0, clk_khz = 0;
+  CHECK(bwd_device(&cus, &clk_khz));
+  bool resident = o.resident;
+  const int res_nw = (B + 15) / 16;
+  const int res_lds = bwd_res_lds_bytes(kBwdResNCI, kBwdResNRB, res_nw);
+  if (resident) {
+    int per_cu = 0;
+    if (prepare_fn(bwd_res_fn(res_nw), res_lds, 64 * kBwdResWaves, &per_cu) != hipSuccess ||
+        (long)per_cu * cus < rs.nt16) {
+      (void)hipGetLastError();
+      resident = false;
+    }
+  }
+  // the error word
+  hipLaunchKernelGGL(bwd_zero, dim3(1), dim3(kBwdThreads), 0, st, reinterpret_cast<uint4*>(w + o.ctl), 16L);
+  CHECK(hipGetLastError());
   // the padding of dp's load-order copy (rows >= B, columns >= 4H) stays zero
   {
     const long n16 = (long)rs.nbt * rs.nch * 128;
@@ -562,7 +628,36 @@ lstm_status_t bwd_run(const lstm_desc_t* d, const void* x, const void* h0, const
     hipLaunchKernelGGL(bwd_block_rt<BF16>, dim3((H + 63) / 64, rs.nch), dim3(kBwdThreads), 0, st,
                        static_cast<const void*>(Rl), H, rs.nch, static_cast<uint4*>(RTf));
     CHECK(hipGetLastError());
-    for (int t = T - 1; t >= 0; --t) {
+    if (resident) {
+      const long nflag = (long)rs.nt16 * kFlagStride * 4 / 16;
+      hipLaunchKernelGGL(bwd_zero, dim3((unsigned)std::min<long>((nflag + kBwdThreads - 1) / kBwdThreads, 64)),
+                         dim3(kBwdThreads), 0, st, reinterpret_cast<uint4*>(w + o.flg), nflag);
+      CHECK(hipGetLastError());
+      BwdResParams P{};
+      P.RTf = static_cast<const uint4*>(RTf);
+      P.DPx = w + o.dpx;
+      P.xslot = (long long)rs.nbt * rs.nch * 2048 / (long long)s;
+      P.dY = dY;
+      P.gates = gates;
+      P.cs = cs;
+      P.c0 = c0 ? c0 + (size_t)l * B * H : nullptr;
+      P.dhT = dhT ? dhT + (size_t)l * B * H : nullptr;
+      P.dcT = dcT ? dcT + (size_t)l * B * H : nullptr;
+      P.dP = dP;
+      P.dPh = dPh;
+      P.dh0 = dh0 ? dh0 + (size_t)l * B * H : nullptr;
+      P.dc0 = dc0 ? dc0 + (size_t)l * B * H : nullptr;
+      P.flags = reinterpret_cast<int*>(w + o.flg);
+      P.err = reinterpret_cast<int*>(w + o.ctl);
+      P.timeout_ticks = kBwdTimeoutUs * clk_khz / 1000;
+      P.T = T, P.B = B, P.H = H, P.nch = rs.nch, P.wgs = rs.nt16;
+      P.grid = (rs.nt16 + 7) & ~7;
+      P.xcd_remap = 1;
+      void* args[] = {&P};
+      CHECK(hipLaunchCooperativeKernel(bwd_res_fn(res_nw), dim3(P.grid), dim3(64 * kBwdResWaves), args,
+                                       (unsigned)res_lds, st));
+    }
+    for (int t = T - 1; t >= 0 && !resident; --t) {
       StepArgs a;
       a.dY = dY + (size_t)t * B * H;
       a.dhp = t < T - 1 ? dhp : nullptr;
@@ -633,6 +728,14 @@ lstm_status_t bwd_run(const lstm_desc_t* d, const void* x, const void* h0, const
 using namespace lstm;
 
 extern "C" {
+
+lstm_status_t lstm_bwd_last_error(const void* ws, hipStream_t stream) {
+  if (!ws) return LSTM_ERR_WORKSPACE;
+  if (hipStreamSynchronize(stream) != hipSuccess) return LSTM_ERR_HIP;
+  int v = 0;
+  if (hipMemcpy(&v, ws, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess) return LSTM_ERR_HIP;
+  return v == 0 ? LSTM_OK : LSTM_ERR_BARRIER_TIMEOUT;
+}
 
 size_t lstm_bwd_workspace_size(const lstm_desc_t* d) {
   BwdLayout o;

@@ -56,6 +56,7 @@ def run_and_check(inp, dy, dhT, dcT, dev, what):
         vb = b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32)
         assert torch.equal(va, vb), "training forward must equal lstm_fwd"
     tp.backward()
+    assert sl.lstm_bwd_last_error(tp.bws) == sl.LSTM_OK
     got = tp.grads_f64()
     # the oracle sees the upstream gradients the GPU saw (rounded to fp32)
     f32 = lambda a: None if a is None else np.asarray(a, dtype=np.float32).astype(np.float64)  # noqa: E731
@@ -111,6 +112,17 @@ def test_gpu_backward_large_hidden(dev):
     dy, dhT, dcT = upstream(cfg, 821)
     say("backward H=4096 L=2 T=4 B=32 bf16")
     run_and_check(inp, dy, dhT, dcT, dev, "bwd H4096")
+
+
+# the on-chip recurrent chain (bf16 H = 4096, B <= 32): one column tile, a
+# ragged second tile, and no upstream state gradients (dh0 / dc0 still out)
+@pytest.mark.parametrize("B,states", [(16, True), (20, False), (32, False)])
+def test_gpu_backward_on_chip_chain(dev, B, states):
+    cfg = li.custom_config(1, 512, 4096, B, 5, "bf16", cfg_id=840 + B)
+    inp = li.make_inputs(cfg, random_state=True)
+    dy, dhT, dcT = upstream(cfg, 850 + B, with_states=states)
+    say(f"backward on-chip chain H=4096 L=1 T=5 B={B} states={states}")
+    run_and_check(inp, dy, dhT, dcT, dev, f"bwd chain H4096 B={B}")
 
 
 def test_gpu_backward_wavefront_and_layerwise_forward_agree(dev):
