@@ -231,6 +231,13 @@ lstm_rec_res_kernel(const RecParams P) {
       __syncthreads();
       if (!s_ok) return;
     }
+    // The pre-activations are needed in registers from here on: left alone
+    // the compiler moves their loads after the next pass's h loads, and the
+    // first gate phase then waits for those (loads complete in order).
+    if constexpr (kEarlyG) {
+#pragma unroll
+      for (int j = 0; j < NW; ++j) asm volatile("" : "+v"(gq[j]));
+    }
     stamp(t, 1);
 
     // a null h_{t-1} (t = 0 without h0) is zero: nothing to multiply
