@@ -429,7 +429,10 @@ struct BwdLayout {
 // 64 columns; 48 register and 16 LDS blocks per wave), at most two batch tiles.
 constexpr int kBwdResNCI = 64, kBwdResNRB = 48;
 bool bwd_resident_shape(const lstm_desc_t* d) {
-  return d->dtype == LSTM_BF16 && d->H == 4 * kBwdResNCI * 64 / 4 && d->B <= 32;
+  // (the kernel's exchange offsets are 32-bit: T slots of 2 batch tiles x 256
+  // chunks x 1024 elements stay below 2^31)
+  return d->dtype == LSTM_BF16 && d->H == 4 * kBwdResNCI * 64 / 4 && d->B <= 32 &&
+         (long long)d->T * 2 * (4 * d->H / 64) * 1024 < (1LL << 31);
 }
 
 const void* bwd_res_fn(int nw) {

@@ -130,13 +130,15 @@ lstm_bwd_res_kernel(const BwdResParams P) {
     if (t >= 0) {
 #pragma unroll
       for (int j = 0; j < NW; ++j) {
+        // (32-bit offsets from the arguments' base addresses: the host keeps
+        // T B 4H and every exchange offset below 2^31)
         const int b = min(16 * j + (tid & 15), B - 1);
-        const long bh = ((long)t * B + b) * H + unit, g4 = ((long)t * B + b) * 4 * H + unit;
+        const unsigned bh = (unsigned)(t * B + b) * H + unit, g4 = (unsigned)(t * B + b) * 4 * H + unit;
         in[j][0] = P.dY[bh];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) in[j][1 + k] = P.gates[g4 + (long)k * H];
+        for (int k = 0; k < 4; ++k) in[j][1 + k] = P.gates[g4 + (unsigned)(k * H)];
         in[j][5] = P.cs[bh];
-        in[j][6] = t > 0 ? P.cs[bh - (long)B * H] : (P.c0 ? P.c0[(long)b * H + unit] : 0.f);
+        in[j][6] = t > 0 ? P.cs[bh - (unsigned)(B * H)] : (P.c0 ? P.c0[(unsigned)(b * H + unit)] : 0.f);
       }
     }
     if (s > 0) {
@@ -204,7 +206,7 @@ lstm_bwd_res_kernel(const BwdResParams P) {
         for (int w = 0; w < KS; ++w) dhr += red[w * 64 + alane][arow];
       }
       if (live) {
-        const long bh = (long)b * H + unit;
+        const unsigned bh = (unsigned)(b * H + unit);
         if (t < 0) {
           if (P.dh0) P.dh0[bh] = dhr;
         } else {
@@ -217,18 +219,18 @@ lstm_bwd_res_kernel(const BwdResParams P) {
           const float d[4] = {dc * gg * ig * (1.f - ig), dc * cp * fg * (1.f - fg), dc * ig * (1.f - gg * gg),
                               dh * tc * og * (1.f - og)};
           dcrec[j] = dc * fg;
-          const long row = ((long)t * B + b) * 4 * H + unit;
-          T* xs = DPx + (long)t * P.xslot;
+          const unsigned row = (unsigned)(t * B + b) * 4 * H + unit;
+          // load order of dp_t: row b, column k H + unit (H is whole chunks,
+          // so the place inside a chunk is the same for the four gates)
+          const int kc = unit % KC, hh = kc / (KC / 2), qq = (kc % (KC / 2)) / EPH, e = kc % EPH;
+          const unsigned xo = (unsigned)t * (unsigned)P.xslot +
+                              ((unsigned)((b >> 4) * nch + unit / KC) * 2 + hh) * (FB / 2) + (qq * 16 + (b & 15)) * EPH + e;
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
             const T hv = from_float<BF16>(d[k]);
-            P.dP[row + (long)k * H] = d[k];
-            dPh[row + (long)k * H] = hv;
-            // load order of dp_t: row b, column k H + unit
-            const int col = k * H + unit, c = col / KC, kc = col % KC;
-            const int hh = kc / (KC / 2), qq = (kc % (KC / 2)) / EPH, e = kc % EPH;
-            store_coherent<BF16>(xs + (((long)(b >> 4) * nch + c) * 2 + hh) * (FB / 2) + (qq * 16 + (b & 15)) * EPH + e,
-                                 hv);
+            P.dP[row + (unsigned)(k * H)] = d[k];
+            dPh[row + (unsigned)(k * H)] = hv;
+            store_coherent<BF16>(DPx + xo + (unsigned)(k * (H / KC) * FB), hv);
           }
           if (t == 0 && P.dc0) P.dc0[bh] = dcrec[j];
         }
