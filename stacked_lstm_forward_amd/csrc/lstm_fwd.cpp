@@ -24,8 +24,9 @@ hipError_t rec_prepare(bool bf16, bool stream, bool vec, bool frag, int nwv, int
 hipError_t launch_clear(int* p, long long n, hipStream_t s);
 hipError_t launch_rec(bool bf16, bool stream, bool vec, bool frag, int nwv, const RecParams& p, int lds_bytes,
                       bool plain, hipStream_t s);
-hipError_t res_prepare(bool bf16, int mw, int nw, int nci, int nrb, int lds_bytes, int* max_blocks_per_cu);
+hipError_t res_prepare(bool bf16, int mw, int nw, int nci, int nrb, bool save, int lds_bytes, int* max_blocks_per_cu);
 hipError_t launch_rec_res(bool bf16, int nci, int nrb, const RecParams& p, int lds_bytes, bool plain, hipStream_t s);
+hipError_t launch_h0_frag(bool bf16, const void* h0, void* dst, int B, int H, long long tile_elems, hipStream_t s);
 }  // namespace lstm
 
 using namespace lstm;
@@ -388,7 +389,7 @@ lstm_status_t fwd_impl(const lstm_desc_t* d, const void* x, const void* h0, cons
     int per_cu = 0;
     const bool res = lp.res_nrb > 0;
     if (res && !vec) return LSTM_ERR_UNSUPPORTED;  // planned only for aligned rows
-    hipError_t pe = res ? res_prepare(bf16, lp.mw, lp.nw, lp.res_nci, lp.res_nrb, lp.lds_bytes, &per_cu)
+    hipError_t pe = res ? res_prepare(bf16, lp.mw, lp.nw, lp.res_nci, lp.res_nrb, reserve != nullptr, lp.lds_bytes, &per_cu)
                         : rec_prepare(bf16, lp.stream, vec, frag, lp.nwaves, lp.mw, lp.nw, lds, &per_cu);
     if (pe == hipSuccess && rp.sent && (long long)per_cu * dev.info.num_cus < lp.grid) {
       // the second reduction area costs co-residency: step counters instead
@@ -408,6 +409,12 @@ lstm_status_t fwd_impl(const lstm_desc_t* d, const void* x, const void* h0, cons
   auto rec = [&](const RecLaunch& rl) -> lstm_status_t {
     const LaunchPlan& lp = *rl.lp;
     if (!before(LSTM_KERNEL_RECURRENT)) return LSTM_ERR_HIP;
+    // the register-resident kernel reads h_{t-1} from load-order slot t: h0
+    // goes to slot 0 first (counted as part of the recurrence)
+    if (rl.res && rl.rp.layer[0].h0 &&
+        launch_h0_frag(bf16, rl.rp.layer[0].h0, rl.rp.layer[0].F, B, H, (long long)(H / p.KC) * (2048 / (long long)ds),
+                       stream) != hipSuccess)
+      return LSTM_ERR_HIP;
     const bool plain = opts && opts->plain_launch;
     const hipError_t le = rl.res ? launch_rec_res(bf16, lp.res_nci, lp.res_nrb, rl.rp, lp.lds_bytes, plain, stream)
                                  : launch_rec(bf16, lp.stream, rl.vec, rl.frag, lp.nwaves, rl.rp, rl.lds, plain, stream);

@@ -466,6 +466,24 @@ __global__ void __launch_bounds__(256) lstm_clear(int* p, long long n) {
   for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256) p[i] = 0;
 }
 
+// h0 of one layer, row-major [B][H], rewritten in the order the register-
+// resident kernel loads its recurrent operand (lstm_rec_res.h: for column tile
+// j and chunk c a block of FB elements, half hh at +FB/2, lane qq*16 + r at
+// +EPH (qq*16 + r)), so that its first step reads h0 like every later h_{t-1}.
+// Rows >= B of the last column tile are not written (their sums are never
+// finished).
+template <typename T, int KC>
+__global__ void __launch_bounds__(256) lstm_h0_frag(const T* __restrict__ h0, T* __restrict__ dst, int B, int H,
+                                                    long long tile_elems) {
+  constexpr int EPH = 16 / (int)sizeof(T), FB = 2048 / (int)sizeof(T);
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long long)B * H) return;
+  const int b = (int)(i / H), k = (int)(i % H);
+  const int c = k / KC, kc = k % KC;
+  const int hh = kc / (KC / 2), qq = (kc % (KC / 2)) / EPH, e = kc % EPH;
+  dst[(b >> 4) * tile_elems + (long long)c * FB + hh * (FB / 2) + (qq * 16 + (b & 15)) * EPH + e] = h0[i];
+}
+
 // ----------------------------------------------------------------------------
 // Host-side launchers (the only code outside this directory's kernels that
 // touches them).  The recurrent kernel's instantiations live in
@@ -476,17 +494,17 @@ LSTM_DECL(f32, lds, 4) LSTM_DECL(f32, stream, 4) LSTM_DECL(bf16, lds, 4) LSTM_DE
 LSTM_DECL(f32, lds, 8) LSTM_DECL(f32, stream, 8) LSTM_DECL(bf16, lds, 8) LSTM_DECL(bf16, stream, 8)
 #undef LSTM_DECL
 
-const void* rec_res_kernel_ptr_shape0(int nw);
-const void* rec_res_kernel_ptr_shape1(int nw);
-const void* rec_res_kernel_ptr_shape2(int nw);
+const void* rec_res_kernel_ptr_shape0(int nw, bool save);
+const void* rec_res_kernel_ptr_shape1(int nw, bool save);
+const void* rec_res_kernel_ptr_shape2(int nw, bool save);
 static_assert(kResShapes == 3, "one instantiation unit per resident shape");
 
-const void* rec_res_kernel_ptr(bool bf16, int mw, int nw, int nci, int nrb) {
-  const void* (*const per_shape[kResShapes])(int) = {rec_res_kernel_ptr_shape0, rec_res_kernel_ptr_shape1,
+const void* rec_res_kernel_ptr(bool bf16, int mw, int nw, int nci, int nrb, bool save) {
+  const void* (*const per_shape[kResShapes])(int, bool) = {rec_res_kernel_ptr_shape0, rec_res_kernel_ptr_shape1,
                                                       rec_res_kernel_ptr_shape2};
   for (int k = 0; k < kResShapes; ++k) {
     const ResShape& r = kResShape[k];
-    if ((r.bf16 != 0) == bf16 && r.mw == mw && r.nci == nci && r.nrb == nrb) return per_shape[k](nw);
+    if ((r.bf16 != 0) == bf16 && r.mw == mw && r.nci == nci && r.nrb == nrb) return per_shape[k](nw, save);
   }
   return nullptr;
 }
@@ -662,6 +680,18 @@ hipError_t launch_clear(int* p, long long n, hipStream_t s) {
   return hipGetLastError();
 }
 
+hipError_t launch_h0_frag(bool bf16, const void* h0, void* dst, int B, int H, long long tile_elems, hipStream_t s) {
+  const long long n = (long long)B * H;
+  const unsigned blocks = (unsigned)((n + 255) / 256);
+  if (bf16)
+    hipLaunchKernelGGL((lstm_h0_frag<uint16_t, 64>), dim3(blocks), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(h0), static_cast<uint16_t*>(dst), B, H, tile_elems);
+  else
+    hipLaunchKernelGGL((lstm_h0_frag<float, 32>), dim3(blocks), dim3(256), 0, s, static_cast<const float*>(h0),
+                       static_cast<float*>(dst), B, H, tile_elems);
+  return hipGetLastError();
+}
+
 hipError_t rec_prepare(bool bf16, bool stream, bool vec, bool frag, int nwv, int mw, int nw, int lds_bytes,
                        int* max_blocks_per_cu) {
   const void* fn = rec_kernel_fn(bf16, stream, vec, nwv, mw, nw, frag);
@@ -669,14 +699,14 @@ hipError_t rec_prepare(bool bf16, bool stream, bool vec, bool frag, int nwv, int
   return prepare_fn(fn, lds_bytes, 64 * nwv, max_blocks_per_cu);
 }
 
-hipError_t res_prepare(bool bf16, int mw, int nw, int nci, int nrb, int lds_bytes, int* max_blocks_per_cu) {
-  const void* fn = rec_res_kernel_ptr(bf16, mw, nw, nci, nrb);
+hipError_t res_prepare(bool bf16, int mw, int nw, int nci, int nrb, bool save, int lds_bytes, int* max_blocks_per_cu) {
+  const void* fn = rec_res_kernel_ptr(bf16, mw, nw, nci, nrb, save);
   if (!fn) return hipErrorInvalidValue;
   return prepare_fn(fn, lds_bytes, 64 * 4, max_blocks_per_cu);
 }
 
 hipError_t launch_rec_res(bool bf16, int nci, int nrb, const RecParams& p, int lds_bytes, bool plain, hipStream_t s) {
-  const void* fn = rec_res_kernel_ptr(bf16, p.mw, p.nw, nci, nrb);
+  const void* fn = rec_res_kernel_ptr(bf16, p.mw, p.nw, nci, nrb, p.layer[0].save_gates != nullptr);
   if (!fn) return hipErrorInvalidValue;
   void* args[] = {const_cast<RecParams*>(&p)};
   if (plain) return hipLaunchKernel(fn, dim3(p.grid), dim3(64 * 4), args, (unsigned)lds_bytes, s);

@@ -312,10 +312,11 @@ int make_plan(const int32_t L, const int32_t I, const int32_t H, const int32_t B
   p.slot_elems = slot_bytes / p.dsize;
   off += (size_t)L * T * slot_bytes;
   // one layer's load-order exchange for layerwise runs (the row-major slots
-  // above then feed the next layer's input GEMM); one set of T slots, reused
-  // layer after layer
+  // above then feed the next layer's input GEMM); one set of slots, reused
+  // layer after layer: T, plus one in front for the register-resident
+  // kernel's h0 (it reads slot t and writes slot t + 1)
   p.xf_off = off;
-  off += (size_t)T * slot_bytes;
+  off += (size_t)(T + 1) * slot_bytes;
   p.ws_bytes = off;
   return kStatusOk;
 }

@@ -18,13 +18,18 @@
 // wave has NCI chunks and all its offsets are compile-time constants.
 // Block b of a wave is (chunk index ci = b / MW, M-tile b % MW).  The last
 // LPC = (NB - NRB) / NCI M-tiles of every chunk live in LDS, the others in
-// registers: a chunk's LDS blocks are read while the previous chunk's products
-// run, so LDS latency stays hidden (with all LDS blocks in the last chunks,
+// registers.  A chunk's products take its LDS M-tiles first and then read the
+// next chunk's LDS blocks into the same registers, so each LDS read has three
+// register M-tiles' products to land (with all LDS blocks in the last chunks,
 // each read only one block ahead, those chunks stalled on LDS and a pass took
-// about twice its matrix-core time).  The NW column tiles are
-// done one after the other (MW accumulators and one h fragment per chunk in
+// about twice its matrix-core time; two buffers read a whole chunk ahead cost
+// the registers a deeper h ring needs more).  The NW column tiles are done
+// one after the other (MW accumulators and one h fragment per chunk in
 // registers); after each, the four K-groups' partial sums meet in LDS and
-// K-group i finishes M-tile i of that column tile.
+// K-group i finishes M-tile i of that column tile.  Multiplying both tiles of
+// B = 32 in one pass (each weight block feeding two accumulators) was
+// measured no faster: the passes are bound by how many h loads each wave
+// keeps in flight, not by the hand-over between tiles.
 //
 // Exchange layout.  A wave's load of one fragment half touches 16 batch rows
 // of h; from a row-major [B][H] buffer that is 16 pieces of 64 bytes 2H bytes
@@ -34,10 +39,15 @@
 // +1 KiB, lane l's 16 bytes at +16 l:
 //     Xf[t][((j * nch + c) * 2 + h) * 64 + lane][8 bf16]
 // and every load instruction of a step reads 1 KiB in one piece.  The row-major
-// copy (the next layer's input, or y) is still written; step 0 reads the
-// caller's row-major h0.
+// copy (the next layer's input, or y) is still written.  Step t reads slot t
+// and writes slot t + 1; slot 0 holds h0, rewritten in this order before the
+// launch (lstm_h0_frag), so every step takes the same path.  The loads are
+// buffer loads whose only per-lane operand is one 32-bit offset: tile, chunk
+// and half are compile-time offsets, which keeps registers for the ring.
 // The step protocol (write-through stores, step counters, bounded waits) is the
-// one of lstm_rec_kernel.
+// one of lstm_rec_kernel.  SAVE adds the training forward's stores (gates,
+// cell and hidden states of every step); without them the inference kernel
+// has the registers for one more chunk of h loads in flight.
 #pragma once
 
 #include "lstm_rec.h"
@@ -80,7 +90,7 @@ struct ResOps<false> {
   }
 };
 
-template <bool BF16, int MW, int NW, int NCI, int NRB>
+template <bool BF16, int MW, int NW, int NCI, int NRB, bool SAVE>
 __global__ void __launch_bounds__(64 * kResWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
 lstm_rec_res_kernel(const RecParams P) {
   typedef typename Dt<BF16>::T T;
@@ -91,9 +101,13 @@ lstm_rec_res_kernel(const RecParams P) {
   constexpr int LPC = NLB / NCI;   // LDS M-tiles per chunk
   constexpr int RPC = MW - LPC;    // register M-tiles per chunk
   static_assert(NLB % NCI == 0, "LDS blocks spread evenly over the chunks");
-  // chunks of h loads in flight (H = 4096, B = 32: 2 -> 0.51 ms per layer, 4 -> 0.42, 6 no better;
-  // 3 with more than two column tiles, whose per-tile state takes the registers)
-  constexpr int PD = NW <= 2 ? 4 : 3;
+  // h load chunks in flight per wave (bf16 H = 4096, B = 32: 2 -> 0.51 ms per
+  // layer, 4 -> 0.42 (later 0.356), 5 -> 0.342 once the addressing and the
+  // single LDS buffer below freed the registers, 6 spills; 3 with more than
+  // two column tiles, whose per-tile state takes the registers).  A shape
+  // with at most 36 register blocks has registers for a deeper ring.
+  constexpr bool kRoomy = BF16 && NRB <= 36;
+  constexpr int PD = kRoomy ? (NW <= 2 ? 8 : 6) : (NW <= 2 ? 5 : 3);
   static_assert(NRB >= 0 && NRB <= NB, "register blocks");
   static_assert(MW <= KS, "one finishing K-group per M-tile");
   extern __shared__ __align__(16) unsigned char smem[];
@@ -120,9 +134,6 @@ lstm_rec_res_kernel(const RecParams P) {
   bool mval[MW];
   long arow[MW];
   uint32_t mr_[MW];
-  // element offsets of this lane's two fragment halves of its first chunk:
-  // row-major (h0) and fragment order (Xf); chunk ci adds ci * KS * KC, resp. ci * KS * FB
-  uint32_t hrm[NW][2], hfr[NW][2];
 #pragma unroll
   for (int i = 0; i < MW; ++i) {
     mval[i] = i < mcnt;
@@ -130,14 +141,10 @@ lstm_rec_res_kernel(const RecParams P) {
     mr_[i] = (mval[i] && cr.r >= 0) ? 0xffffffffu : 0u;
     arow[i] = cr.r >= 0 ? cr.r : 0;
   }
-#pragma unroll
-  for (int j = 0; j < NW; ++j) {
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      hrm[j][hh] = min(16 * j + (lane & 15), B - 1) * H + kg * KC + frag_col<BF16>(q, hh);
-      hfr[j][hh] = (j * NCH + kg) * FB + hh * (FB / 2) + lane * EPH;
-    }
-  }
+  // byte offset of this lane's 16 bytes in its first block of a slot; tile j,
+  // chunk slot ci and half hh add the compile-time (j NCH + ci KS) FB + hh FB/2
+  // elements, so every h load of a step takes this one register
+  const int hlane = (kg * FB + lane * EPH) * Dt<BF16>::SZ;
 
   // ---- this wave's weight blocks: M-tile i < RPC of chunk slot ci is
   // register block ci * RPC + i, M-tile i >= RPC is LDS block ci * LPC + i - RPC
@@ -240,11 +247,11 @@ lstm_rec_res_kernel(const RecParams P) {
     }
     stamp(t, 1);
 
-    // a null h_{t-1} (t = 0 without h0) is zero: nothing to multiply
-    const bool fr = t > 0;
-    const T* hsrc = fr ? Xf + (long)(t - 1) * P.fslot : h0p;
-    const long cstride = fr ? KS * FB : KS * KC;
-    T* fout = Xf + (long)t * P.fslot;
+    // h_{t-1} is load-order slot t (slot 0: h0, written there before the
+    // launch); a null h0 is zero: nothing to multiply at t = 0
+    const T* hsrc = (t > 0 || h0p) ? Xf + (long)t * P.fslot : nullptr;
+    const __amdgpu_buffer_rsrc_t hrs = raw_buffer(hsrc, (int)(P.fslot * Dt<BF16>::SZ));
+    T* fout = Xf + (long)(t + 1) * P.fslot;
     // row-major copy: y for the top layer, else the next layer's input
     T* rout = Lr.Yout ? reinterpret_cast<T*>(Lr.Yout) + (long)t * B * H : Xp + (long)t * slot;
     // (the host gives every resident layer either y or a row-major X)
@@ -255,14 +262,26 @@ lstm_rec_res_kernel(const RecParams P) {
     // tile's sums are combined and its gates computed.  Load g is chunk slot
     // g % NCI of column tile g / NCI.
     Frag rb[PD];
-    // a chunk's LDS blocks are read one chunk ahead into the other of two
-    // buffers (the next tile's first chunk during this tile's last one)
-    Frag al[2][LPC > 0 ? LPC : 1];
+    // One LDS buffer: a chunk's products take its LDS M-tiles first, and the
+    // next chunk's LDS blocks are read into the same registers right after
+    // them, three register M-tiles (six products) ahead of their use.  With
+    // three column tiles two buffers, the next chunk's blocks read a whole
+    // chunk ahead, time the same and are kept; with four, one buffer and
+    // ordinary loads (below) spill least and run fastest.
+    constexpr bool kLdsAhead = NW == 3;
+    Frag al[kLdsAhead ? 2 : 1][LPC > 0 ? LPC : 1];
     auto issue = [&](Frag& dst, int g) {
-      const int jj = g / NCI, ci = g % NCI;
-      const T* pc = hsrc + ci * cstride;
-      dst.v[0] = *reinterpret_cast<const uint4*>(pc + (fr ? hfr[jj][0] : hrm[jj][0]));
-      dst.v[1] = *reinterpret_cast<const uint4*>(pc + (fr ? hfr[jj][1] : hrm[jj][1]));
+      const int o = ((g / NCI) * NCH + (g % NCI) * KS) * FB * Dt<BF16>::SZ;
+      if constexpr (NW == 4) {
+        // (four column tiles: ordinary loads measured faster, 0.75 against
+        // 0.88 ms per layer at bf16 H = 4096, B = 64)
+        const char* pc = reinterpret_cast<const char*>(hsrc) + o + hlane;
+        dst.v[0] = *reinterpret_cast<const uint4*>(pc);
+        dst.v[1] = *reinterpret_cast<const uint4*>(pc + 1024);
+      } else {
+        dst.v[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(hrs, hlane, o, 0));
+        dst.v[1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(hrs, hlane, o + 1024, 0));
+      }
     };
     if (hsrc) {
 #pragma unroll
@@ -281,13 +300,23 @@ lstm_rec_res_kernel(const RecParams P) {
 #pragma unroll
         for (int ci = 0; ci < NCI; ++ci) {
           const int g = j * NCI + ci, s = g % PD;
-          if (ci + 1 < NCI || j + 1 < NW) {
-            const int cn = (ci + 1) % NCI;
+          if constexpr (kLdsAhead) {
+            if (ci + 1 < NCI || j + 1 < NW) {
+              const int cn = (ci + 1) % NCI;
 #pragma unroll
-            for (int e = 0; e < LPC; ++e) al[cn & 1][e] = lds_get(As + (cn * LPC + e) * 128, lane);
+              for (int e = 0; e < LPC; ++e) al[cn & 1][e] = lds_get(As + (cn * LPC + e) * 128, lane);
+            }
           }
 #pragma unroll
-          for (int i = 0; i < MW; ++i) {
+          for (int ii = 0; ii < MW; ++ii) {
+            const int i = kLdsAhead ? ii : (ii + RPC) % MW;  // one buffer: the LDS M-tiles (i >= RPC) first
+            if constexpr (!kLdsAhead) {
+              if (ii == LPC && (ci + 1 < NCI || j + 1 < NW)) {
+                const int cn = (ci + 1) % NCI;
+#pragma unroll
+                for (int e = 0; e < LPC; ++e) al[0][e] = lds_get(As + (cn * LPC + e) * 128, lane);
+              }
+            }
             // no branch: a missing M-tile has zero weights and a missing
             // column tile a clamped h row; their sums are never finished
             const V x0 = Ops::cast(rb[s].v[0]), x1 = Ops::cast(rb[s].v[1]);
@@ -296,8 +325,8 @@ lstm_rec_res_kernel(const RecParams P) {
               a0 = wreg[ci * RPC + (i < RPC ? i : 0)].h[0];
               a1 = wreg[ci * RPC + (i < RPC ? i : 0)].h[1];
             } else {
-              a0 = Ops::cast(al[ci & 1][i < RPC ? 0 : i - RPC].v[0]);
-              a1 = Ops::cast(al[ci & 1][i < RPC ? 0 : i - RPC].v[1]);
+              a0 = Ops::cast(al[kLdsAhead ? (ci & 1) : 0][i < RPC ? 0 : i - RPC].v[0]);
+              a1 = Ops::cast(al[kLdsAhead ? (ci & 1) : 0][i < RPC ? 0 : i - RPC].v[1]);
             }
             // one accumulator's products back to back (bf16: a pair issues
             // every 16.9 cycles, alternating accumulators every 22.9, which
@@ -331,11 +360,13 @@ lstm_rec_res_kernel(const RecParams P) {
           store_coherent<BF16>(fout + fo + u, hv);
           rout[o + u] = hv;
           if (last && Lr.hT) reinterpret_cast<T*>(Lr.hT)[o + u] = hv;
-          if (Lr.save_h) reinterpret_cast<T*>(Lr.save_h)[(long)t * B * H + o + u] = hv;
+          if constexpr (SAVE) reinterpret_cast<T*>(Lr.save_h)[(long)t * B * H + o + u] = hv;
         });
         if (cell == kCellLstm && last && Lr.cT) Lr.cT[o] = st[j];
-        if (cell == kCellLstm && Lr.save_gates)
-          save_lstm_step(Lr.save_gates, Lr.save_c, p, st[j], t, B, H, 16 * j + (lane & 15), funit);
+        if constexpr (SAVE) {
+          if (cell == kCellLstm)
+            save_lstm_step(Lr.save_gates, Lr.save_c, p, st[j], t, B, H, 16 * j + (lane & 15), funit);
+        }
       }
       // the next column tile reuses the partial-sum area
       if (j + 1 < NW) __syncthreads();

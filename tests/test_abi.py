@@ -134,8 +134,9 @@ def test_workspace_size_formula():
         # tiles x 16 x KC chunks), whichever is larger, from a 256-byte boundary
         elems = max(c.B * c.H, -(-c.B // 16) * 16 * -(-c.H // kc) * kc)
         slot = -(-elems * ds // 256) * 256
-        # L x T exchange slots, plus T slots of one layer's load-order exchange
-        expect = 256 + c.L * 1024 * 128 + c.T * mt * c.B * 16 * 4 + c.L * c.T * slot + c.T * slot
+        # L x T exchange slots, plus T + 1 slots of one layer's load-order
+        # exchange (slot 0: h0 for the register-resident kernel)
+        expect = 256 + c.L * 1024 * 128 + c.T * mt * c.B * 16 * 4 + c.L * c.T * slot + (c.T + 1) * slot
         assert expect <= n <= expect + 4 * 256, (name, n, expect)
 
 
