@@ -272,8 +272,9 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_colsum_final(const float* par
 
 // R_l^T in load order: element (n, k) = R_l[k][n] for n < H, k < 4H, zero in
 // the padding.  Workgroup (x, c): columns n of R 64 x .. 64 x + 63 and rows k
-// of chunk c, through an LDS tile.
-template <bool BF16>
+// of chunk c, through an LDS tile.  UNIT_MAJOR orders K as k = 4 u + g (gate g
+// of unit u, row g H + u of R_l), the order of the on-chip chain's exchange.
+template <bool BF16, bool UNIT_MAJOR>
 __global__ void __launch_bounds__(kBwdThreads) bwd_block_rt(const void* R, int H, int nch, uint4* out) {
   typedef typename Dt<BF16>::T T;
   constexpr int KC = Dt<BF16>::KC, EPH = KC / 8;
@@ -282,7 +283,8 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_block_rt(const void* R, int H
   const T* Rp = static_cast<const T*>(R);
   for (int i = threadIdx.x; i < KC * 64; i += kBwdThreads) {
     const int kr = i / 64, nc = i % 64, k = c * KC + kr, n = n0 + nc;
-    tile[kr][nc] = (k < G && n < H) ? Rp[(long)k * H + n] : T(0);
+    const long row = UNIT_MAJOR ? (long)(k % 4) * H + k / 4 : (long)k;
+    tile[kr][nc] = (k < G && n < H) ? Rp[row * H + n] : T(0);
   }
   __syncthreads();
   // 4 row tiles x 2 halves x 64 lanes of 16 bytes
@@ -420,24 +422,27 @@ RecShape rec_shape(int B, int H, bool bf16) {
 }
 
 struct BwdLayout {
-  size_t ctl, flg, dpx, rtf, dpf, wt, dp, dph, dpt, ut, ht, dy0, dy1, dhp, dcrec, colp, total;
+  size_t ctl, flg, dpx, prt, rtf, dpf, wt, dp, dph, dpt, ut, ht, dy0, dy1, dhp, dcrec, colp, total;
   RecShape rs;
   bool resident;  // the chain runs in lstm_bwd_res_kernel
 };
 
 // The on-chip chain kernel's shape: bf16, H = 4096 (4 K-groups of 64 chunks of
 // 64 columns; 48 register and 16 LDS blocks per wave), at most two batch tiles.
-constexpr int kBwdResNCI = 64, kBwdResNRB = 48;
+// The on-chip chain's shape: bf16, H = 4 waves x 16 chunks x 64 (each
+// workgroup's K quarter), one or two batch tiles; 4 H / 16 workgroups.
 bool bwd_resident_shape(const lstm_desc_t* d) {
-  // (the kernel's exchange offsets are 32-bit: T slots of 2 batch tiles x 256
-  // chunks x 1024 elements stay below 2^31)
-  return d->dtype == LSTM_BF16 && d->H == 4 * kBwdResNCI * 64 / 4 && d->B <= 32 &&
-         (long long)d->T * 2 * (4 * d->H / 64) * 1024 < (1LL << 31);
+  // (the kernel's exchange and partial-sum offsets are 32-bit: T slots of 2
+  // batch tiles x 256 chunks x 1024 elements, and T + 1 slots of 2^19
+  // partial sums, stay below 2^31)
+  return d->dtype == LSTM_BF16 && d->H == kBwdResWaves * kBwdResNCI * 64 && d->B <= 32 &&
+         (long long)(d->T + 1) * 2 * (4 * d->H / 64) * 1024 < (1LL << 31);
 }
+int bwd_res_wgs(int H) { return 4 * (H / 64); }
 
 const void* bwd_res_fn(int nw) {
-  return nw == 1 ? reinterpret_cast<const void*>(&lstm_bwd_res_kernel<true, 1, kBwdResNCI, kBwdResNRB>)
-                 : reinterpret_cast<const void*>(&lstm_bwd_res_kernel<true, 2, kBwdResNCI, kBwdResNRB>);
+  return nw == 1 ? reinterpret_cast<const void*>(&lstm_bwd_res_kernel<true, 1>)
+                 : reinterpret_cast<const void*>(&lstm_bwd_res_kernel<true, 2>);
 }
 
 // Compute units and wall-clock rate (kHz) of the current device, once per device.
@@ -482,8 +487,11 @@ bool bwd_layout(const lstm_desc_t* d, BwdLayout* o) {
     return at;
   };
   o->ctl = take(256);  // the error word first, as in the forward's workspace
-  o->flg = take(o->resident ? (size_t)o->rs.nt16 * kFlagStride * 4 : 0);
+  // the on-chip chain: two sets of step counters, the dp exchange, the partial sums
+  const int rwgs = bwd_res_wgs(d->H);
+  o->flg = take(o->resident ? (size_t)2 * rwgs * kFlagStride * 4 : 0);
   o->dpx = take(o->resident ? (size_t)d->T * o->rs.nbt * o->rs.nch * 2048 : 0);
+  o->prt = take(o->resident ? (size_t)(d->T + 1) * bwd_res_part_floats(rwgs, o->rs.nbt) * 4 : 0);
   o->rtf = take((size_t)o->rs.nt16 * o->rs.nch * 2048);
   o->dpf = take((size_t)o->rs.nbt * o->rs.nch * 2048);
   o->wt = take(Imax * G * s);
@@ -601,11 +609,12 @@ lstm_status_t bwd_run(const lstm_desc_t* d, const void* x, const void* h0, const
   CHECK(bwd_device(&cus, &clk_khz));
   bool resident = o.resident;
   const int res_nw = (B + 15) / 16;
-  const int res_lds = bwd_res_lds_bytes(kBwdResNCI, kBwdResNRB, res_nw);
+  const int res_lds = bwd_res_lds_bytes(res_nw);
+  const int res_wgs = bwd_res_wgs(H);
   if (resident) {
     int per_cu = 0;
     if (prepare_fn(bwd_res_fn(res_nw), res_lds, 64 * kBwdResWaves, &per_cu) != hipSuccess ||
-        (long)per_cu * cus < rs.nt16) {
+        (long)per_cu * cus < res_wgs) {
       (void)hipGetLastError();
       resident = false;
     }
@@ -628,11 +637,16 @@ lstm_status_t bwd_run(const lstm_desc_t* d, const void* x, const void* h0, const
     const float* cs = reinterpret_cast<const float*>(rsv + (size_t)L * tbh * 16 + (size_t)l * tbh * 4);
     const char* hs = rsv + (size_t)L * tbh * 20 + (size_t)l * tbh * s;
     // R_l^T in load order: the per-step product's streamed operand
-    hipLaunchKernelGGL(bwd_block_rt<BF16>, dim3((H + 63) / 64, rs.nch), dim3(kBwdThreads), 0, st,
-                       static_cast<const void*>(Rl), H, rs.nch, static_cast<uint4*>(RTf));
+    // (K unit-major for the on-chip chain)
+    if (resident)
+      hipLaunchKernelGGL((bwd_block_rt<BF16, true>), dim3((H + 63) / 64, rs.nch), dim3(kBwdThreads), 0, st,
+                         static_cast<const void*>(Rl), H, rs.nch, static_cast<uint4*>(RTf));
+    else
+      hipLaunchKernelGGL((bwd_block_rt<BF16, false>), dim3((H + 63) / 64, rs.nch), dim3(kBwdThreads), 0, st,
+                         static_cast<const void*>(Rl), H, rs.nch, static_cast<uint4*>(RTf));
     CHECK(hipGetLastError());
     if (resident) {
-      const long nflag = (long)rs.nt16 * kFlagStride * 4 / 16;
+      const long nflag = (long)2 * res_wgs * kFlagStride * 4 / 16;
       hipLaunchKernelGGL(bwd_zero, dim3((unsigned)std::min<long>((nflag + kBwdThreads - 1) / kBwdThreads, 64)),
                          dim3(kBwdThreads), 0, st, reinterpret_cast<uint4*>(w + o.flg), nflag);
       CHECK(hipGetLastError());
@@ -650,11 +664,13 @@ lstm_status_t bwd_run(const lstm_desc_t* d, const void* x, const void* h0, const
       P.dPh = dPh;
       P.dh0 = dh0 ? dh0 + (size_t)l * B * H : nullptr;
       P.dc0 = dc0 ? dc0 + (size_t)l * B * H : nullptr;
-      P.flags = reinterpret_cast<int*>(w + o.flg);
+      P.part = reinterpret_cast<float*>(w + o.prt);
+      P.flags_d = reinterpret_cast<int*>(w + o.flg);
+      P.flags_p = P.flags_d + (long)res_wgs * kFlagStride;
       P.err = reinterpret_cast<int*>(w + o.ctl);
       P.timeout_ticks = kBwdTimeoutUs * clk_khz / 1000;
-      P.T = T, P.B = B, P.H = H, P.nch = rs.nch, P.wgs = rs.nt16;
-      P.grid = (rs.nt16 + 7) & ~7;
+      P.T = T, P.B = B, P.H = H, P.nch = rs.nch, P.wgs = res_wgs;
+      P.grid = (res_wgs + 7) & ~7;
       P.xcd_remap = 1;
       void* args[] = {&P};
       CHECK(hipLaunchCooperativeKernel(bwd_res_fn(res_nw), dim3(P.grid), dim3(64 * kBwdResWaves), args,
