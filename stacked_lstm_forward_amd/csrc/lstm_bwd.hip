@@ -38,7 +38,7 @@ namespace lstm {
 // lstm_kernels.hip
 hipError_t prepare_fn(const void* fn, int lds_bytes, int block, int* blocks_per_cu);
 hipError_t launch_gemm_plain(bool bf16, const void* A, const void* B, float* C, long long ldc, int M, int N, int K,
-                             int num_cus, hipStream_t s);
+                             int num_cus, float* C2, long long c2_floats, hipStream_t s);
 
 namespace {
 
@@ -422,7 +422,7 @@ RecShape rec_shape(int B, int H, bool bf16) {
 }
 
 struct BwdLayout {
-  size_t ctl, flg, dpx, prt, rtf, dpf, wt, dp, dph, dpt, ut, ht, dy0, dy1, dhp, dcrec, colp, total;
+  size_t ctl, flg, dpx, prt, rtf, dpf, wt, dp, dph, dpt, ut, ht, dy0, dy1, dhp, dcrec, colp, spl, total;
   RecShape rs;
   bool resident;  // the chain runs in lstm_bwd_res_kernel
 };
@@ -505,6 +505,7 @@ bool bwd_layout(const lstm_desc_t* d, BwdLayout* o) {
   o->dhp = take((size_t)o->rs.S * B * H * 4);
   o->dcrec = take(B * H * 4);
   o->colp = take((TB + kColSlab - 1) / kColSlab * G * 4);
+  o->spl = take(TB * Imax * 4);  // one K range's partial sums of the input-gradient product
   o->total = off;
   return true;
 }
@@ -566,8 +567,9 @@ hipError_t rec_product(const RecShape& r, const void* RTf, const void* DPf, floa
 // C = A B^T (see gemm_nt) on the direct-to-LDS kernel when the operands suit
 // it (K-contiguous rows of whole chunks, 16-byte aligned), else gemm_nt.
 template <bool BF16>
-hipError_t big_product(const void* A, const void* Bm, float* C, long ldc, int M, int N, int K, hipStream_t st) {
-  const hipError_t e = launch_gemm_plain(BF16, A, Bm, C, ldc, M, N, K, 0, st);
+hipError_t big_product(const void* A, const void* Bm, float* C, long ldc, int M, int N, int K, float* spare,
+                       long long spare_floats, hipStream_t st) {
+  const hipError_t e = launch_gemm_plain(BF16, A, Bm, C, ldc, M, N, K, 0, spare, spare_floats, st);
   if (e != hipErrorNotSupported) return e;
   return gemm_nt<BF16, kBigWM, kBigWN>(A, K, Bm, K, C, ldc, 0, M, N, K, 1, st);
 }
@@ -594,6 +596,8 @@ lstm_status_t bwd_run(const lstm_desc_t* d, const void* x, const void* h0, const
   float* dhp = reinterpret_cast<float*>(w + o.dhp);
   float* dcrec = reinterpret_cast<float*>(w + o.dcrec);
   float* colp = reinterpret_cast<float*>(w + o.colp);
+  float* spl = reinterpret_cast<float*>(w + o.spl);  // partial sums of split products
+  const long long spl_floats = (long long)TB * std::max(I, H);
   const char* rsv = static_cast<const char*>(reserve);
   const size_t tbh = (size_t)T * B * H;
   const float* dY = dy;
@@ -726,13 +730,13 @@ lstm_status_t bwd_run(const lstm_desc_t* d, const void* x, const void* h0, const
     const void* h0l = h0 ? static_cast<const char*>(h0) + (size_t)l * B * H * s : nullptr;
     CHECK(transpose<BF16>(hs, H, h0l, H, B, (int)TB, H, HT, TB, st));  // row t*B+b: h_{t-1}[b] (h0 at t = 0)
     float* dWl = dW + (l == 0 ? 0 : (G * I + (size_t)(l - 1) * G * H));
-    CHECK(big_product<BF16>(dPT, UT, dWl, Il, (int)G, Il, (int)TB, st));
-    CHECK(big_product<BF16>(dPT, HT, dR + (size_t)l * G * H, H, (int)G, H, (int)TB, st));
+    CHECK(big_product<BF16>(dPT, UT, dWl, Il, (int)G, Il, (int)TB, spl, spl_floats, st));
+    CHECK(big_product<BF16>(dPT, HT, dR + (size_t)l * G * H, H, (int)G, H, (int)TB, spl, spl_floats, st));
     if (l > 0 || dx) {
       // dU = dP W_l: the layer below's dY, or dx
       CHECK(transpose<BF16>(Wl, Il, nullptr, 0, 0, (int)G, Il, WT, G, st));
       float* dU = l > 0 ? dYbuf[next] : dx;
-      CHECK(big_product<BF16>(dPh, WT, dU, Il, (int)TB, Il, (int)G, st));
+      CHECK(big_product<BF16>(dPh, WT, dU, Il, (int)TB, Il, (int)G, spl, spl_floats, st));
       dY = dU;
       next ^= 1;
     }

@@ -278,8 +278,11 @@ __global__ void __launch_bounds__(kDmaThreads) lstm_input_gemm_dma(const GemmPar
   const int nN = (P.N + NT * 16 - 1) / (NT * 16);
   const int total = nM * nN;
   const int per_xcd = (int)gridDim.x >> 3;
-  const int v = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  if (v >= total) return;
+  const int vs = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  // plain products may split K: workgroup vs takes chunk range vs / total
+  const int ks = (PLAIN && P.ksplit > 1) ? P.ksplit : 1;
+  if (vs >= total * ks) return;
+  const int z = vs / total, v = vs % total;
   constexpr int kGroupM = 4;
   const int in_group = kGroupM * nN;
   const int first_m = (v / in_group) * kGroupM;
@@ -288,7 +291,8 @@ __global__ void __launch_bounds__(kDmaThreads) lstm_input_gemm_dma(const GemmPar
   const int nblk = (v % in_group) / gsize;
   const int mtb = mblk * kDmaTiles;                  // first M-tile
   const long n0 = (long)nblk * NT * 16;              // first column
-  const int nch = P.K / KC;
+  const int c_first = z * (P.K / KC) / ks;           // this workgroup's chunk range of K
+  const int nch = (z + 1) * (P.K / KC) / ks - c_first;
 
   // Staging.  A block holds its 16 rows' 128-byte chunks row by row, 8 pieces
   // of 16 bytes each, piece p of row r in slot p ^ ((r >> 1) & 7).  One
@@ -300,8 +304,8 @@ __global__ void __launch_bounds__(kDmaThreads) lstm_input_gemm_dma(const GemmPar
   // Wave w loads W load-slots w*kDmaALoads + k and U load-slots w*kDmaBLoads + k
   // (slot j: block j/2, half j%2; U slots past 2 NT repeat the last one).
   constexpr int EPH = 16 / Dt<BF16>::SZ;  // elements of one 16-byte piece
-  const T* Wg = reinterpret_cast<const T*>(P.W);
-  const T* Ug = reinterpret_cast<const T*>(P.U);
+  const T* Wg = reinterpret_cast<const T*>(P.W) + (long)c_first * KC;
+  const T* Ug = reinterpret_cast<const T*>(P.U) + (long)c_first * KC;
   uint32_t srcA[kDmaALoads], srcB[kDmaBLoads];  // byte offsets (the launcher keeps them below 2^32)
   uint32_t dstA[kDmaALoads], dstB[kDmaBLoads];  // byte offsets inside a stage (wave-uniform)
 #pragma unroll
@@ -413,6 +417,7 @@ __global__ void __launch_bounds__(kDmaThreads) lstm_input_gemm_dma(const GemmPar
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the last (redundant) loads have landed
 
   if constexpr (PLAIN) {
+    float* const C = z == 0 ? P.C : P.C2 + (long)(z - 1) * P.split_stride;
 #pragma unroll
     for (int i = 0; i < WM; ++i) {
       const int mt = mtb + WM * wm + i;
@@ -423,7 +428,7 @@ __global__ void __launch_bounds__(kDmaThreads) lstm_input_gemm_dma(const GemmPar
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int row = 16 * mt + 4 * q + k;
-          if (row < P.H) P.C[(long)row * P.ldc + col] = acc[i][j][k];
+          if (row < P.H) C[(long)row * P.ldc + col] = acc[i][j][k];
         }
       }
     }
@@ -456,6 +461,19 @@ __global__ void __launch_bounds__(kDmaThreads) lstm_input_gemm_dma(const GemmPar
       for (int k = 0; k < 4; ++k) g[k] = wrow[k] ? acc[i][j][k] + bv[k] : bv[k];
       *reinterpret_cast<f32x4*>(dst) = g;
     }
+  }
+}
+
+// C[m][n] += C2[z S + m ldc + n] for z = 0 .. parts - 1, in that order: the
+// partial sums of a plain product whose K range was split.
+__global__ void __launch_bounds__(256) gemm_split_sum(float* C, const float* C2, long long S, int parts, int M, int N,
+                                                      long long ldc) {
+  const long long n = (long long)M * N;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256) {
+    const long long o = (i / N) * ldc + i % N;
+    float v = C[o];
+    for (int z = 0; z < parts; ++z) v += C2[z * S + o];
+    C[o] = v;
   }
 }
 
@@ -611,6 +629,7 @@ hipError_t launch_dma(bool bf16, const GemmParams& p, hipStream_t s) {
     return (nM * ((p.N + nt * 16 - 1) / (nt * 16)) + cus - 1) / cus;
   };
   int nt = rounds(14) * (kDmaTiles + 14) < rounds(16) * (kDmaTiles + 16) ? 14 : 16;
+  if (p.ksplit > 1) nt = 16;  // (the split was chosen for 16)
   auto kernel_of = [&](int n) { return dma_kernel(bf16, n, p.C != nullptr); };
   const void* fn = kernel_of(nt);
   // 16 column tiles take all 160 KiB of a CU's LDS; a device that gives a
@@ -624,7 +643,7 @@ hipError_t launch_dma(bool bf16, const GemmParams& p, hipStream_t s) {
   }
   if (e != hipSuccess) return e;
   const unsigned lds = dma_lds_bytes(nt);
-  const int tiles = ((p.N + nt * 16 - 1) / (nt * 16)) * nM;
+  const int tiles = ((p.N + nt * 16 - 1) / (nt * 16)) * nM * (p.ksplit > 1 ? p.ksplit : 1);
   const dim3 grid((tiles + 7) & ~7);  // a multiple of the 8 XCDs (extra workgroups only help zeroing)
   void* args[] = {const_cast<GemmParams*>(&p)};
   return hipLaunchKernel(fn, grid, dim3(kDmaThreads), args, lds, s);
@@ -659,7 +678,7 @@ hipError_t launch_input_gemm(bool bf16, const GemmParams& p, hipStream_t s) {
 // the direct-to-LDS kernel.  hipErrorNotSupported when the operands do not
 // suit it (the caller then uses another kernel); nothing is enqueued then.
 hipError_t launch_gemm_plain(bool bf16, const void* A, const void* B, float* C, long long ldc, int M, int N, int K,
-                             int num_cus, hipStream_t s) {
+                             int num_cus, float* C2, long long c2_floats, hipStream_t s) {
   const long long esz = bf16 ? 2 : 4;
   auto al16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
   GemmParams p{};
@@ -670,7 +689,25 @@ hipError_t launch_gemm_plain(bool bf16, const void* A, const void* B, float* C, 
   p.cell = kCellRnnTanh;
   p.num_cus = num_cus;
   if (M < 1 || N < 1 || K < 1 || !dma_fits(bf16, p)) return hipErrorNotSupported;
-  return launch_dma(bf16, p, s);
+  // A product of few 256 x 256 tiles with a long K (the input gradient
+  // dP W_l: 1600 x 4096 x 16384 makes 112 tiles on 256 CUs) splits K so the
+  // tiles fill the chip: ranges of at least 16 chunks, as many as the spare
+  // buffer holds, the partial sums added in order afterwards.
+  const int cus = num_cus > 0 ? num_cus : 256;
+  const int tiles16 = ((p.Mt + kDmaTiles - 1) / kDmaTiles) * ((N + 255) / 256);
+  const int nch = K / (bf16 ? Dt<true>::KC : Dt<false>::KC);
+  const long long cfl = (long long)M * ldc;
+  int ks = 1;
+  while (ks < 4 && tiles16 * (ks + 1) <= cus && nch / (ks + 1) >= 16 && C2 && (long long)ks * cfl <= c2_floats &&
+         ldc >= N)
+    ++ks;
+  if (ks > 1) p.C2 = C2, p.split_stride = cfl, p.ksplit = ks;
+  hipError_t e = launch_dma(bf16, p, s);
+  if (e != hipSuccess || ks == 1) return e;
+  const long long n = (long long)M * N;
+  hipLaunchKernelGGL(gemm_split_sum, dim3((unsigned)std::min<long long>((n + 255) / 256, 4096)), dim3(256), 0, s, C,
+                     static_cast<const float*>(C2), cfl, ks - 1, M, N, ldc);
+  return hipGetLastError();
 }
 
 hipError_t launch_clear(int* p, long long n, hipStream_t s) {

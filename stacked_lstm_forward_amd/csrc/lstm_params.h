@@ -46,9 +46,15 @@ struct GemmParams {
   int cell;            // lstm_cell_t
   int num_cus;         // compute units of the device (tile-shape choice; 0: 256)
   // plain product (the backward pass's weight and input gradients): C[m][n] =
-  // sum over k of W[m][k] U[n][k], rows m < H, fp32, row stride ldc; no bias
+  // sum over k of W[m][k] U[n][k], rows m < H, fp32, row stride ldc; no bias.
+  // With ksplit > 1 the K range is split in ksplit equal chunk ranges: range 0
+  // writes C, range z > 0 writes C2 + (z - 1) split_stride (same row stride),
+  // and the launcher adds them into C afterwards, in order.
   float* C;
   long long ldc;
+  float* C2;
+  long long split_stride;
+  int ksplit;
 };
 
 // One layer of a recurrent launch.
