@@ -135,3 +135,37 @@ def test_gpu_backward_wavefront_and_layerwise_forward_agree(dev):
     dy, dhT, dcT = upstream(cfg, 831)
     say("backward after a wavefront forward")
     run_and_check(inp, dy, dhT, dcT, dev, "bwd wavefront L3 H128")
+
+
+# dx, dh0 and dc0 are optional outputs (NULL: not written); the weight
+# gradients must not depend on them: the on-chip chain (bf16 H = 4096) and the
+# streamed chain, with and without a dh0 iteration
+@pytest.mark.parametrize("shape", [(1, 512, 4096, 16, 3, "bf16"), (2, 24, 20, 3, 5, "f32"), (2, 64, 64, 16, 4, "bf16")])
+def test_gpu_backward_without_input_gradients(dev, shape):
+    import stacked_lstm_forward_amd as sl
+    from stacked_lstm_forward_amd import runner
+    L, I, H, B, T, dtype = shape
+    cfg = li.custom_config(L, I, H, B, T, dtype, cfg_id=870 + H + B)
+    inp = li.make_inputs(cfg, random_state=True)
+    dy, dhT, dcT = upstream(cfg, 880 + H)
+    say(f"backward without dx/dh0/dc0 {shape}")
+    tp = runner.prepare_train(inp, dy, dhT, dcT, dev)
+    tp.dx = tp.dh0 = tp.dc0 = None
+    tp.forward()
+    tp.backward()
+    assert sl.lstm_bwd_last_error(tp.bws) == sl.LSTM_OK
+    f32 = lambda a: None if a is None else np.asarray(a, dtype=np.float32).astype(np.float64)  # noqa: E731
+    ref = orcb.lstm_backward_inputs(inp, f32(dy), f32(dhT), f32(dcT))
+    dW = tp.dW.double().cpu().numpy()
+    offs = [0, 4 * H * I] + [4 * H * I + k * 4 * H * H for k in range(1, L)]
+    got_dW = [dW[offs[l]:offs[l] + 4 * H * (I if l == 0 else H)].reshape(4 * H, -1) for l in range(L)]
+    got_dR = list(tp.dR.double().cpu().numpy().reshape(L, 4 * H, H))
+    got_db = list(tp.db.double().cpu().numpy().reshape(L, 4 * H))
+    tol = TOL[dtype]
+    errs = {"dW": max(rel_err(g, r) for g, r in zip(got_dW, ref["dW"])),
+            "dR": max(rel_err(g, r) for g, r in zip(got_dR, ref["dR"])),
+            "db": max(rel_err(g, r) for g, r in zip(got_db, ref["db"]))}
+    say(f"no dx/dh0/dc0 {shape}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    record(f"bwd no-input-grads {shape}", tol, errs)
+    for k, v in errs.items():
+        assert np.isfinite(v) and v <= tol, (shape, k, v)
