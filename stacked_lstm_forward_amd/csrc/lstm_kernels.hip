@@ -237,62 +237,28 @@ __device__ __forceinline__ void mfma_half<false>(f32x4& acc, const uint4& a, con
   for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[e], fb[e], acc, 0, 0, 0);
 }
 
-// NT column tiles per workgroup (16, or 14 when that packs the columns into
-// fewer rounds of workgroups than 16 would: see launch_input_gemm); each of
-// the two column-halves of waves takes NT / 2.  PLAIN: rows in order (row m of
-// tile mt is 16 mt + m, rows >= H unused) and the product written to C[m][n]
-// without bias (the backward pass's gradient products).
-template <bool BF16, int NT, bool PLAIN>
-__global__ void __launch_bounds__(kDmaThreads) lstm_input_gemm_dma(const GemmParams P) {
-  static_assert(NT % 2 == 0 && NT <= kDmaTiles, "column tiles per workgroup");
+// One workgroup tile of the direct-to-LDS product: M-tiles mtb .. mtb + 15,
+// NT column tiles from column n0, K chunks c_first .. c_first + nch - 1; the
+// stage layout is that of NTS column tiles (NT <= NTS), so tiles of two widths
+// can share one launch.  Each of the two column-halves of waves takes NT / 2.
+// PLAIN: rows in order (row m of tile mt is 16 mt + m, rows >= H unused) and
+// the product written to C[m][n] without bias (the backward pass's gradient
+// products); z > 0 selects partial-sum buffer z - 1 of a split K.
+template <bool BF16, int NT, int NTS, bool PLAIN>
+__device__ __forceinline__ void dma_tile(const GemmParams& P, int mtb, long n0, int z, int c_first, int nch) {
+  static_assert(NT % 2 == 0 && NT <= NTS && NTS <= kDmaTiles, "column tiles per workgroup");
   constexpr int WM = kDmaTiles / 4;          // M-tiles per wave (4 M-quarters x 2 column halves)
   constexpr int WN = NT / 2;                 // column tiles per wave
   typedef typename Dt<BF16>::T T;
   constexpr int KC = Dt<BF16>::KC;
-  constexpr uint32_t kABytes = kDmaTiles * 2048, kBBytes = NT * 2048;  // one stage
+  constexpr uint32_t kABytes = kDmaTiles * 2048, kBBytes = NTS * 2048;  // one stage
   extern __shared__ __align__(16) unsigned char gsmem[];
   const uint4* lds = reinterpret_cast<const uint4*>(gsmem);
   // LDS byte address of the dynamic area (M0 takes LDS addresses, not generic ones)
   typedef __attribute__((address_space(3))) unsigned char lds_byte_t;
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_byte_t*)gsmem;
-
   const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if (P.zero_ptr) {  // grid-stride zeroing of the error word and step counters
-    const long nwg = (long)gridDim.x * gridDim.y;
-    const long wg = (long)blockIdx.y * gridDim.x + blockIdx.x;
-    for (long i = wg * kDmaThreads + tid; i < P.zero_count; i += nwg * kDmaThreads) P.zero_ptr[i] = 0;
-  }
-  if (P.fill_ptr) {  // grid-stride: the unwritten pattern of a data-valid exchange
-    const long nwg = (long)gridDim.x * gridDim.y;
-    const long wg = (long)blockIdx.y * gridDim.x + blockIdx.x;
-    for (long i = wg * kDmaThreads + tid; i < P.fill_count; i += nwg * kDmaThreads) P.fill_ptr[i] = kSentinelWord;
-  }
-  // Tile order: the 1-D grid (a multiple of 8) goes round-robin over the 8
-  // XCDs, so workgroup ids are first regrouped into one contiguous range per
-  // XCD, and that range walks the (M, N) tile grid in groups of 4 M-blocks
-  // with N inner: the ~32 workgroups an XCD runs at once share 4 blocks of W
-  // rows and 8 blocks of U columns through their L2 instead of each pulling
-  // its own from memory.
-  const int nM = (P.Mt + kDmaTiles - 1) / kDmaTiles;
-  const int nN = (P.N + NT * 16 - 1) / (NT * 16);
-  const int total = nM * nN;
-  const int per_xcd = (int)gridDim.x >> 3;
-  const int vs = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-  // plain products may split K: workgroup vs takes chunk range vs / total
-  const int ks = (PLAIN && P.ksplit > 1) ? P.ksplit : 1;
-  if (vs >= total * ks) return;
-  const int z = vs / total, v = vs % total;
-  constexpr int kGroupM = 4;
-  const int in_group = kGroupM * nN;
-  const int first_m = (v / in_group) * kGroupM;
-  const int gsize = min(nM - first_m, kGroupM);
-  const int mblk = first_m + (v % in_group) % gsize;
-  const int nblk = (v % in_group) / gsize;
-  const int mtb = mblk * kDmaTiles;                  // first M-tile
-  const long n0 = (long)nblk * NT * 16;              // first column
-  const int c_first = z * (P.K / KC) / ks;           // this workgroup's chunk range of K
-  const int nch = (z + 1) * (P.K / KC) / ks - c_first;
 
   // Staging.  A block holds its 16 rows' 128-byte chunks row by row, 8 pieces
   // of 16 bytes each, piece p of row r in slot p ^ ((r >> 1) & 7).  One
@@ -464,6 +430,63 @@ __global__ void __launch_bounds__(kDmaThreads) lstm_input_gemm_dma(const GemmPar
   }
 }
 
+// The grouped input projection (or a plain product) on the direct-to-LDS
+// kernel.  NT column tiles per workgroup (16, or 14 when that packs the
+// columns into fewer rounds of workgroups than 16 would: see launch_dma);
+// with P.nbig > 0 (NT = 14 only) the column blocks of every M-block are
+// P.nblk tiles, the first P.nbig of them NT wide and the others NT - 2 (fewer
+// idle CUs in the last round: the 1600 columns of a 4096-wide layer at
+// B = 32, T = 50 make 2 x 14 + 6 x 12 column tiles per M-block; 0.196 ->
+// 0.189 ms per layer).
+template <bool BF16, int NT, bool PLAIN>
+__global__ void __launch_bounds__(kDmaThreads) lstm_input_gemm_dma(const GemmParams P) {
+  constexpr int KC = Dt<BF16>::KC;
+  const int tid = threadIdx.x;
+  if (P.zero_ptr) {  // grid-stride zeroing of the error word and step counters
+    const long nwg = (long)gridDim.x * gridDim.y;
+    const long wg = (long)blockIdx.y * gridDim.x + blockIdx.x;
+    for (long i = wg * kDmaThreads + tid; i < P.zero_count; i += nwg * kDmaThreads) P.zero_ptr[i] = 0;
+  }
+  if (P.fill_ptr) {  // grid-stride: the unwritten pattern of a data-valid exchange
+    const long nwg = (long)gridDim.x * gridDim.y;
+    const long wg = (long)blockIdx.y * gridDim.x + blockIdx.x;
+    for (long i = wg * kDmaThreads + tid; i < P.fill_count; i += nwg * kDmaThreads) P.fill_ptr[i] = kSentinelWord;
+  }
+  // Tile order: the 1-D grid (a multiple of 8) goes round-robin over the 8
+  // XCDs, so workgroup ids are first regrouped into one contiguous range per
+  // XCD, and that range walks the (M, N) tile grid in groups of 4 M-blocks
+  // with N inner: the ~32 workgroups an XCD runs at once share 4 blocks of W
+  // rows and 8 blocks of U columns through their L2 instead of each pulling
+  // its own from memory.
+  const int nM = (P.Mt + kDmaTiles - 1) / kDmaTiles;
+  const bool mixed = P.nbig > 0;
+  const int nN = mixed ? P.nblk : (P.N + NT * 16 - 1) / (NT * 16);
+  const int total = nM * nN;
+  const int per_xcd = (int)gridDim.x >> 3;
+  const int vs = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  // plain products may split K: workgroup vs takes chunk range vs / total
+  const int ks = (PLAIN && P.ksplit > 1) ? P.ksplit : 1;
+  if (vs >= total * ks) return;
+  const int z = vs / total, v = vs % total;
+  constexpr int kGroupM = 4;
+  const int in_group = kGroupM * nN;
+  const int first_m = (v / in_group) * kGroupM;
+  const int gsize = min(nM - first_m, kGroupM);
+  const int mblk = first_m + (v % in_group) % gsize;
+  const int nblk = (v % in_group) / gsize;
+  const int mtb = mblk * kDmaTiles;                  // first M-tile
+  const int c_first = z * (P.K / KC) / ks;           // this workgroup's chunk range of K
+  const int nch = (z + 1) * (P.K / KC) / ks - c_first;
+  if constexpr (NT == 14) {  // (a second body in the 16-wide kernel measured slower: 0.157 -> 0.168 ms)
+    if (mixed && nblk >= P.nbig) {
+      const long n0 = ((long)P.nbig * NT + (long)(nblk - P.nbig) * (NT - 2)) * 16;
+      dma_tile<BF16, NT - 2, NT, PLAIN>(P, mtb, n0, z, c_first, nch);
+      return;
+    }
+  }
+  dma_tile<BF16, NT, NT, PLAIN>(P, mtb, (long)nblk * NT * 16, z, c_first, nch);
+}
+
 // C[m][n] += C2[z S + m ldc + n] for z = 0 .. parts - 1, in that order: the
 // partial sums of a plain product whose K range was split.
 __global__ void __launch_bounds__(256) gemm_split_sum(float* C, const float* C2, long long S, int parts, int M, int N,
@@ -630,6 +653,56 @@ hipError_t launch_dma(bool bf16, const GemmParams& p, hipStream_t s) {
   };
   int nt = rounds(14) * (kDmaTiles + 14) < rounds(16) * (kDmaTiles + 16) ? 14 : 16;
   if (p.ksplit > 1) nt = 16;  // (the split was chosen for 16)
+  GemmParams q = p;
+  q.nbig = 0, q.nblk = 0;
+  if (p.ksplit <= 1 && nt == 14) {
+    // Mixed widths when they shorten the busiest CU: the tiles of each
+    // XCD's range go, in launch order, to whichever of its CUs frees first
+    // (a tile costs its load blocks per chunk, 16 + width); compare with
+    // uniform tiles of the chosen width.
+    const int cus = p.num_cus > 0 ? p.num_cus : 256;
+    const int nct = (p.N + 15) / 16;
+    auto makespan = [&](int nblk, int nbig, int wbig, int wsmall) {
+      const int total = nM * nblk;
+      const int grid = (total + 7) & ~7, per_xcd = grid / 8, cpx = std::max(1, cus / 8);
+      long long worst = 0;
+      std::vector<long long> busy(cpx);
+      for (int x = 0; x < 8; ++x) {
+        std::fill(busy.begin(), busy.end(), 0LL);
+        for (int v = x * per_xcd; v < std::min(total, (x + 1) * per_xcd); ++v) {
+          const int in_group = 4 * nblk, first_m = (v / in_group) * 4, gsize = std::min(nM - first_m, 4);
+          const int nb = (v % in_group) / gsize;
+          const int w = nb < nbig ? wbig : wsmall;
+          auto it = std::min_element(busy.begin(), busy.end());
+          *it += kDmaTiles + w;
+        }
+        worst = std::max(worst, *std::max_element(busy.begin(), busy.end()));
+      }
+      return worst;
+    };
+    // (the choice is a function of the shape: made once per process)
+    struct Seen {
+      int Mt, N, cus, nbig, nblk;
+    };
+    static std::mutex mu;
+    static std::vector<Seen> seen;
+    std::lock_guard<std::mutex> lock(mu);
+    auto hit = std::find_if(seen.begin(), seen.end(),
+                            [&](const Seen& e) { return e.Mt == p.Mt && e.N == p.N && e.cus == cus; });
+    if (hit == seen.end()) {
+      Seen e{p.Mt, p.N, cus, 0, 0};
+      const int nblk_u = (nct + nt - 1) / nt;
+      const long long uniform = makespan(nblk_u, nblk_u, nt, nt);
+      // the fewest blocks of widths nt and nt - 2 that cover the columns
+      const int k = (nct + nt - 1) / nt;
+      const int need = nct - (nt - 2) * k;  // columns beyond k narrow blocks
+      const int nbig = need <= 0 ? 0 : (need + 1) / 2;
+      if (nbig > 0 && nbig < k && makespan(k, nbig, nt, nt - 2) < uniform) e.nbig = nbig, e.nblk = k;
+      seen.push_back(e);
+      hit = seen.end() - 1;
+    }
+    q.nbig = hit->nbig, q.nblk = hit->nblk;
+  }
   auto kernel_of = [&](int n) { return dma_kernel(bf16, n, p.C != nullptr); };
   const void* fn = kernel_of(nt);
   // 16 column tiles take all 160 KiB of a CU's LDS; a device that gives a
@@ -643,9 +716,10 @@ hipError_t launch_dma(bool bf16, const GemmParams& p, hipStream_t s) {
   }
   if (e != hipSuccess) return e;
   const unsigned lds = dma_lds_bytes(nt);
-  const int tiles = ((p.N + nt * 16 - 1) / (nt * 16)) * nM * (p.ksplit > 1 ? p.ksplit : 1);
+  const int nblk = q.nbig > 0 ? q.nblk : (p.N + nt * 16 - 1) / (nt * 16);
+  const int tiles = nblk * nM * (p.ksplit > 1 ? p.ksplit : 1);
   const dim3 grid((tiles + 7) & ~7);  // a multiple of the 8 XCDs (extra workgroups only help zeroing)
-  void* args[] = {const_cast<GemmParams*>(&p)};
+  void* args[] = {&q};
   return hipLaunchKernel(fn, grid, dim3(kDmaThreads), args, lds, s);
 }
 

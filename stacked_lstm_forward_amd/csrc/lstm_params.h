@@ -55,6 +55,9 @@ struct GemmParams {
   float* C2;
   long long split_stride;
   int ksplit;
+  // direct-to-LDS kernel, mixed column-tile widths: nblk column blocks per
+  // M-block, the first nbig of NT column tiles, the rest of NT - 2 (0: all NT)
+  int nbig, nblk;
 };
 
 // One layer of a recurrent launch.
