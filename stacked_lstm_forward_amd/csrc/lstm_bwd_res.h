@@ -184,10 +184,12 @@ lstm_bwd_res_kernel(const BwdResParams P) {
       }
     }
     if (s > 0) {
-      // dp_{t+1} of this quarter's units: finished by workgroups 64 kq .. 64 kq + 63
+      // dp_{t+1} of this quarter's units: finished by the quarter's workgroups
+      // (wgs / 4 of them: 64 kq .. 64 kq + 63 at H = 4096)
       if (kg == 0) {
-        const bool ok = wait_counts_serial(P.flags_d + (long)(KS * 16) * kq * kFlagStride, KS * 16, s, nullptr, 0, 0,
-                                           P.err, P.timeout_ticks);
+        const int nq = P.wgs / 4;
+        const bool ok = wait_counts_serial(P.flags_d + (long)nq * kq * kFlagStride, nq, s, nullptr, 0, 0, P.err,
+                                           P.timeout_ticks);
         if (lane == 0) s_ok = ok ? 1 : 0;
       }
       __syncthreads();
