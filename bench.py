@@ -224,22 +224,27 @@ def train_bench(args, cfg, workload, inp) -> int:
     dcT = rng.standard_normal((cfg.L, cfg.B, cfg.H)).astype(np.float32)
     tp = runner.prepare_train(inp, dy, dhT, dcT, "cuda:0")
     stream = torch.cuda.current_stream()
+    plain = bool(args.plain_launch)
     for _ in range(args.warmup):
-        tp.forward(stream)
-        tp.backward(stream)
+        tp.forward(stream, plain)
+        tp.backward(stream, plain)
     torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record(stream)
     for k in range(args.steps):
         ev[k][0].record(stream)
-        tp.forward(stream)
+        tp.forward(stream, plain)
         ev[k][1].record(stream)
-        tp.backward(stream)
+        tp.backward(stream, plain)
         ev[k][2].record(stream)
     t1.record(stream)
     torch.cuda.synchronize()
     st = sl_last_error(tp.fwd)
+    if not st:
+        import stacked_lstm_forward_amd as sl
+        b = sl.lstm_bwd_last_error(tp.bws)
+        st = "" if b == sl.LSTM_OK else sl.lstm_status_string(b)
     if st:
         print(f"timed training run failed: {st}", file=sys.stderr)
         return 1

@@ -42,10 +42,11 @@
  *
  * Recurrent chain: for bf16 layers with H = 4096 and B <= 32 (when all 256 of
  * its workgroups fit on the device at once) it runs as one persistent launch
- * per layer that keeps R_l^T on chip and exchanges dp_t through `ws` with
- * per-workgroup step counters; a step wait longer than 2 s sets the error word
- * that lstm_bwd_last_error reports.  Other shapes run it as two launches per
- * step that stream R_l^T from memory.
+ * per layer that keeps R_l^T on chip, each workgroup taking 64 units and a
+ * quarter of K; dp_t and the partial sums of dh_rec go through `ws` with
+ * per-workgroup step counters, and a step wait longer than 2 s sets the
+ * error word that lstm_bwd_last_error reports.  Other shapes run it as two
+ * launches per step that stream R_l^T from memory.
  */
 #ifndef LSTM_BWD_H
 #define LSTM_BWD_H
@@ -66,6 +67,21 @@ lstm_status_t lstm_fwd_train(const lstm_desc_t *d,
                              void *y, void *hT, float *cT,
                              void *reserve, void *ws, hipStream_t stream);
 
+/* lstm_fwd_train with the options of lstm_fwd_ex (opts may be NULL). */
+lstm_status_t lstm_fwd_train_ex(const lstm_desc_t *d,
+                                const void *x, const void *h0, const float *c0,
+                                const void *W, const void *R, const void *b,
+                                void *y, void *hT, float *cT,
+                                void *reserve, void *ws, hipStream_t stream, const lstm_fwd_opts_t *opts);
+
+/* Options for lstm_bwd_ex.  Zero-initialise and set what you need. */
+typedef struct {
+  int32_t plain_launch;  /* 1: start the on-chip recurrent chain with an ordinary launch instead of a
+                            cooperative one (for profilers that do not handle cooperative launches);
+                            co-residency is still checked against the occupancy limit          */
+  int32_t reserved[7];   /* zero */
+} lstm_bwd_opts_t;
+
 /* Bytes of the workspace lstm_bwd needs for `d` (0: invalid or unsupported). */
 size_t lstm_bwd_workspace_size(const lstm_desc_t *d);
 
@@ -82,6 +98,15 @@ lstm_status_t lstm_bwd(const lstm_desc_t *d,
                        float *dx, float *dh0, float *dc0,
                        float *dW, float *dR, float *db,
                        void *ws, hipStream_t stream);
+
+/* lstm_bwd with options (opts may be NULL, which equals lstm_bwd). */
+lstm_status_t lstm_bwd_ex(const lstm_desc_t *d,
+                          const void *x, const void *h0, const float *c0,
+                          const void *W, const void *R, const void *reserve,
+                          const float *dy, const float *dhT, const float *dcT,
+                          float *dx, float *dh0, float *dc0,
+                          float *dW, float *dR, float *db,
+                          void *ws, hipStream_t stream, const lstm_bwd_opts_t *opts);
 
 #ifdef __cplusplus
 }

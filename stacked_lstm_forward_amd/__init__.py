@@ -17,6 +17,7 @@ The functions carry the C names:
     lstm_train_reserve_size(desc), lstm_bwd_workspace_size(desc) -> int
     lstm_fwd_train(desc, x, h0, c0, W, R, b, y, hT, cT, reserve, ws, stream=None) -> status
     lstm_bwd(desc, x, h0, c0, W, R, reserve, dy, dhT, dcT, dx, dh0, dc0, dW, dR, db, ws, stream=None) -> status
+    lstm_fwd_train_ex(..., opts) / lstm_bwd_ex(..., opts): the same with LstmOpts / BwdOpts
 
 Tensor arguments may be torch tensors (their ``data_ptr()``), raw integer
 device addresses, or None for the nullable ones (h0, c0, hT, cT).
@@ -41,13 +42,17 @@ CELL_IDS = {"lstm": LSTM_CELL_LSTM, "gru": LSTM_CELL_GRU, "rnn_tanh": LSTM_CELL_
 EXPORTED = ("lstm_fwd_workspace_size", "lstm_fwd", "lstm_fwd_ex", "lstm_status_string",
             "lstm_fwd_validate", "lstm_fwd_last_error", "lstm_fwd_plan", "lstm_fwd_noalloc")
 NOALLOC_MAX_WORKSPACE = 64 << 20  # LSTM_FWD_NOALLOC_MAX_WORKSPACE
-EXPORTED_TRAIN = ("lstm_train_reserve_size", "lstm_fwd_train", "lstm_bwd_workspace_size", "lstm_bwd",
-                  "lstm_bwd_last_error")
+EXPORTED_TRAIN = ("lstm_train_reserve_size", "lstm_fwd_train", "lstm_fwd_train_ex", "lstm_bwd_workspace_size",
+                  "lstm_bwd", "lstm_bwd_ex", "lstm_bwd_last_error")
 
 
 class LstmDesc(ctypes.Structure):
     _fields_ = [("L", ctypes.c_int32), ("I", ctypes.c_int32), ("H", ctypes.c_int32),
                 ("B", ctypes.c_int32), ("T", ctypes.c_int32), ("dtype", ctypes.c_int32), ("cell", ctypes.c_int32)]
+
+
+class BwdOpts(ctypes.Structure):
+    _fields_ = [("plain_launch", ctypes.c_int32), ("reserved", ctypes.c_int32 * 7)]
 
 
 class LstmOpts(ctypes.Structure):
@@ -127,6 +132,10 @@ def load_library() -> ctypes.CDLL:
     lib.lstm_fwd_train.restype = i32
     lib.lstm_bwd.argtypes = [pdesc] + [vp] * 17
     lib.lstm_bwd.restype = i32
+    lib.lstm_fwd_train_ex.argtypes = [pdesc] + [vp] * 12 + [ctypes.POINTER(LstmOpts)]
+    lib.lstm_fwd_train_ex.restype = i32
+    lib.lstm_bwd_ex.argtypes = [pdesc] + [vp] * 17 + [ctypes.POINTER(BwdOpts)]
+    lib.lstm_bwd_ex.restype = i32
     _lib = lib
     return lib
 
@@ -201,6 +210,20 @@ def lstm_bwd(desc, x, h0, c0, W, R, reserve, dy, dhT, dcT, dx, dh0, dc0, dW, dR,
                                        _ptr(W), _ptr(R), _ptr(reserve), _ptr(dy), _ptr(dhT), _ptr(dcT), _ptr(dx),
                                        _ptr(dh0), _ptr(dc0), _ptr(dW), _ptr(dR), _ptr(db), _ptr(ws),
                                        _stream(stream)))
+
+
+def lstm_fwd_train_ex(desc, x, h0, c0, W, R, b, y, hT, cT, reserve, ws, stream=None, opts=None) -> int:
+    return int(load_library().lstm_fwd_train_ex(ctypes.byref(desc), _ptr(x), _ptr(h0), _ptr(c0), _ptr(W), _ptr(R),
+                                                _ptr(b), _ptr(y), _ptr(hT), _ptr(cT), _ptr(reserve), _ptr(ws),
+                                                _stream(stream), None if opts is None else ctypes.byref(opts)))
+
+
+def lstm_bwd_ex(desc, x, h0, c0, W, R, reserve, dy, dhT, dcT, dx, dh0, dc0, dW, dR, db, ws, stream=None,
+                opts=None) -> int:
+    return int(load_library().lstm_bwd_ex(None if desc is None else ctypes.byref(desc), _ptr(x), _ptr(h0), _ptr(c0),
+                                          _ptr(W), _ptr(R), _ptr(reserve), _ptr(dy), _ptr(dhT), _ptr(dcT), _ptr(dx),
+                                          _ptr(dh0), _ptr(dc0), _ptr(dW), _ptr(dR), _ptr(db), _ptr(ws),
+                                          _stream(stream), None if opts is None else ctypes.byref(opts)))
 
 
 def lstm_fwd_validate(desc, x, W, R, b, y, ws, ws_bytes: int) -> int:

@@ -578,7 +578,7 @@ template <bool BF16>
 lstm_status_t bwd_run(const lstm_desc_t* d, const void* x, const void* h0, const float* c0, const void* W,
                       const void* R, const void* reserve, const float* dy, const float* dhT, const float* dcT,
                       float* dx, float* dh0, float* dc0, float* dW, float* dR, float* db, void* ws, const BwdLayout& o,
-                      hipStream_t st) {
+                      bool plain, hipStream_t st) {
   const int L = d->L, I = d->I, H = d->H, B = d->B, T = d->T;
   const long TB = (long)T * B, G = 4L * H;
   const size_t s = BF16 ? 2 : 4;
@@ -677,8 +677,11 @@ lstm_status_t bwd_run(const lstm_desc_t* d, const void* x, const void* h0, const
       P.grid = (res_wgs + 7) & ~7;
       P.xcd_remap = 1;
       void* args[] = {&P};
-      CHECK(hipLaunchCooperativeKernel(bwd_res_fn(res_nw), dim3(P.grid), dim3(64 * kBwdResWaves), args,
-                                       (unsigned)res_lds, st));
+      if (plain)
+        CHECK(hipLaunchKernel(bwd_res_fn(res_nw), dim3(P.grid), dim3(64 * kBwdResWaves), args, (unsigned)res_lds, st));
+      else
+        CHECK(hipLaunchCooperativeKernel(bwd_res_fn(res_nw), dim3(P.grid), dim3(64 * kBwdResWaves), args,
+                                         (unsigned)res_lds, st));
     }
     for (int t = T - 1; t >= 0 && !resident; --t) {
       StepArgs a;
@@ -765,10 +768,10 @@ size_t lstm_bwd_workspace_size(const lstm_desc_t* d) {
   return bwd_layout(d, &o) ? o.total : 0;
 }
 
-lstm_status_t lstm_bwd(const lstm_desc_t* d, const void* x, const void* h0, const float* c0, const void* W,
-                       const void* R, const void* reserve, const float* dy, const float* dhT, const float* dcT,
-                       float* dx, float* dh0, float* dc0, float* dW, float* dR, float* db, void* ws,
-                       hipStream_t stream) {
+lstm_status_t lstm_bwd_ex(const lstm_desc_t* d, const void* x, const void* h0, const float* c0, const void* W,
+                          const void* R, const void* reserve, const float* dy, const float* dhT, const float* dcT,
+                          float* dx, float* dh0, float* dc0, float* dW, float* dR, float* db, void* ws,
+                          hipStream_t stream, const lstm_bwd_opts_t* opts) {
   if (!d || d->L < 1 || d->I < 1 || d->H < 1 || d->B < 1 || d->T < 1) return LSTM_ERR_INVALID_ARG;
   if (d->dtype != LSTM_F32 && d->dtype != LSTM_BF16) return LSTM_ERR_INVALID_ARG;
   if (d->cell < LSTM_CELL_LSTM || d->cell > LSTM_CELL_RNN_RELU) return LSTM_ERR_INVALID_ARG;
@@ -780,9 +783,17 @@ lstm_status_t lstm_bwd(const lstm_desc_t* d, const void* x, const void* h0, cons
   // the products address their operands with 32-bit tile indices and 64-bit offsets;
   // keep every dimension below 2^31 elements
   if ((long long)d->T * d->B * 4 * d->H >= (1LL << 31)) return LSTM_ERR_UNSUPPORTED;
+  const bool plain = opts && opts->plain_launch;
   return d->dtype == LSTM_BF16
-             ? bwd_run<true>(d, x, h0, c0, W, R, reserve, dy, dhT, dcT, dx, dh0, dc0, dW, dR, db, ws, o, stream)
-             : bwd_run<false>(d, x, h0, c0, W, R, reserve, dy, dhT, dcT, dx, dh0, dc0, dW, dR, db, ws, o, stream);
+             ? bwd_run<true>(d, x, h0, c0, W, R, reserve, dy, dhT, dcT, dx, dh0, dc0, dW, dR, db, ws, o, plain, stream)
+             : bwd_run<false>(d, x, h0, c0, W, R, reserve, dy, dhT, dcT, dx, dh0, dc0, dW, dR, db, ws, o, plain, stream);
+}
+
+lstm_status_t lstm_bwd(const lstm_desc_t* d, const void* x, const void* h0, const float* c0, const void* W,
+                       const void* R, const void* reserve, const float* dy, const float* dhT, const float* dcT,
+                       float* dx, float* dh0, float* dc0, float* dW, float* dR, float* db, void* ws,
+                       hipStream_t stream) {
+  return lstm_bwd_ex(d, x, h0, c0, W, R, reserve, dy, dhT, dcT, dx, dh0, dc0, dW, dR, db, ws, stream, nullptr);
 }
 
 }  // extern "C"

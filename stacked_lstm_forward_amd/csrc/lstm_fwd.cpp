@@ -470,11 +470,17 @@ size_t lstm_train_reserve_size(const lstm_desc_t* d) {
   return (tbh * (16 + 4 + (d->dtype == LSTM_BF16 ? 2 : 4)) + 255) & ~(size_t)255;
 }
 
+lstm_status_t lstm_fwd_train_ex(const lstm_desc_t* d, const void* x, const void* h0, const float* c0, const void* W,
+                                const void* R, const void* b, void* y, void* hT, float* cT, void* reserve, void* ws,
+                                hipStream_t stream, const lstm_fwd_opts_t* opts) {
+  if (!reserve) return LSTM_ERR_INVALID_ARG;
+  return fwd_impl(d, x, h0, c0, W, R, b, y, hT, cT, ws, stream, opts, reserve);
+}
+
 lstm_status_t lstm_fwd_train(const lstm_desc_t* d, const void* x, const void* h0, const float* c0, const void* W,
                              const void* R, const void* b, void* y, void* hT, float* cT, void* reserve, void* ws,
                              hipStream_t stream) {
-  if (!reserve) return LSTM_ERR_INVALID_ARG;
-  return fwd_impl(d, x, h0, c0, W, R, b, y, hT, cT, ws, stream, nullptr, reserve);
+  return lstm_fwd_train_ex(d, x, h0, c0, W, R, b, y, hT, cT, reserve, ws, stream, nullptr);
 }
 
 lstm_status_t lstm_fwd(const lstm_desc_t* d, const void* x, const void* h0, const float* c0, const void* W,

@@ -257,6 +257,9 @@ lstm_rec_res_kernel(const RecParams P) {
     // (the host gives every resident layer either y or a row-major X)
     const bool last = (t == T_ - 1);
 
+    T hl[4];      // the last tile's new h values (up to four units: the simple RNN)
+    int nl = 0;   // ... how many
+    f32x4 pl{};   // ... its pre-activations (training saves)
     // The h loads of the step form one stream over all column tiles, PD
     // chunks ahead: the next tile's first chunks are in flight while this
     // tile's sums are combined and its gates computed.  Load g is chunk slot
@@ -355,16 +358,27 @@ lstm_rec_res_kernel(const RecParams P) {
         for (int r = 0; r < KS; ++r) p += red[(kg * KS + r) * 64 + lane];
         const long o = (long)(16 * j + (lane & 15)) * H + funit;
         const long fo = (long)j * NCH * FB + fpos;
+        // The last tile's stores that no other workgroup reads in this launch
+        // (the row-major copy, hT, the training saves) wait until the step is
+        // published: the step counter then waits only for the exchange.
+        const bool later = j == NW - 1;
         cell_update(cell, p, st[j], H - funit, [&](int u, float h) {
           const T hv = from_float<BF16>(h);
           store_coherent<BF16>(fout + fo + u, hv);
+          if (later) {
+            hl[u] = hv;
+            nl = u + 1;
+            return;
+          }
           rout[o + u] = hv;
           if (last && Lr.hT) reinterpret_cast<T*>(Lr.hT)[o + u] = hv;
           if constexpr (SAVE) reinterpret_cast<T*>(Lr.save_h)[(long)t * B * H + o + u] = hv;
         });
         if (cell == kCellLstm && last && Lr.cT) Lr.cT[o] = st[j];
         if constexpr (SAVE) {
-          if (cell == kCellLstm)
+          if (later)
+            pl = p;
+          else if (cell == kCellLstm)
             save_lstm_step(Lr.save_gates, Lr.save_c, p, st[j], t, B, H, 16 * j + (lane & 15), funit);
         }
       }
@@ -379,6 +393,18 @@ lstm_rec_res_kernel(const RecParams P) {
     if (tid == 0)
       __hip_atomic_store(Lr.flags + (long)v * kFlagStride, t + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     stamp(t, 5);
+    if (flive[NW - 1]) {
+      const long o = (long)(16 * (NW - 1) + (lane & 15)) * H + funit;
+      for (int u = 0; u < nl; ++u) {
+        rout[o + u] = hl[u];
+        if (last && Lr.hT) reinterpret_cast<T*>(Lr.hT)[o + u] = hl[u];
+        if constexpr (SAVE) reinterpret_cast<T*>(Lr.save_h)[(long)t * B * H + o + u] = hl[u];
+      }
+      if constexpr (SAVE) {
+        if (cell == kCellLstm)
+          save_lstm_step(Lr.save_gates, Lr.save_c, pl, st[NW - 1], t, B, H, 16 * (NW - 1) + (lane & 15), funit);
+      }
+    }
   }
 }
 

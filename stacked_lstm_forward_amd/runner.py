@@ -8,8 +8,9 @@ from typing import Optional
 
 import numpy as np
 
-from . import (LSTM_BF16, LSTM_F32, LstmDesc, LstmOpts, check, lstm_bwd, lstm_bwd_workspace_size, lstm_fwd,
-               lstm_fwd_ex, lstm_fwd_train, lstm_fwd_workspace_size, lstm_train_reserve_size, make_desc)
+from . import (LSTM_BF16, LSTM_F32, BwdOpts, LstmDesc, LstmOpts, check, lstm_bwd, lstm_bwd_ex,
+               lstm_bwd_workspace_size, lstm_fwd, lstm_fwd_ex, lstm_fwd_train, lstm_fwd_train_ex,
+               lstm_fwd_workspace_size, lstm_train_reserve_size, make_desc)
 
 
 def _torch():
@@ -119,13 +120,25 @@ class TrainProblem:
     dR: object
     db: object
 
-    def forward(self, stream=None) -> None:
+    def forward(self, stream=None, plain_launch=False) -> None:
         p = self.fwd
+        if plain_launch:
+            o = LstmOpts()
+            o.plain_launch = 1
+            check(lstm_fwd_train_ex(p.desc, p.x, p.h0, p.c0, p.W, p.R, p.b, p.y, p.hT, p.cT, self.reserve, p.ws,
+                                    stream, o), "lstm_fwd_train_ex")
+            return
         check(lstm_fwd_train(p.desc, p.x, p.h0, p.c0, p.W, p.R, p.b, p.y, p.hT, p.cT, self.reserve, p.ws, stream),
               "lstm_fwd_train")
 
-    def backward(self, stream=None) -> None:
+    def backward(self, stream=None, plain_launch=False) -> None:
         p = self.fwd
+        if plain_launch:
+            o = BwdOpts()
+            o.plain_launch = 1
+            check(lstm_bwd_ex(p.desc, p.x, p.h0, p.c0, p.W, p.R, self.reserve, self.dy, self.dhT, self.dcT, self.dx,
+                              self.dh0, self.dc0, self.dW, self.dR, self.db, self.bws, stream, o), "lstm_bwd_ex")
+            return
         check(lstm_bwd(p.desc, p.x, p.h0, p.c0, p.W, p.R, self.reserve, self.dy, self.dhT, self.dcT, self.dx,
                        self.dh0, self.dc0, self.dW, self.dR, self.db, self.bws, stream), "lstm_bwd")
 

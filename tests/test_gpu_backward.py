@@ -169,3 +169,24 @@ def test_gpu_backward_without_input_gradients(dev, shape):
     record(f"bwd no-input-grads {shape}", tol, errs)
     for k, v in errs.items():
         assert np.isfinite(v) and v <= tol, (shape, k, v)
+
+
+def test_gpu_backward_plain_launch_options(dev):
+    """lstm_fwd_train_ex / lstm_bwd_ex with plain (non-cooperative) launches
+    give the same bits as the default entry points (the on-chip chain)."""
+    import torch
+    import stacked_lstm_forward_amd as sl
+    from stacked_lstm_forward_amd import runner
+    cfg = li.custom_config(1, 512, 4096, 20, 3, "bf16", cfg_id=890)
+    inp = li.make_inputs(cfg, random_state=True)
+    dy, dhT, dcT = upstream(cfg, 891)
+    say("backward with plain-launch options")
+    a = runner.prepare_train(inp, dy, dhT, dcT, dev)
+    a.forward()
+    a.backward()
+    b = runner.prepare_train(inp, dy, dhT, dcT, dev)
+    b.forward(plain_launch=True)
+    b.backward(plain_launch=True)
+    assert sl.lstm_bwd_last_error(b.bws) == sl.LSTM_OK
+    for x, y in ((a.dx, b.dx), (a.dh0, b.dh0), (a.dc0, b.dc0), (a.dW, b.dW), (a.dR, b.dR), (a.db, b.db)):
+        assert torch.equal(x.view(torch.int32), y.view(torch.int32))
