@@ -152,8 +152,10 @@ typedef struct {
   int32_t trace_stride;       /* virtual workgroup stride between traced workgroups (>= 1)         */
   int32_t plain_launch;       /* 1: launch the persistent kernel with an ordinary launch instead of a
                                  cooperative one (for profilers that do not handle cooperative
-                                 launches).  Co-residency is still checked against the occupancy
-                                 limit; a grid that is not co-resident ends with
+                                 launches, and for HIP graph capture: a forward enqueued this way
+                                 on a capturing stream replays to the same bits; it records no
+                                 memset nodes).  Co-residency is still checked against the
+                                 occupancy limit; a grid that is not co-resident ends with
                                  LSTM_ERR_BARRIER_TIMEOUT rather than a hang.                      */
 } lstm_fwd_opts_t;
 
