@@ -121,7 +121,8 @@ def roofline_of(model: dict, ms: float, peaks: dict, dtype: str) -> dict:
 
 # Sources the forward's kernels are not built from (the backward pass, the
 # peak microbenchmarks, the allocation-free entry point's wrapper).
-DIGEST_EXCLUDED = ("lstm_bwd.hip", "lstm_bwd_res.h", "lstm_peaks.hip", "lstm_fwd_noalloc.hip")
+DIGEST_EXCLUDED = ("lstm_bwd.hip", "lstm_bwd_res.h", "lstm_bwd_res_inst.hip", "lstm_peaks.hip",
+                   "lstm_fwd_noalloc.hip")
 
 
 def kernel_source_digest() -> str:

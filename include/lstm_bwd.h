@@ -40,9 +40,10 @@
  * Errors: status codes as in lstm_fwd.h, checked on the host before anything
  * is enqueued; a cell other than the LSTM returns LSTM_ERR_UNSUPPORTED.
  *
- * Recurrent chain: for bf16 layers with H = 4096 and B <= 32 (when all 256 of
- * its workgroups fit on the device at once) it runs as one persistent launch
- * per layer that keeps R_l^T on chip, each workgroup taking 64 units and a
+ * Recurrent chain: for H = 256, 512, 1024, 1536, 2048 or 4096 in bf16 and
+ * H = 256, 512 or 1024 in fp32, with B <= 64 (32 at H = 4096), it runs as one
+ * persistent launch per layer that keeps R_l^T on chip (when its H / 16
+ * workgroups fit on the device at once), each workgroup taking 64 units and a
  * quarter of K; dp_t and the partial sums of dh_rec go through `ws` with
  * per-workgroup step counters, and a step wait longer than 2 s sets the
  * error word that lstm_bwd_last_error reports.  Other shapes run it as two
@@ -84,6 +85,14 @@ typedef struct {
 
 /* Bytes of the workspace lstm_bwd needs for `d` (0: invalid or unsupported). */
 size_t lstm_bwd_workspace_size(const lstm_desc_t *d);
+
+/* 1 if lstm_bwd runs the recurrent chain of `d` as the persistent on-chip
+ * launch described above, 0 if it streams R_l^T (or `d` is invalid).  Host
+ * only, no HIP calls; at run time the on-chip chain also needs its
+ * workgroups co-resident on the device and dy, reserve, c0, dhT, dcT, dh0 and
+ * dc0 16-byte aligned (it moves them 16 bytes at a time), else the streamed
+ * chain runs. */
+int lstm_bwd_chain_on_chip(const lstm_desc_t *d);
 
 /* Status of the last lstm_bwd on `ws`: synchronises `stream`, then reads the
  * workspace's error word (LSTM_ERR_BARRIER_TIMEOUT if a step wait of the

@@ -15,6 +15,7 @@ The functions carry the C names:
     lstm_status_string(status) -> str
     lstm_fwd_noalloc(desc, x, h0, c0, W, R, b, y, hT, cT, dev_status=None, stream=None) -> status
     lstm_train_reserve_size(desc), lstm_bwd_workspace_size(desc) -> int
+    lstm_bwd_chain_on_chip(desc) -> bool
     lstm_fwd_train(desc, x, h0, c0, W, R, b, y, hT, cT, reserve, ws, stream=None) -> status
     lstm_bwd(desc, x, h0, c0, W, R, reserve, dy, dhT, dcT, dx, dh0, dc0, dW, dR, db, ws, stream=None) -> status
     lstm_fwd_train_ex(..., opts) / lstm_bwd_ex(..., opts): the same with LstmOpts / BwdOpts
@@ -43,7 +44,7 @@ EXPORTED = ("lstm_fwd_workspace_size", "lstm_fwd", "lstm_fwd_ex", "lstm_status_s
             "lstm_fwd_validate", "lstm_fwd_last_error", "lstm_fwd_plan", "lstm_fwd_noalloc")
 NOALLOC_MAX_WORKSPACE = 64 << 20  # LSTM_FWD_NOALLOC_MAX_WORKSPACE
 EXPORTED_TRAIN = ("lstm_train_reserve_size", "lstm_fwd_train", "lstm_fwd_train_ex", "lstm_bwd_workspace_size",
-                  "lstm_bwd", "lstm_bwd_ex", "lstm_bwd_last_error")
+                  "lstm_bwd_chain_on_chip", "lstm_bwd", "lstm_bwd_ex", "lstm_bwd_last_error")
 
 
 class LstmDesc(ctypes.Structure):
@@ -126,6 +127,8 @@ def load_library() -> ctypes.CDLL:
     lib.lstm_train_reserve_size.restype = sz
     lib.lstm_bwd_workspace_size.argtypes = [pdesc]
     lib.lstm_bwd_workspace_size.restype = sz
+    lib.lstm_bwd_chain_on_chip.argtypes = [pdesc]
+    lib.lstm_bwd_chain_on_chip.restype = i32
     lib.lstm_bwd_last_error.argtypes = [vp, vp]
     lib.lstm_bwd_last_error.restype = i32
     lib.lstm_fwd_train.argtypes = [pdesc, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
@@ -197,6 +200,10 @@ def lstm_bwd_last_error(ws, stream=None) -> int:
 
 def lstm_bwd_workspace_size(desc) -> int:
     return int(load_library().lstm_bwd_workspace_size(ctypes.byref(desc)))
+
+
+def lstm_bwd_chain_on_chip(desc) -> bool:
+    return bool(load_library().lstm_bwd_chain_on_chip(ctypes.byref(desc)))
 
 
 def lstm_fwd_train(desc, x, h0, c0, W, R, b, y, hT, cT, reserve, ws, stream=None) -> int:

@@ -39,6 +39,16 @@ namespace lstm {
 hipError_t prepare_fn(const void* fn, int lds_bytes, int block, int* blocks_per_cu);
 hipError_t launch_gemm_plain(bool bf16, const void* A, const void* B, float* C, long long ldc, int M, int N, int K,
                              int num_cus, float* C2, long long c2_floats, hipStream_t s);
+// lstm_bwd_res_inst.hip: the on-chip chain kernel of kBwdResShape[k] for nw batch tiles
+const void* bwd_res_kernel_ptr_shape0(int nw);
+const void* bwd_res_kernel_ptr_shape1(int nw);
+const void* bwd_res_kernel_ptr_shape2(int nw);
+const void* bwd_res_kernel_ptr_shape3(int nw);
+const void* bwd_res_kernel_ptr_shape4(int nw);
+const void* bwd_res_kernel_ptr_shape5(int nw);
+const void* bwd_res_kernel_ptr_shape6(int nw);
+const void* bwd_res_kernel_ptr_shape7(int nw);
+const void* bwd_res_kernel_ptr_shape8(int nw);
 
 namespace {
 
@@ -274,17 +284,32 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_colsum_final(const float* par
 // the padding.  Workgroup (x, c): columns n of R 64 x .. 64 x + 63 and rows k
 // of chunk c, through an LDS tile.  UNIT_MAJOR orders K as k = 4 u + g (gate g
 // of unit u, row g H + u of R_l), the order of the on-chip chain's exchange.
+// Rows are read in 16-byte pieces (each tile row is one 128- or 256-byte run of
+// R_l) when every row of R_l starts 16-byte aligned (`vec`: the host checks the
+// base and that H is a multiple of 16 / size of an element), element by
+// element otherwise.
 template <bool BF16, bool UNIT_MAJOR>
-__global__ void __launch_bounds__(kBwdThreads) bwd_block_rt(const void* R, int H, int nch, uint4* out) {
+__global__ void __launch_bounds__(kBwdThreads) bwd_block_rt(const void* R, int H, int nch, int vec, uint4* out) {
   typedef typename Dt<BF16>::T T;
-  constexpr int KC = Dt<BF16>::KC, EPH = KC / 8;
-  __shared__ T tile[KC][64 + 16 / sizeof(T)];
+  constexpr int KC = Dt<BF16>::KC, EPH = KC / 8, VE = 16 / sizeof(T), RV = 64 / VE;
+  __shared__ __align__(16) T tile[KC][64 + VE];
   const int n0 = blockIdx.x * 64, c = blockIdx.y, G = 4 * H;
   const T* Rp = static_cast<const T*>(R);
-  for (int i = threadIdx.x; i < KC * 64; i += kBwdThreads) {
-    const int kr = i / 64, nc = i % 64, k = c * KC + kr, n = n0 + nc;
+  for (int i = threadIdx.x; i < KC * RV; i += kBwdThreads) {
+    const int kr = i / RV, nc = (i % RV) * VE, k = c * KC + kr, n = n0 + nc;
     const long row = UNIT_MAJOR ? (long)(k % 4) * H + k / 4 : (long)k;
-    tile[kr][nc] = (k < G && n < H) ? Rp[row * H + n] : T(0);
+    uint4 v = uint4{0u, 0u, 0u, 0u};
+    if (k < G && n < H) {
+      if (vec) {
+        v = *reinterpret_cast<const uint4*>(Rp + row * H + n);
+      } else {
+        T t[VE];
+#pragma unroll
+        for (int e = 0; e < VE; ++e) t[e] = n + e < H ? Rp[row * H + n + e] : T(0);
+        __builtin_memcpy(&v, t, 16);
+      }
+    }
+    *reinterpret_cast<uint4*>(&tile[kr][nc]) = v;
   }
   __syncthreads();
   // 4 row tiles x 2 halves x 64 lanes of 16 bytes
@@ -424,25 +449,46 @@ RecShape rec_shape(int B, int H, bool bf16) {
 struct BwdLayout {
   size_t ctl, flg, dpx, prt, rtf, dpf, wt, dp, dph, dpt, ut, ht, dy0, dy1, dhp, dcrec, colp, spl, total;
   RecShape rs;
-  bool resident;  // the chain runs in lstm_bwd_res_kernel
+  int res_nci;  // > 0: the chain runs in lstm_bwd_res_kernel with this many chunks per wave
+  int res_nw;   // ... and this many batch tiles (1, 2 or 4; 3 runs as 4)
 };
 
-// The on-chip chain kernel's shape: bf16, H = 4096 (4 K-groups of 64 chunks of
-// 64 columns; 48 register and 16 LDS blocks per wave), at most two batch tiles.
-// The on-chip chain's shape: bf16, H = 4 waves x 16 chunks x 64 (each
-// workgroup's K quarter), one or two batch tiles; 4 H / 16 workgroups.
-bool bwd_resident_shape(const lstm_desc_t* d) {
-  // (the kernel's exchange and partial-sum offsets are 32-bit: T slots of 2
-  // batch tiles x 256 chunks x 1024 elements, and T + 1 slots of 2^19
-  // partial sums, stay below 2^31)
-  return d->dtype == LSTM_BF16 && d->H == kBwdResWaves * kBwdResNCI * 64 && d->B <= 32 &&
-         (long long)(d->T + 1) * 2 * (4 * d->H / 64) * 1024 < (1LL << 31);
+// Batch tiles the on-chip chain runs for B sequences (its instantiations take
+// 1, 2 or 4; a third tile runs as a fourth, all padding).
+int bwd_res_nw(int B) {
+  const int nbt = (B + 15) / 16;
+  return nbt <= 2 ? nbt : 4;
+}
+
+// The on-chip chain's shape for a problem: NCI, the chunks of KC columns of
+// each wave's share of a workgroup's K quarter (H / (4 KC)), when kBwdResShape
+// has it; 0 otherwise (the streamed chain runs).  H must be a multiple of 256
+// (whole unit groups of 64 per K quarter) and B at most 64 (32 at NCI = 16).
+int bwd_resident_nci(const lstm_desc_t* d) {
+  const bool bf16 = d->dtype == LSTM_BF16;
+  const int KC = bf16 ? 64 : 32;
+  if (d->cell != LSTM_CELL_LSTM || d->H % 256 != 0 || d->B > 64) return 0;
+  const int nci = d->H / (4 * KC), nw = bwd_res_nw(d->B);
+  bool listed = false;
+  for (const BwdResShape& sh : kBwdResShape) listed = listed || (sh.bf16 == (bf16 ? 1 : 0) && sh.nci == nci);
+  if (!listed || nw > (nci >= 16 ? 2 : 4)) return 0;
+  // the kernel's per-step offsets are 32-bit: T + 1 slots of the dp exchange
+  // (nw tiles x 4H / KC chunks x 2 KiB) and the T B 4H saved gates
+  const long long xslot = (long long)nw * (4LL * d->H / KC) * (2048 / (bf16 ? 2 : 4));
+  if ((long long)(d->T + 1) * xslot >= (1LL << 31) || (long long)d->T * d->B * 4 * d->H >= (1LL << 31)) return 0;
+  return nci;
 }
 int bwd_res_wgs(int H) { return 4 * (H / 64); }
 
-const void* bwd_res_fn(int nw) {
-  return nw == 1 ? reinterpret_cast<const void*>(&lstm_bwd_res_kernel<true, 1>)
-                 : reinterpret_cast<const void*>(&lstm_bwd_res_kernel<true, 2>);
+const void* bwd_res_fn(bool bf16, int nci, int nw) {
+  const void* (*const per_shape[kBwdResShapes])(int) = {
+      bwd_res_kernel_ptr_shape0, bwd_res_kernel_ptr_shape1, bwd_res_kernel_ptr_shape2,
+      bwd_res_kernel_ptr_shape3, bwd_res_kernel_ptr_shape4, bwd_res_kernel_ptr_shape5,
+      bwd_res_kernel_ptr_shape6, bwd_res_kernel_ptr_shape7, bwd_res_kernel_ptr_shape8};
+  static_assert(kBwdResShapes == 9, "one compile unit per shape");
+  for (int k = 0; k < kBwdResShapes; ++k)
+    if (kBwdResShape[k].bf16 == (bf16 ? 1 : 0) && kBwdResShape[k].nci == nci) return per_shape[k](nw);
+  return nullptr;
 }
 
 // Compute units and wall-clock rate (kHz) of the current device, once per device.
@@ -479,7 +525,9 @@ bool bwd_layout(const lstm_desc_t* d, BwdLayout* o) {
   const size_t H = d->H, B = d->B, TB = (size_t)d->T * d->B, G = 4 * H;
   const size_t Imax = std::max<size_t>(d->I, H);
   o->rs = rec_shape(d->B, d->H, d->dtype == LSTM_BF16);
-  o->resident = bwd_resident_shape(d);
+  o->res_nci = bwd_resident_nci(d);
+  o->res_nw = bwd_res_nw(d->B);
+  const bool resident = o->res_nci > 0;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -489,9 +537,9 @@ bool bwd_layout(const lstm_desc_t* d, BwdLayout* o) {
   o->ctl = take(256);  // the error word first, as in the forward's workspace
   // the on-chip chain: two sets of step counters, the dp exchange, the partial sums
   const int rwgs = bwd_res_wgs(d->H);
-  o->flg = take(o->resident ? (size_t)2 * rwgs * kFlagStride * 4 : 0);
-  o->dpx = take(o->resident ? (size_t)d->T * o->rs.nbt * o->rs.nch * 2048 : 0);
-  o->prt = take(o->resident ? (size_t)(d->T + 1) * bwd_res_part_floats(rwgs, o->rs.nbt) * 4 : 0);
+  o->flg = take(resident ? (size_t)2 * rwgs * kFlagStride * 4 : 0);
+  o->dpx = take(resident ? (size_t)d->T * o->res_nw * o->rs.nch * 2048 : 0);
+  o->prt = take(resident ? (size_t)(d->T + 1) * bwd_res_part_floats(rwgs, o->res_nw) * 4 : 0);
   o->rtf = take((size_t)o->rs.nt16 * o->rs.nch * 2048);
   o->dpf = take((size_t)o->rs.nbt * o->rs.nch * 2048);
   o->wt = take(Imax * G * s);
@@ -611,13 +659,17 @@ lstm_status_t bwd_run(const lstm_desc_t* d, const void* x, const void* h0, const
   // streamed chain runs
   int cus = 0, clk_khz = 0;
   CHECK(bwd_device(&cus, &clk_khz));
-  bool resident = o.resident;
-  const int res_nw = (B + 15) / 16;
-  const int res_lds = bwd_res_lds_bytes(res_nw);
+  // (its per-step loads and stores are 16 bytes wide: the caller's per-step
+  // tensors must be 16-byte aligned, as torch allocations are)
+  bool resident = o.res_nci > 0 && aligned16(dy) && aligned16(reserve) && aligned16(c0) && aligned16(dhT) &&
+                  aligned16(dcT) && aligned16(dh0) && aligned16(dc0);
+  const int res_nw = o.res_nw;
+  const int res_lds = resident ? bwd_res_lds_bytes(res_nw, o.res_nci) : 0;
   const int res_wgs = bwd_res_wgs(H);
+  const void* res_fn = resident ? bwd_res_fn(BF16, o.res_nci, res_nw) : nullptr;
   if (resident) {
     int per_cu = 0;
-    if (prepare_fn(bwd_res_fn(res_nw), res_lds, 64 * kBwdResWaves, &per_cu) != hipSuccess ||
+    if (!res_fn || prepare_fn(res_fn, res_lds, 64 * kBwdResWaves, &per_cu) != hipSuccess ||
         (long)per_cu * cus < res_wgs) {
       (void)hipGetLastError();
       resident = false;
@@ -642,12 +694,13 @@ lstm_status_t bwd_run(const lstm_desc_t* d, const void* x, const void* h0, const
     const char* hs = rsv + (size_t)L * tbh * 20 + (size_t)l * tbh * s;
     // R_l^T in load order: the per-step product's streamed operand
     // (K unit-major for the on-chip chain)
+    const int rt_vec = aligned16(Rl) && H % (16 / (BF16 ? 2 : 4)) == 0;
     if (resident)
       hipLaunchKernelGGL((bwd_block_rt<BF16, true>), dim3((H + 63) / 64, rs.nch), dim3(kBwdThreads), 0, st,
-                         static_cast<const void*>(Rl), H, rs.nch, static_cast<uint4*>(RTf));
+                         static_cast<const void*>(Rl), H, rs.nch, rt_vec, static_cast<uint4*>(RTf));
     else
       hipLaunchKernelGGL((bwd_block_rt<BF16, false>), dim3((H + 63) / 64, rs.nch), dim3(kBwdThreads), 0, st,
-                         static_cast<const void*>(Rl), H, rs.nch, static_cast<uint4*>(RTf));
+                         static_cast<const void*>(Rl), H, rs.nch, rt_vec, static_cast<uint4*>(RTf));
     CHECK(hipGetLastError());
     if (resident) {
       const long nflag = (long)2 * res_wgs * kFlagStride * 4 / 16;
@@ -657,7 +710,7 @@ lstm_status_t bwd_run(const lstm_desc_t* d, const void* x, const void* h0, const
       BwdResParams P{};
       P.RTf = static_cast<const uint4*>(RTf);
       P.DPx = w + o.dpx;
-      P.xslot = (long long)rs.nbt * rs.nch * 2048 / (long long)s;
+      P.xslot = (long long)res_nw * rs.nch * 2048 / (long long)s;
       P.dY = dY;
       P.gates = gates;
       P.cs = cs;
@@ -678,9 +731,9 @@ lstm_status_t bwd_run(const lstm_desc_t* d, const void* x, const void* h0, const
       P.xcd_remap = 1;
       void* args[] = {&P};
       if (plain)
-        CHECK(hipLaunchKernel(bwd_res_fn(res_nw), dim3(P.grid), dim3(64 * kBwdResWaves), args, (unsigned)res_lds, st));
+        CHECK(hipLaunchKernel(res_fn, dim3(P.grid), dim3(64 * kBwdResWaves), args, (unsigned)res_lds, st));
       else
-        CHECK(hipLaunchCooperativeKernel(bwd_res_fn(res_nw), dim3(P.grid), dim3(64 * kBwdResWaves), args,
+        CHECK(hipLaunchCooperativeKernel(res_fn, dim3(P.grid), dim3(64 * kBwdResWaves), args,
                                          (unsigned)res_lds, st));
     }
     for (int t = T - 1; t >= 0 && !resident; --t) {
@@ -766,6 +819,11 @@ lstm_status_t lstm_bwd_last_error(const void* ws, hipStream_t stream) {
 size_t lstm_bwd_workspace_size(const lstm_desc_t* d) {
   BwdLayout o;
   return bwd_layout(d, &o) ? o.total : 0;
+}
+
+int lstm_bwd_chain_on_chip(const lstm_desc_t* d) {
+  BwdLayout o;
+  return bwd_layout(d, &o) && o.res_nci > 0 ? 1 : 0;
 }
 
 lstm_status_t lstm_bwd_ex(const lstm_desc_t* d, const void* x, const void* h0, const float* c0, const void* W,

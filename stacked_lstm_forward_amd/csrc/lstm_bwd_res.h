@@ -8,22 +8,25 @@
 // the forward's resident kernel, R_l^T stays in registers and LDS for the
 // whole chain, and per step only dp_{t+1} is read.
 //
-// Work split (H = 4096: 256 workgroups, one per CU).  The K index of the
-// product is ordered unit-major, k = 4 u + g for gate g of unit u (R_l^T and
-// the exchanged dp use the same order, so the product is unchanged).
-// Workgroup v = 4 ug + kq owns output units 64 ug .. 64 ug + 63 (four M-tiles
-// of 16) and the K quarter kq: input units 1024 kq .. 1024 kq + 1023, all four
-// gates.  So it reads a quarter of dp_{t+1} per step (256 KiB at B = 32, not
-// all of it: one workgroup per 16 units reading all 1 MiB took 18.5 us a
-// step, bound by those reads), and the four workgroups of a unit group add
-// their partial sums: each leaves its sums in a per-step slot, then
-// workgroup (ug, kq) adds the four partials of M-tile kq in a fixed order and
-// finishes those 16 units (the elementwise part) for every sequence.
+// Work split (H a multiple of 256: H / 16 workgroups, one per CU; 256 at
+// H = 4096).  The K index of the product is ordered unit-major, k = 4 u + g
+// for gate g of unit u (R_l^T and the exchanged dp use the same order, so the
+// product is unchanged).  Workgroup v = 4 ug + kq owns output units 64 ug ..
+// 64 ug + 63 (four M-tiles of 16) and the K quarter kq: input units H / 4 kq
+// .. H / 4 (kq + 1) - 1, all four gates.  So it reads a quarter of dp_{t+1}
+// per step (256 KiB at bf16 H = 4096, B = 32, not all of it: one workgroup per
+// 16 units reading all 1 MiB took 18.5 us a step, bound by those reads), and
+// the four workgroups of a unit group add their partial sums: each leaves its
+// sums in a per-step slot, then workgroup (ug, kq) adds the four partials of
+// M-tile kq in a fixed order and finishes those 16 units (the elementwise
+// part) for every sequence.
 // Inside a workgroup, as in the forward: wave w is K-group w of 4 and owns
-// chunks w, w + 4, ... of the quarter (16 chunks of 64) of every M-tile: 48
-// fragment blocks in registers, one per chunk (16) in LDS; the column tiles
-// run one after the other with one stream of dp loads five chunks ahead; the
-// four waves' sums meet in LDS.
+// chunks w, w + 4, ... of the quarter (NCI = H / (4 KC) chunks of KC: 16 at
+// bf16 H = 4096) of every M-tile: NRB fragment blocks in registers and the
+// others in LDS, spread evenly over the chunks (at H = 4096: 48 and one per
+// chunk, 16; smaller layers: three M-tiles of every chunk in registers, one
+// in LDS); the column tiles run one after the other with one stream of dp
+// loads five chunks ahead; the four waves' sums meet in LDS.
 //
 // Step protocol, two counters per workgroup (agent-scope stores, bounded
 // waits with the error word):
@@ -62,14 +65,28 @@ struct BwdResParams {
 };
 
 constexpr int kBwdResWaves = 4;
-constexpr int kBwdResMW = 4;    // M-tiles (of 16 output units) per workgroup
-constexpr int kBwdResNCI = 16;  // chunks of the K quarter per wave (H = 4096)
-constexpr int kBwdResNRB = 48;  // ... of whose blocks in registers
-constexpr int kBwdResPf = 7;    // per-step inputs of one (unit, sequence): dY, i, f, g, o, c_t, c_{t-1}
+constexpr int kBwdResMW = 4;  // M-tiles (of 16 output units) per workgroup
+constexpr int kBwdResPf = 7;  // per-step inputs of one (unit, sequence): dY, i, f, g, o, c_t, c_{t-1}
+
+// Fragment blocks (of each wave's MW NCI) kept in registers, for NCI chunks
+// of the K quarter per wave: 48 of 64 at NCI = 16 (bf16 H = 4096), else three
+// of the four M-tiles of every chunk.
+__host__ __device__ constexpr int bwd_res_nrb(int nci) { return nci >= 16 ? 48 : 3 * nci; }
+
+// The instantiated shapes, (bf16, NCI): NCI = H / (4 KC), so H = 4096, 256,
+// 512, 1024, 1536 and 2048 in bf16 and 256, 512 and 1024 in fp32.  Each is
+// built with 1, 2 and 4 batch tiles (NCI = 16: 1 and 2), one compile unit per
+// shape (lstm_bwd_res_inst.hip).
+struct BwdResShape {
+  int bf16, nci;
+};
+constexpr int kBwdResShapes = 9;
+constexpr BwdResShape kBwdResShape[kBwdResShapes] = {{1, 16}, {1, 1}, {1, 2}, {1, 4}, {1, 6},
+                                                      {1, 8},  {0, 2}, {0, 4}, {0, 8}};
 
 // LDS bytes: the LDS weight blocks, one tile's partial sums, the parked inputs.
-__host__ __device__ constexpr int bwd_res_lds_bytes(int nw) {
-  return kBwdResWaves * (kBwdResMW * kBwdResNCI - kBwdResNRB) * 2048 + kBwdResMW * kBwdResWaves * 64 * 16 +
+__host__ __device__ constexpr int bwd_res_lds_bytes(int nw, int nci) {
+  return kBwdResWaves * (kBwdResMW * nci - bwd_res_nrb(nci)) * 2048 + kBwdResMW * kBwdResWaves * 64 * 16 +
          nw * kBwdResPf * 256 * 4;
 }
 
@@ -87,14 +104,14 @@ __host__ __device__ constexpr long long bwd_res_part_floats(int wgs, int nw) {
   return (long long)wgs * nw * kBwdResMW * 64 * 4;
 }
 
-template <bool BF16, int NW>
+template <bool BF16, int NW, int NCI>
 __global__ void __launch_bounds__(64 * kBwdResWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
 lstm_bwd_res_kernel(const BwdResParams P) {
   typedef typename Dt<BF16>::T T;
   typedef ResOps<BF16> Ops;
   typedef typename Ops::V V;
-  constexpr int SZ = Dt<BF16>::SZ;
-  constexpr int KS = kBwdResWaves, MW = kBwdResMW, NCI = kBwdResNCI, NRB = kBwdResNRB;
+  constexpr int SZ = Dt<BF16>::SZ, KC = Dt<BF16>::KC;
+  constexpr int KS = kBwdResWaves, MW = kBwdResMW, NRB = bwd_res_nrb(NCI);
   constexpr int NB = MW * NCI, NLB = NB - NRB, LPC = NLB / NCI, RPC = MW - LPC;
   static_assert(NLB % NCI == 0 && LPC >= 1, "LDS blocks spread evenly over the chunks");
   constexpr int FB = 2048 / SZ, EPH = 16 / SZ;
@@ -111,7 +128,11 @@ lstm_bwd_res_kernel(const BwdResParams P) {
   const int H = P.H, B = P.B, T_ = P.T, nch = P.nch;
   uint4* As = reinterpret_cast<uint4*>(smem) + (long)kg * NLB * 128;
   f32x4* red = reinterpret_cast<f32x4*>(smem + KS * NLB * 2048);
-  float* pf = reinterpret_cast<float*>(smem + KS * NLB * 2048 + MW * KS * 64 * 16);
+  f32x4* pf = reinterpret_cast<f32x4*>(smem + KS * NLB * 2048 + MW * KS * 64 * 16);
+  // LDS byte address of this wave's input area (M0 takes LDS addresses)
+  typedef __attribute__((address_space(3))) unsigned char lds_byte_t;
+  const uint32_t pf_lds = (uint32_t)(uintptr_t)(lds_byte_t*)(smem + KS * NLB * 2048 + MW * KS * 64 * 16) +
+                          (uint32_t)(kg * kBwdResPf) * 1024;
 
   // ---- this wave's blocks of R_l^T: M-tile 4 ug + i, chunk 64 kq + kg + 4 ci
   // (M-tile i < RPC of chunk slot ci in register block ci RPC + i, the others
@@ -140,22 +161,26 @@ lstm_bwd_res_kernel(const BwdResParams P) {
     }
   }
 
-  // ---- the (unit, sequence) pair this thread finishes in column tile j:
-  // element kg of lane `lane`'s sums of M-tile kq, i.e. unit
-  // 64 ug + 16 kq + 4 (lane >> 4) + kg, sequence 16 j + (lane & 15)
-  const int unit = 64 * ug + 16 * kq + 4 * (lane >> 4) + kg;
-  const int bl = lane & 15;
-  float dcrec[NW];
-#pragma unroll
-  for (int j = 0; j < NW; ++j) {
-    const int b = 16 * j + bl;
-    dcrec[j] = (b < B && P.dcT) ? P.dcT[(long)b * H + unit] : 0.f;
-  }
-  // dp of this pair's unit in load order: k = 4 unit + g is chunk unit / 16,
-  // half (lane >> 4) >> 1, quad 2 ((lane >> 4) & 1) + kg / 2, element
-  // 4 (kg & 1) + g: the four gates are four consecutive elements
-  const unsigned xunit = (unsigned)(unit / 16) * FB + ((lane >> 4) >> 1) * (FB / 2) +
-                         ((2 * ((lane >> 4) & 1) + kg / 2) * 16) * EPH + 4 * (kg & 1);
+  // ---- what this thread finishes: wave kg < NW finishes column tile kg of
+  // M-tile kq, lane `lane` the four units u0 .. u0 + 3 of sequence fb (the
+  // lane's four sums of that tile, so every per-step load and store is 16
+  // bytes); the other waves only multiply
+  const int u0 = 64 * ug + 16 * kq + 4 * (lane >> 4);
+  const int fb = min(16 * kg + (lane & 15), B - 1);  // clamped for the loads of padding lanes
+  const bool fwave = kg < NW;                        // wave-uniform
+  const bool fin = fwave && 16 * kg + (lane & 15) < B;
+  f32x4 dcrec = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (fin && P.dcT) dcrec = *reinterpret_cast<const f32x4*>(P.dcT + (long)fb * H + u0);
+  // dp of the four units in load order: k = 4 u0 .. 4 u0 + 15 lie in chunk
+  // 4 u0 / KC from column kc0 = 4 u0 % KC: half kc0 / (KC / 2), quads from
+  // (kc0 % (KC / 2)) / EPH on, each quad one lane's 16 bytes (two units' four
+  // gates in bf16, one unit's in fp32), 256 bytes apart; byte offset of the
+  // first in column tile kg's part of an exchange slot:
+  const int xkc = (4 * u0) % KC;
+  const int xoff = ((kg * nch + (4 * u0) / KC) * FB + (xkc / (KC / 2)) * (FB / 2) +
+                    (((xkc % (KC / 2)) / EPH) * 16 + (fb & 15)) * EPH) *
+                   SZ;
+  const int xbytes = (int)(P.xslot * SZ);
 
   T* DPx = reinterpret_cast<T*>(P.DPx);
   T* dPh = reinterpret_cast<T*>(P.dPh);
@@ -167,21 +192,23 @@ lstm_bwd_res_kernel(const BwdResParams P) {
   for (int s = 0; s <= T_; ++s) {
     const int t = T_ - 1 - s;  // step whose dp this iteration computes (-1: dh0 only)
     if (t < 0 && !P.dh0) break;
-    // per-step inputs of this thread's pairs, loaded before the waits
-    float in[NW][kBwdResPf];
-    if (t >= 0) {
+    // per-step inputs of this thread's units, loaded before the waits
+    // straight into this wave's LDS area (no registers held across the
+    // waits; read after a vmcnt wait): dY, i, f, g, o, c_t, c_{t-1}.  Bases
+    // per step (wave-uniform), 32-bit byte offsets within a step's rows.
+    if (t >= 0 && fwave) {
+      const long tb = (long)t * B;
+      const uint32_t rh = (uint32_t)(fb * H + u0) * 4, rg = (uint32_t)(fb * 4 * H + u0) * 4;
+      dma16(P.dY + tb * H, rh, pf_lds);
 #pragma unroll
-      for (int j = 0; j < NW; ++j) {
-        // (32-bit offsets from the arguments' base addresses: the host keeps
-        // T B 4H and every exchange and partial-sum offset below 2^31)
-        const int b = min(16 * j + bl, B - 1);
-        const unsigned bh = (unsigned)(t * B + b) * H + unit, g4 = (unsigned)(t * B + b) * 4 * H + unit;
-        in[j][0] = P.dY[bh];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) in[j][1 + k] = P.gates[g4 + (unsigned)(k * H)];
-        in[j][5] = P.cs[bh];
-        in[j][6] = t > 0 ? P.cs[bh - (unsigned)(B * H)] : (P.c0 ? P.c0[(unsigned)(b * H + unit)] : 0.f);
-      }
+      for (int k = 0; k < 4; ++k) dma16(P.gates + tb * 4 * H, rg + (uint32_t)(k * H) * 4, pf_lds + (1 + k) * 1024);
+      dma16(P.cs + tb * H, rh, pf_lds + 5 * 1024);
+      if (t > 0)
+        dma16(P.cs + (tb - B) * H, rh, pf_lds + 6 * 1024);
+      else if (P.c0)
+        dma16(P.c0, rh, pf_lds + 6 * 1024);
+      else
+        pf[(kg * kBwdResPf + 6) * 64 + lane] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     if (s > 0) {
       // dp_{t+1} of this quarter's units: finished by the quarter's workgroups
@@ -195,16 +222,7 @@ lstm_bwd_res_kernel(const BwdResParams P) {
       __syncthreads();
       if (!s_ok) return;
     }
-    if (t >= 0) {
-#pragma unroll
-      for (int j = 0; j < NW; ++j)
-#pragma unroll
-        for (int k = 0; k < kBwdResPf; ++k) pf[(j * kBwdResPf + k) * 256 + tid] = in[j][k];
-    }
-
-    float dhr[NW];
-#pragma unroll
-    for (int j = 0; j < NW; ++j) dhr[j] = 0.f;
+    f32x4 dhr = f32x4{0.f, 0.f, 0.f, 0.f};
     if (s > 0) {
       // ---- this workgroup's partial dh_rec = dp_{t+1} R_l over its K quarter
       const T* src = DPx + (long)(t + 1) * P.xslot + (long)(NCI * KS * kq) * FB;
@@ -279,53 +297,60 @@ lstm_bwd_res_kernel(const BwdResParams P) {
       }
       __syncthreads();
       if (!s_ok) return;
-      const float* pin = P.part + (long)s * pslot + (long)(4 * ug) * (NW * MW * 256);
+      if (fwave) {
+        const f32x4* pin = reinterpret_cast<const f32x4*>(P.part + (long)s * pslot + (long)(4 * ug) * (NW * MW * 256)) +
+                           (kg * MW + kq) * 64 + lane;
+        dhr = pin[0];
 #pragma unroll
-      for (int j = 0; j < NW; ++j)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) dhr[j] += pin[(long)w * (NW * MW * 256) + ((j * MW + kq) * 64 + lane) * 4 + kg];
+        for (int w = 1; w < 4; ++w) dhr += pin[w * (NW * MW * 64)];
+      }
     }
 
-    // ---- the elementwise part of this thread's pairs (the exchange copy of
+    // ---- the elementwise part of this thread's units (the exchange copy of
     // dp first: the step counter waits only for it; dP and its dtype copy,
     // read by later kernels, are stored after the counter)
-    float dps[NW][4];
-#pragma unroll
-    for (int j = 0; j < NW; ++j) {
-      const int b = 16 * j + bl;
-      if (b >= B) continue;
-      const unsigned bh = (unsigned)(b * H + unit);
+    f32x4 dps[4];  // dps[g][e]: gate g of unit u0 + e
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's direct-to-LDS input loads
+    if (fin) {
+      const long fbh = (long)fb * H + u0;
       if (t < 0) {
-        P.dh0[bh] = dhr[j];
-        continue;
-      }
-      const float* x = pf + j * kBwdResPf * 256 + tid;
-      const float ig = x[1 * 256], fg = x[2 * 256], gg = x[3 * 256], og = x[4 * 256];
-      const float ct = x[5 * 256], cp = x[6 * 256];
-      const float dh = x[0] + (s > 0 ? dhr[j] : (P.dhT ? P.dhT[bh] : 0.f));
-      const float tc = tanh_f(ct);
-      const float dc = dh * og * (1.f - tc * tc) + dcrec[j];
-      const float d[4] = {dc * gg * ig * (1.f - ig), dc * cp * fg * (1.f - fg), dc * ig * (1.f - gg * gg),
-                          dh * tc * og * (1.f - og)};
-      dcrec[j] = dc * fg;
-      T hv[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        dps[j][k] = d[k];
-        hv[k] = from_float<BF16>(d[k]);
-      }
-      // the four gates' dp as one 8-byte word of the exchange
-      const unsigned xo = (unsigned)t * (unsigned)P.xslot + (unsigned)((b >> 4) * nch) * FB + xunit + (b & 15) * EPH;
-      if constexpr (BF16) {
-        const unsigned long long wv = (unsigned long long)hv[0] | ((unsigned long long)hv[1] << 16) |
-                                      ((unsigned long long)hv[2] << 32) | ((unsigned long long)hv[3] << 48);
-        __hip_atomic_store(reinterpret_cast<unsigned long long*>(DPx + xo), wv, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+        *reinterpret_cast<f32x4*>(P.dh0 + fbh) = dhr;
       } else {
+        const f32x4* x = pf + kg * kBwdResPf * 64 + lane;
+        const f32x4 ig = x[1 * 64], fg = x[2 * 64], gg = x[3 * 64], og = x[4 * 64], ct = x[5 * 64], cp = x[6 * 64];
+        const f32x4 dh =
+            x[0] + (s > 0 ? dhr : (P.dhT ? *reinterpret_cast<const f32x4*>(P.dhT + fbh) : f32x4{0.f, 0.f, 0.f, 0.f}));
 #pragma unroll
-        for (int k = 0; k < 4; ++k) store_coherent<BF16>(DPx + xo + k, hv[k]);
+        for (int e = 0; e < 4; ++e) {
+          const float tc = tanh_f(ct[e]);
+          const float dc = dh[e] * og[e] * (1.f - tc * tc) + dcrec[e];
+          dps[0][e] = dc * gg[e] * ig[e] * (1.f - ig[e]);
+          dps[1][e] = dc * cp[e] * fg[e] * (1.f - fg[e]);
+          dps[2][e] = dc * ig[e] * (1.f - gg[e] * gg[e]);
+          dps[3][e] = dh[e] * tc * og[e] * (1.f - og[e]);
+          dcrec[e] = dc * fg[e];
+        }
+        // the exchange: unit u0 + e's four gates are elements 4 e .. 4 e + 3
+        // of the 16 (EPH per 16-byte quad)
+        const __amdgpu_buffer_rsrc_t xrs = raw_buffer(DPx + (long)t * P.xslot, xbytes);
+        if constexpr (BF16) {
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            unsigned w[4];
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+              const int e = 2 * p + h / 2, g = 2 * (h % 2);
+              w[h] = (unsigned)from_float<true>(dps[g][e]) | ((unsigned)from_float<true>(dps[g + 1][e]) << 16);
+            }
+            store16_coherent(xrs, xoff + p * 256, __builtin_bit_cast(f32x4, make_uint4(w[0], w[1], w[2], w[3])));
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            store16_coherent(xrs, xoff + e * 256, f32x4{dps[0][e], dps[1][e], dps[2][e], dps[3][e]});
+        }
+        if (t == 0 && P.dc0) *reinterpret_cast<f32x4*>(P.dc0 + fbh) = dcrec;
       }
-      if (t == 0 && P.dc0) P.dc0[bh] = dcrec[j];
     }
     if (t < 0) break;
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -333,15 +358,18 @@ lstm_bwd_res_kernel(const BwdResParams P) {
     __syncthreads();
     if (tid == 0)
       __hip_atomic_store(P.flags_d + (long)v * kFlagStride, s + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (fin) {
+      const unsigned row = (unsigned)(t * B + fb) * 4 * H + u0;
 #pragma unroll
-    for (int j = 0; j < NW; ++j) {
-      const int b = 16 * j + bl;
-      if (b >= B) continue;
-      const unsigned row = (unsigned)(t * B + b) * 4 * H + unit;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        P.dP[row + (unsigned)(k * H)] = dps[j][k];
-        dPh[row + (unsigned)(k * H)] = from_float<BF16>(dps[j][k]);
+      for (int g = 0; g < 4; ++g) {
+        *reinterpret_cast<f32x4*>(P.dP + row + (unsigned)(g * H)) = dps[g];
+        if constexpr (BF16) {
+          const unsigned lo = (unsigned)from_float<true>(dps[g][0]) | ((unsigned)from_float<true>(dps[g][1]) << 16);
+          const unsigned hi = (unsigned)from_float<true>(dps[g][2]) | ((unsigned)from_float<true>(dps[g][3]) << 16);
+          *reinterpret_cast<uint2*>(dPh + row + (unsigned)(g * H)) = make_uint2(lo, hi);
+        } else {
+          *reinterpret_cast<f32x4*>(dPh + row + (unsigned)(g * H)) = dps[g];
+        }
       }
     }
   }

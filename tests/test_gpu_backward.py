@@ -96,9 +96,12 @@ def test_gpu_backward_small(dev, shape, dtype):
 @pytest.mark.parametrize("name,T", [("c1", None), ("c2", 12), ("c3", 12), ("c5", 64)])
 def test_gpu_backward_workload_shapes(dev, name, T):
     """The workloads' shapes (T cut where noted), zero initial states, dy only."""
+    import stacked_lstm_forward_amd as sl
     cfg = li.CONFIGS[name]
     if T is not None:
         cfg = li.Config(f"{cfg.name}-T{T}", cfg.cfg_id, cfg.L, cfg.I, cfg.H, cfg.B, T, cfg.dtype)
+    # c2, c3 and c5 run the chain on chip, c1 (H = 128) streams it
+    assert sl.lstm_bwd_chain_on_chip(sl.make_desc(cfg.L, cfg.I, cfg.H, cfg.B, cfg.T, cfg.dtype)) == (name != "c1")
     inp = li.make_inputs(cfg)
     dy, _, _ = upstream(cfg, 810, with_states=False)
     say(f"backward workload {cfg.name}")
@@ -125,6 +128,34 @@ def test_gpu_backward_on_chip_chain(dev, B, states):
     run_and_check(inp, dy, dhT, dcT, dev, f"bwd chain H4096 B={B}")
 
 
+# the on-chip chain at its other shapes: every (dtype, H) it is built for
+# below H = 4096, one to four batch tiles (a third tile runs as a padded
+# fourth), with and without upstream state gradients
+ON_CHIP = [
+    # L, I, H, B, T, dtype, states
+    (2, 64, 256, 40, 5, "bf16", True),
+    (1, 96, 512, 20, 6, "bf16", False),
+    (1, 128, 1024, 5, 4, "bf16", True),
+    (1, 64, 1536, 4, 5, "bf16", False),
+    (1, 64, 2048, 64, 3, "bf16", True),
+    (2, 48, 256, 33, 5, "f32", True),
+    (1, 64, 512, 16, 4, "f32", False),
+    (1, 32, 1024, 48, 3, "f32", True),
+]
+
+
+@pytest.mark.parametrize("shape", ON_CHIP, ids=[f"{s[5]}-H{s[2]}-B{s[3]}-L{s[0]}" for s in ON_CHIP])
+def test_gpu_backward_on_chip_chain_shapes(dev, shape):
+    import stacked_lstm_forward_amd as sl
+    L, I, H, B, T, dtype, states = shape
+    assert sl.lstm_bwd_chain_on_chip(sl.make_desc(L, I, H, B, T, dtype))
+    cfg = li.custom_config(L, I, H, B, T, dtype, cfg_id=900 + H + B + L)
+    inp = li.make_inputs(cfg, random_state=True)
+    dy, dhT, dcT = upstream(cfg, 910 + H + B, with_states=states)
+    say(f"backward on-chip chain {shape}")
+    run_and_check(inp, dy, dhT, dcT, dev, f"bwd chain {dtype} H{H} B{B} L{L}")
+
+
 def test_gpu_backward_wavefront_and_layerwise_forward_agree(dev):
     """The training forward saves the same activations in both schedules."""
     import stacked_lstm_forward_amd as sl
@@ -138,9 +169,10 @@ def test_gpu_backward_wavefront_and_layerwise_forward_agree(dev):
 
 
 # dx, dh0 and dc0 are optional outputs (NULL: not written); the weight
-# gradients must not depend on them: the on-chip chain (bf16 H = 4096) and the
-# streamed chain, with and without a dh0 iteration
-@pytest.mark.parametrize("shape", [(1, 512, 4096, 16, 3, "bf16"), (2, 24, 20, 3, 5, "f32"), (2, 64, 64, 16, 4, "bf16")])
+# gradients must not depend on them: the on-chip chain (bf16 H = 4096 and 256,
+# fp32 H = 512) and the streamed chain, with and without a dh0 iteration
+@pytest.mark.parametrize("shape", [(1, 512, 4096, 16, 3, "bf16"), (2, 24, 20, 3, 5, "f32"), (2, 64, 64, 16, 4, "bf16"),
+                                   (2, 64, 256, 24, 4, "bf16"), (1, 32, 512, 8, 3, "f32")])
 def test_gpu_backward_without_input_gradients(dev, shape):
     import stacked_lstm_forward_amd as sl
     from stacked_lstm_forward_amd import runner
