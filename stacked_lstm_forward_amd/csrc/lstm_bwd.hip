@@ -537,7 +537,8 @@ bool bwd_layout(const lstm_desc_t* d, BwdLayout* o) {
   o->ctl = take(256);  // the error word first, as in the forward's workspace
   // the on-chip chain: two sets of step counters, the dp exchange, the partial sums
   const int rwgs = bwd_res_wgs(d->H);
-  o->flg = take(resident ? (size_t)2 * rwgs * kFlagStride * 4 : 0);
+  // (counters for up to res_nw batch groups of rwgs workgroups)
+  o->flg = take(resident ? (size_t)2 * o->res_nw * rwgs * kFlagStride * 4 : 0);
   o->dpx = take(resident ? (size_t)d->T * o->res_nw * o->rs.nch * 2048 : 0);
   o->prt = take(resident ? (size_t)(d->T + 1) * bwd_res_part_floats(rwgs, o->res_nw) * 4 : 0);
   o->rtf = take((size_t)o->rs.nt16 * o->rs.nch * 2048);
@@ -664,17 +665,24 @@ lstm_status_t bwd_run(const lstm_desc_t* d, const void* x, const void* h0, const
   bool resident = o.res_nci > 0 && aligned16(dy) && aligned16(reserve) && aligned16(c0) && aligned16(dhT) &&
                   aligned16(dcT) && aligned16(dh0) && aligned16(dc0);
   const int res_nw = o.res_nw;
-  const int res_lds = resident ? bwd_res_lds_bytes(res_nw, o.res_nci) : 0;
   const int res_wgs = bwd_res_wgs(H);
-  const void* res_fn = resident ? bwd_res_fn(BF16, o.res_nci, res_nw) : nullptr;
-  if (resident) {
+  // batch groups: the most (of res_nw, res_nw / 2, .., 1; each group runs
+  // res_nw / groups column tiles on its own res_wgs workgroups) whose grid
+  // is co-resident
+  int res_groups = 0, res_lds = 0;
+  const void* res_fn = nullptr;
+  for (int g = res_nw; resident && g >= 1 && !res_groups; g /= 2) {
+    const void* fn = bwd_res_fn(BF16, o.res_nci, res_nw / g);
+    const int lds = bwd_res_lds_bytes(res_nw / g, o.res_nci);
     int per_cu = 0;
-    if (!res_fn || prepare_fn(res_fn, res_lds, 64 * kBwdResWaves, &per_cu) != hipSuccess ||
-        (long)per_cu * cus < res_wgs) {
+    if (fn && prepare_fn(fn, lds, 64 * kBwdResWaves, &per_cu) == hipSuccess && (long)per_cu * cus >= (long)g * res_wgs) {
+      res_groups = g, res_fn = fn, res_lds = lds;
+    } else {
       (void)hipGetLastError();
-      resident = false;
     }
   }
+  if (!res_groups) resident = false;
+  const int res_all = res_groups * res_wgs;  // workgroups in all
   // the error word
   hipLaunchKernelGGL(bwd_zero, dim3(1), dim3(kBwdThreads), 0, st, reinterpret_cast<uint4*>(w + o.ctl), 16L);
   CHECK(hipGetLastError());
@@ -703,7 +711,7 @@ lstm_status_t bwd_run(const lstm_desc_t* d, const void* x, const void* h0, const
                          static_cast<const void*>(Rl), H, rs.nch, rt_vec, static_cast<uint4*>(RTf));
     CHECK(hipGetLastError());
     if (resident) {
-      const long nflag = (long)2 * res_wgs * kFlagStride * 4 / 16;
+      const long nflag = (long)2 * res_all * kFlagStride * 4 / 16;
       hipLaunchKernelGGL(bwd_zero, dim3((unsigned)std::min<long>((nflag + kBwdThreads - 1) / kBwdThreads, 64)),
                          dim3(kBwdThreads), 0, st, reinterpret_cast<uint4*>(w + o.flg), nflag);
       CHECK(hipGetLastError());
@@ -723,11 +731,11 @@ lstm_status_t bwd_run(const lstm_desc_t* d, const void* x, const void* h0, const
       P.dc0 = dc0 ? dc0 + (size_t)l * B * H : nullptr;
       P.part = reinterpret_cast<float*>(w + o.prt);
       P.flags_d = reinterpret_cast<int*>(w + o.flg);
-      P.flags_p = P.flags_d + (long)res_wgs * kFlagStride;
+      P.flags_p = P.flags_d + (long)res_all * kFlagStride;
       P.err = reinterpret_cast<int*>(w + o.ctl);
       P.timeout_ticks = kBwdTimeoutUs * clk_khz / 1000;
-      P.T = T, P.B = B, P.H = H, P.nch = rs.nch, P.wgs = res_wgs;
-      P.grid = (res_wgs + 7) & ~7;
+      P.T = T, P.B = B, P.H = H, P.nch = rs.nch, P.wgs = res_all, P.groups = res_groups;
+      P.grid = (res_all + 7) & ~7;
       P.xcd_remap = 1;
       void* args[] = {&P};
       if (plain)

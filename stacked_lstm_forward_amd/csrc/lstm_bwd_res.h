@@ -1,5 +1,6 @@
 // Persistent kernel of one layer's recurrent chain in the backward pass, with
-// R_l^T kept on chip (template definitions; instantiated in lstm_bwd.hip).
+// R_l^T kept on chip (template definitions; instantiated in
+// lstm_bwd_res_inst.hip).
 //
 // The chain runs t = T-1 .. 0: dh_t = dY[t] + dh_rec, dc_t = dh_t o (1 -
 // tanh(c_t)^2) + dc_rec, the gate derivatives dp_t, dc_rec <- dc_t f_t and
@@ -8,10 +9,10 @@
 // the forward's resident kernel, R_l^T stays in registers and LDS for the
 // whole chain, and per step only dp_{t+1} is read.
 //
-// Work split (H a multiple of 256: H / 16 workgroups, one per CU; 256 at
-// H = 4096).  The K index of the product is ordered unit-major, k = 4 u + g
+// Work split (H a multiple of 256: H / 16 workgroups per batch group, one
+// per CU; 256 at H = 4096).  The K index of the product is ordered unit-major, k = 4 u + g
 // for gate g of unit u (R_l^T and the exchanged dp use the same order, so the
-// product is unchanged).  Workgroup v = 4 ug + kq owns output units 64 ug ..
+// product is unchanged).  Workgroup v = 4 ug + kq (of its group) owns output units 64 ug ..
 // 64 ug + 63 (four M-tiles of 16) and the K quarter kq: input units H / 4 kq
 // .. H / 4 (kq + 1) - 1, all four gates.  So it reads a quarter of dp_{t+1}
 // per step (256 KiB at bf16 H = 4096, B = 32, not all of it: one workgroup per
@@ -27,15 +28,21 @@
 // chunk, 16; smaller layers: three M-tiles of every chunk in registers, one
 // in LDS); the column tiles run one after the other with one stream of dp
 // loads five chunks ahead; the four waves' sums meet in LDS.
+// Batch groups: sequences are independent, so when the GPU has room the
+// column tiles are split over `groups` copies of this grid (group jg takes
+// tiles NW jg .. NW jg + NW - 1, holds its own copy of R_l^T and runs its own
+// chain with its own counters); a small layer then spreads its products over
+// more CUs.
 //
 // Step protocol, two counters per workgroup (agent-scope stores, bounded
 // waits with the error word):
 //   flags_d[v] = s + 1 once iteration s's dp (of step T - 1 - s) is written;
 //   flags_p[v] = s + 1 once iteration s's partial sums are written.
-// Iteration s > 0 waits for flags_d >= s of the 64 workgroups that finish its
-// K quarter's units (workgroups 64 kq .. 64 kq + 63), multiplies, publishes
-// its partials and waits for flags_p >= s + 1 of its unit group's four
-// workgroups.  The iteration after the last step computes dh0 = dp_0 R_l.
+// Iteration s > 0 waits for flags_d >= s of the H / 64 workgroups of its
+// batch group that finish its K quarter's units (64 kq .. 64 kq + 63 at
+// H = 4096), multiplies, publishes its partials and waits for flags_p >= s + 1
+// of its unit group's four workgroups.  The iteration after the last step
+// computes dh0 = dp_0 R_l.
 #pragma once
 
 #include "lstm_rec_res.h"
@@ -61,7 +68,10 @@ struct BwdResParams {
   int* flags_p;         // ... of the partial sums
   int* err;             // device error word
   long long timeout_ticks;
-  int T, B, H, nch, wgs, grid, xcd_remap;
+  int T, B, H, nch;
+  int wgs;     // workgroups in all: groups x H / 16
+  int groups;  // batch groups: group jg takes column tiles NW jg .. NW jg + NW - 1 (an independent chain)
+  int grid, xcd_remap;
 };
 
 constexpr int kBwdResWaves = 4;
@@ -122,7 +132,10 @@ lstm_bwd_res_kernel(const BwdResParams P) {
   const int bid = blockIdx.x;
   const int v = P.xcd_remap ? ((bid & 7) * (P.grid >> 3) + (bid >> 3)) : bid;
   if (v >= P.wgs) return;
-  const int ug = v >> 2, kq = v & 3;
+  // batch group jg, and within it unit group ug and K quarter kq
+  const int wgs0 = P.wgs / P.groups, jg = v / wgs0, v0 = v - jg * wgs0;
+  const int ug = v0 >> 2, kq = v0 & 3;
+  const int gw0 = jg * wgs0;  // the group's first workgroup
   const int tid = threadIdx.x, lane = tid & 63;
   const int kg = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = P.H, B = P.B, T_ = P.T, nch = P.nch;
@@ -166,9 +179,10 @@ lstm_bwd_res_kernel(const BwdResParams P) {
   // lane's four sums of that tile, so every per-step load and store is 16
   // bytes); the other waves only multiply
   const int u0 = 64 * ug + 16 * kq + 4 * (lane >> 4);
-  const int fb = min(16 * kg + (lane & 15), B - 1);  // clamped for the loads of padding lanes
+  const int jt = NW * jg + kg;                       // its column tile
+  const int fb = min(16 * jt + (lane & 15), B - 1);  // clamped for the loads of padding lanes
   const bool fwave = kg < NW;                        // wave-uniform
-  const bool fin = fwave && 16 * kg + (lane & 15) < B;
+  const bool fin = fwave && 16 * jt + (lane & 15) < B;
   f32x4 dcrec = f32x4{0.f, 0.f, 0.f, 0.f};
   if (fin && P.dcT) dcrec = *reinterpret_cast<const f32x4*>(P.dcT + (long)fb * H + u0);
   // dp of the four units in load order: k = 4 u0 .. 4 u0 + 15 lie in chunk
@@ -177,7 +191,7 @@ lstm_bwd_res_kernel(const BwdResParams P) {
   // gates in bf16, one unit's in fp32), 256 bytes apart; byte offset of the
   // first in column tile kg's part of an exchange slot:
   const int xkc = (4 * u0) % KC;
-  const int xoff = ((kg * nch + (4 * u0) / KC) * FB + (xkc / (KC / 2)) * (FB / 2) +
+  const int xoff = ((jt * nch + (4 * u0) / KC) * FB + (xkc / (KC / 2)) * (FB / 2) +
                     (((xkc % (KC / 2)) / EPH) * 16 + (fb & 15)) * EPH) *
                    SZ;
   const int xbytes = (int)(P.xslot * SZ);
@@ -212,10 +226,10 @@ lstm_bwd_res_kernel(const BwdResParams P) {
     }
     if (s > 0) {
       // dp_{t+1} of this quarter's units: finished by the quarter's workgroups
-      // (wgs / 4 of them: 64 kq .. 64 kq + 63 at H = 4096)
+      // in this batch group (H / 64 of them: 64 kq .. 64 kq + 63 at H = 4096)
       if (kg == 0) {
-        const int nq = P.wgs / 4;
-        const bool ok = wait_counts_serial(P.flags_d + (long)nq * kq * kFlagStride, nq, s, nullptr, 0, 0, P.err,
+        const int nq = wgs0 / 4;
+        const bool ok = wait_counts_serial(P.flags_d + (long)(gw0 + nq * kq) * kFlagStride, nq, s, nullptr, 0, 0, P.err,
                                            P.timeout_ticks);
         if (lane == 0) s_ok = ok ? 1 : 0;
       }
@@ -225,7 +239,7 @@ lstm_bwd_res_kernel(const BwdResParams P) {
     f32x4 dhr = f32x4{0.f, 0.f, 0.f, 0.f};
     if (s > 0) {
       // ---- this workgroup's partial dh_rec = dp_{t+1} R_l over its K quarter
-      const T* src = DPx + (long)(t + 1) * P.xslot + (long)(NCI * KS * kq) * FB;
+      const T* src = DPx + (long)(t + 1) * P.xslot + ((long)NW * jg * nch + NCI * KS * kq) * FB;
       const __amdgpu_buffer_rsrc_t drs = raw_buffer(src, (int)((long)NW * nch * FB * SZ));
       const __amdgpu_buffer_rsrc_t prs = raw_buffer(P.part + (long)s * pslot + (long)v * (NW * MW * 256), NW * MW * 1024);
       Frag rb[PD];
@@ -291,14 +305,14 @@ lstm_bwd_res_kernel(const BwdResParams P) {
         __hip_atomic_store(P.flags_p + (long)v * kFlagStride, s + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       // ---- the unit group's four partial sums of M-tile kq, in a fixed order
       if (kg == 0) {
-        const bool ok = wait_counts_serial(P.flags_p + (long)(4 * ug) * kFlagStride, 4, s + 1, nullptr, 0, 0, P.err,
+        const bool ok = wait_counts_serial(P.flags_p + (long)(gw0 + 4 * ug) * kFlagStride, 4, s + 1, nullptr, 0, 0, P.err,
                                            P.timeout_ticks);
         if (lane == 0) s_ok = ok ? 1 : 0;
       }
       __syncthreads();
       if (!s_ok) return;
       if (fwave) {
-        const f32x4* pin = reinterpret_cast<const f32x4*>(P.part + (long)s * pslot + (long)(4 * ug) * (NW * MW * 256)) +
+        const f32x4* pin = reinterpret_cast<const f32x4*>(P.part + (long)s * pslot + (long)(gw0 + 4 * ug) * (NW * MW * 256)) +
                            (kg * MW + kq) * 64 + lane;
         dhr = pin[0];
 #pragma unroll
