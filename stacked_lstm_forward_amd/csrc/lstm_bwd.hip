@@ -269,6 +269,7 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_colsum_slab(const float* dP, 
   if (k >= cols) return;
   const int r1 = min(rows, (z + 1) * kColSlab);
   float s = 0.f;
+#pragma unroll 8
   for (int r = z * kColSlab; r < r1; ++r) s += dP[(long)r * cols + k];
   part[(long)z * cols + k] = s;
 }
@@ -276,6 +277,7 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_colsum_final(const float* par
   const int k = blockIdx.x * kBwdThreads + threadIdx.x;
   if (k >= cols) return;
   float s = 0.f;
+#pragma unroll 8
   for (int z = 0; z < slabs; ++z) s += part[(long)z * cols + k];
   db[k] = s;
 }
@@ -451,7 +453,17 @@ struct BwdLayout {
   RecShape rs;
   int res_nci;  // > 0: the chain runs in lstm_bwd_res_kernel with this many chunks per wave
   int res_nw;   // ... and this many batch tiles (1, 2 or 4; 3 runs as 4)
+  size_t spl_floats;
 };
+
+// Floats of the buffer for the extra K ranges' partial sums of the gradient
+// products (launch_gemm_plain splits K when a product has too few tiles to
+// fill the GPU; each extra range needs a copy of C): one copy of the largest
+// T*B-row result (the input gradient), or up to 15 copies of the largest
+// weight gradient (4H x max(I, H)) within 64 MiB.
+size_t bwd_spl_floats(size_t TB, size_t G, size_t Imax) {
+  return std::max(TB * Imax, std::min(15 * G * Imax, (size_t)1 << 24));
+}
 
 // Batch tiles the on-chip chain runs for B sequences (its instantiations take
 // 1, 2 or 4; a third tile runs as a fourth, all padding).
@@ -554,7 +566,8 @@ bool bwd_layout(const lstm_desc_t* d, BwdLayout* o) {
   o->dhp = take((size_t)o->rs.S * B * H * 4);
   o->dcrec = take(B * H * 4);
   o->colp = take((TB + kColSlab - 1) / kColSlab * G * 4);
-  o->spl = take(TB * Imax * 4);  // one K range's partial sums of the input-gradient product
+  o->spl_floats = bwd_spl_floats(TB, G, Imax);
+  o->spl = take(o->spl_floats * 4);  // partial sums of the products' extra K ranges
   o->total = off;
   return true;
 }
@@ -646,7 +659,7 @@ lstm_status_t bwd_run(const lstm_desc_t* d, const void* x, const void* h0, const
   float* dcrec = reinterpret_cast<float*>(w + o.dcrec);
   float* colp = reinterpret_cast<float*>(w + o.colp);
   float* spl = reinterpret_cast<float*>(w + o.spl);  // partial sums of split products
-  const long long spl_floats = (long long)TB * std::max(I, H);
+  const long long spl_floats = (long long)o.spl_floats;
   const char* rsv = static_cast<const char*>(reserve);
   const size_t tbh = (size_t)T * B * H;
   const float* dY = dy;

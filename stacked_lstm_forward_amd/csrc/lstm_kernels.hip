@@ -495,6 +495,7 @@ __global__ void __launch_bounds__(256) gemm_split_sum(float* C, const float* C2,
   for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long long)gridDim.x * 256) {
     const long long o = (i / N) * ldc + i % N;
     float v = C[o];
+#pragma unroll 4
     for (int z = 0; z < parts; ++z) v += C2[z * S + o];
     C[o] = v;
   }
@@ -764,15 +765,16 @@ hipError_t launch_gemm_plain(bool bf16, const void* A, const void* B, float* C, 
   p.num_cus = num_cus;
   if (M < 1 || N < 1 || K < 1 || !dma_fits(bf16, p)) return hipErrorNotSupported;
   // A product of few 256 x 256 tiles with a long K (the input gradient
-  // dP W_l: 1600 x 4096 x 16384 makes 112 tiles on 256 CUs) splits K so the
-  // tiles fill the chip: ranges of at least 16 chunks, as many as the spare
-  // buffer holds, the partial sums added in order afterwards.
+  // dP W_l: 1600 x 4096 x 16384 makes 112 tiles on 256 CUs; a small layer's
+  // weight gradients, 4H x H x T B, a handful) splits K so the tiles fill the
+  // chip: up to 16 ranges of at least 8 chunks, as many as the spare buffer
+  // holds, the partial sums added in order afterwards.
   const int cus = num_cus > 0 ? num_cus : 256;
   const int tiles16 = ((p.Mt + kDmaTiles - 1) / kDmaTiles) * ((N + 255) / 256);
   const int nch = K / (bf16 ? Dt<true>::KC : Dt<false>::KC);
   const long long cfl = (long long)M * ldc;
   int ks = 1;
-  while (ks < 4 && tiles16 * (ks + 1) <= cus && nch / (ks + 1) >= 16 && C2 && (long long)ks * cfl <= c2_floats &&
+  while (ks < 16 && tiles16 * (ks + 1) <= cus && nch / (ks + 1) >= 8 && C2 && (long long)ks * cfl <= c2_floats &&
          ldc >= N)
     ++ks;
   if (ks > 1) p.C2 = C2, p.split_stride = cfl, p.ksplit = ks;
