@@ -49,6 +49,10 @@ const void* bwd_res_kernel_ptr_shape5(int nw);
 const void* bwd_res_kernel_ptr_shape6(int nw);
 const void* bwd_res_kernel_ptr_shape7(int nw);
 const void* bwd_res_kernel_ptr_shape8(int nw);
+const void* bwd_res_kernel_ptr_shape9(int nw);
+const void* bwd_res_kernel_ptr_shape10(int nw);
+const void* bwd_res_kernel_ptr_shape11(int nw);
+const void* bwd_res_kernel_ptr_shape12(int nw);
 
 namespace {
 
@@ -451,7 +455,8 @@ RecShape rec_shape(int B, int H, bool bf16) {
 struct BwdLayout {
   size_t ctl, flg, dpx, prt, rtf, dpf, wt, dp, dph, dpt, ut, ht, dy0, dy1, dhp, dcrec, colp, spl, total;
   RecShape rs;
-  int res_nci;  // > 0: the chain runs in lstm_bwd_res_kernel with this many chunks per wave
+  int res_nci;  // > 0: the chain runs in lstm_bwd_res_kernel with this many chunks per wave,
+  int res_mw;   // ... this many M-tiles per workgroup (4 over a K quarter, 1 over all of K)
   int res_nw;   // ... and this many batch tiles (1, 2 or 4; 3 runs as 4)
   size_t spl_floats;
 };
@@ -472,34 +477,50 @@ int bwd_res_nw(int B) {
   return nbt <= 2 ? nbt : 4;
 }
 
-// The on-chip chain's shape for a problem: NCI, the chunks of KC columns of
-// each wave's share of a workgroup's K quarter (H / (4 KC)), when kBwdResShape
-// has it; 0 otherwise (the streamed chain runs).  H must be a multiple of 256
-// (whole unit groups of 64 per K quarter) and B at most 64 (32 at NCI = 16).
-int bwd_resident_nci(const lstm_desc_t* d) {
+bool bwd_res_listed(bool bf16, int nci, int mw) {
+  for (const BwdResShape& sh : kBwdResShape)
+    if (sh.bf16 == (bf16 ? 1 : 0) && sh.nci == nci && sh.mw == mw) return true;
+  return false;
+}
+
+// The on-chip chain's shape for a problem, when kBwdResShape has it: one
+// M-tile per workgroup over all of K (NCI = H / KC chunks per wave, every
+// block in LDS) when its R_l^T rows fit in LDS, else four M-tiles over a K
+// quarter (NCI = H / (4 KC)); *mw = 0 otherwise (the streamed chain runs).
+// H must be a multiple of 256 (whole unit groups of 64 per K quarter) and B
+// at most 64 (32 with four M-tiles and NCI = 16).
+int bwd_resident_nci(const lstm_desc_t* d, int* mw) {
   const bool bf16 = d->dtype == LSTM_BF16;
   const int KC = bf16 ? 64 : 32;
+  *mw = 0;
   if (d->cell != LSTM_CELL_LSTM || d->H % 256 != 0 || d->B > 64) return 0;
-  const int nci = d->H / (4 * KC), nw = bwd_res_nw(d->B);
-  bool listed = false;
-  for (const BwdResShape& sh : kBwdResShape) listed = listed || (sh.bf16 == (bf16 ? 1 : 0) && sh.nci == nci);
-  if (!listed || nw > (nci >= 16 ? 2 : 4)) return 0;
+  const int nw = bwd_res_nw(d->B);
+  int nci = d->H / KC;
+  if (bwd_res_listed(bf16, nci, 1)) {
+    *mw = 1;
+  } else {
+    nci = d->H / (4 * KC);
+    if (!bwd_res_listed(bf16, nci, 4) || nw > (nci >= 16 ? 2 : 4)) return 0;
+    *mw = 4;
+  }
   // the kernel's per-step offsets are 32-bit: T + 1 slots of the dp exchange
   // (nw tiles x 4H / KC chunks x 2 KiB) and the T B 4H saved gates
   const long long xslot = (long long)nw * (4LL * d->H / KC) * (2048 / (bf16 ? 2 : 4));
   if ((long long)(d->T + 1) * xslot >= (1LL << 31) || (long long)d->T * d->B * 4 * d->H >= (1LL << 31)) return 0;
   return nci;
 }
-int bwd_res_wgs(int H) { return 4 * (H / 64); }
+int bwd_res_wgs(int H) { return H / 16; }
 
-const void* bwd_res_fn(bool bf16, int nci, int nw) {
+const void* bwd_res_fn(bool bf16, int nci, int mw, int nw) {
   const void* (*const per_shape[kBwdResShapes])(int) = {
-      bwd_res_kernel_ptr_shape0, bwd_res_kernel_ptr_shape1, bwd_res_kernel_ptr_shape2,
-      bwd_res_kernel_ptr_shape3, bwd_res_kernel_ptr_shape4, bwd_res_kernel_ptr_shape5,
-      bwd_res_kernel_ptr_shape6, bwd_res_kernel_ptr_shape7, bwd_res_kernel_ptr_shape8};
-  static_assert(kBwdResShapes == 9, "one compile unit per shape");
+      bwd_res_kernel_ptr_shape0, bwd_res_kernel_ptr_shape1,  bwd_res_kernel_ptr_shape2,  bwd_res_kernel_ptr_shape3,
+      bwd_res_kernel_ptr_shape4, bwd_res_kernel_ptr_shape5,  bwd_res_kernel_ptr_shape6,  bwd_res_kernel_ptr_shape7,
+      bwd_res_kernel_ptr_shape8, bwd_res_kernel_ptr_shape9,  bwd_res_kernel_ptr_shape10, bwd_res_kernel_ptr_shape11,
+      bwd_res_kernel_ptr_shape12};
+  static_assert(kBwdResShapes == 13, "one compile unit per shape");
   for (int k = 0; k < kBwdResShapes; ++k)
-    if (kBwdResShape[k].bf16 == (bf16 ? 1 : 0) && kBwdResShape[k].nci == nci) return per_shape[k](nw);
+    if (kBwdResShape[k].bf16 == (bf16 ? 1 : 0) && kBwdResShape[k].nci == nci && kBwdResShape[k].mw == mw)
+      return per_shape[k](nw);
   return nullptr;
 }
 
@@ -537,7 +558,7 @@ bool bwd_layout(const lstm_desc_t* d, BwdLayout* o) {
   const size_t H = d->H, B = d->B, TB = (size_t)d->T * d->B, G = 4 * H;
   const size_t Imax = std::max<size_t>(d->I, H);
   o->rs = rec_shape(d->B, d->H, d->dtype == LSTM_BF16);
-  o->res_nci = bwd_resident_nci(d);
+  o->res_nci = bwd_resident_nci(d, &o->res_mw);
   o->res_nw = bwd_res_nw(d->B);
   const bool resident = o->res_nci > 0;
   size_t off = 0;
@@ -552,7 +573,7 @@ bool bwd_layout(const lstm_desc_t* d, BwdLayout* o) {
   // (counters for up to res_nw batch groups of rwgs workgroups)
   o->flg = take(resident ? (size_t)2 * o->res_nw * rwgs * kFlagStride * 4 : 0);
   o->dpx = take(resident ? (size_t)d->T * o->res_nw * o->rs.nch * 2048 : 0);
-  o->prt = take(resident ? (size_t)(d->T + 1) * bwd_res_part_floats(rwgs, o->res_nw) * 4 : 0);
+  o->prt = take(resident && o->res_mw > 1 ? (size_t)(d->T + 1) * bwd_res_part_floats(rwgs, o->res_nw) * 4 : 0);
   o->rtf = take((size_t)o->rs.nt16 * o->rs.nch * 2048);
   o->dpf = take((size_t)o->rs.nbt * o->rs.nch * 2048);
   o->wt = take(Imax * G * s);
@@ -685,8 +706,8 @@ lstm_status_t bwd_run(const lstm_desc_t* d, const void* x, const void* h0, const
   int res_groups = 0, res_lds = 0;
   const void* res_fn = nullptr;
   for (int g = res_nw; resident && g >= 1 && !res_groups; g /= 2) {
-    const void* fn = bwd_res_fn(BF16, o.res_nci, res_nw / g);
-    const int lds = bwd_res_lds_bytes(res_nw / g, o.res_nci);
+    const void* fn = bwd_res_fn(BF16, o.res_nci, o.res_mw, res_nw / g);
+    const int lds = bwd_res_lds_bytes(res_nw / g, o.res_nci, o.res_mw);
     int per_cu = 0;
     if (fn && prepare_fn(fn, lds, 64 * kBwdResWaves, &per_cu) == hipSuccess && (long)per_cu * cus >= (long)g * res_wgs) {
       res_groups = g, res_fn = fn, res_lds = lds;

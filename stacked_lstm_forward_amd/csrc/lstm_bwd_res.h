@@ -79,24 +79,29 @@ constexpr int kBwdResMW = 4;  // M-tiles (of 16 output units) per workgroup
 constexpr int kBwdResPf = 7;  // per-step inputs of one (unit, sequence): dY, i, f, g, o, c_t, c_{t-1}
 
 // Fragment blocks (of each wave's MW NCI) kept in registers, for NCI chunks
-// of the K quarter per wave: 48 of 64 at NCI = 16 (bf16 H = 4096), else three
-// of the four M-tiles of every chunk.
-__host__ __device__ constexpr int bwd_res_nrb(int nci) { return nci >= 16 ? 48 : 3 * nci; }
+// per wave: with four M-tiles (K quarters), 48 of 64 at NCI = 16 (bf16
+// H = 4096), else three of the four M-tiles of every chunk; with one M-tile
+// (all of K) none, every block in LDS.
+__host__ __device__ constexpr int bwd_res_nrb(int nci, int mw) { return mw == 1 ? 0 : nci >= 16 ? 48 : 3 * nci; }
 
-// The instantiated shapes, (bf16, NCI): NCI = H / (4 KC), so H = 4096, 256,
-// 512, 1024, 1536 and 2048 in bf16 and 256, 512 and 1024 in fp32.  Each is
-// built with 1, 2 and 4 batch tiles (NCI = 16: 1 and 2), one compile unit per
+// The instantiated shapes, (bf16, NCI, MW).  MW = 4: each workgroup four
+// M-tiles over a K quarter, NCI = H / (4 KC): H = 4096, 256, 512, 1024, 1536
+// and 2048 in bf16, 256, 512 and 1024 in fp32.  MW = 1: each workgroup one
+// M-tile over all of K, its R_l^T rows in LDS (64 H x size of an element
+// bytes), NCI = H / KC: H = 256 and 512 in both dtypes.  Each is built with
+// 1, 2 and 4 batch tiles (MW = 4, NCI = 16: 1 and 2), one compile unit per
 // shape (lstm_bwd_res_inst.hip).
 struct BwdResShape {
-  int bf16, nci;
+  int bf16, nci, mw;
 };
-constexpr int kBwdResShapes = 9;
-constexpr BwdResShape kBwdResShape[kBwdResShapes] = {{1, 16}, {1, 1}, {1, 2}, {1, 4}, {1, 6},
-                                                      {1, 8},  {0, 2}, {0, 4}, {0, 8}};
+constexpr int kBwdResShapes = 13;
+constexpr BwdResShape kBwdResShape[kBwdResShapes] = {
+    {1, 16, 4}, {1, 1, 4}, {1, 2, 4}, {1, 4, 4}, {1, 6, 4}, {1, 8, 4}, {0, 2, 4},
+    {0, 4, 4},  {0, 8, 4}, {1, 4, 1}, {1, 8, 1}, {0, 8, 1}, {0, 16, 1}};
 
-// LDS bytes: the LDS weight blocks, one tile's partial sums, the parked inputs.
-__host__ __device__ constexpr int bwd_res_lds_bytes(int nw, int nci) {
-  return kBwdResWaves * (kBwdResMW * nci - bwd_res_nrb(nci)) * 2048 + kBwdResMW * kBwdResWaves * 64 * 16 +
+// LDS bytes: the LDS weight blocks, one tile's K-group sums, the parked inputs.
+__host__ __device__ constexpr int bwd_res_lds_bytes(int nw, int nci, int mw) {
+  return kBwdResWaves * (mw * nci - bwd_res_nrb(nci, mw)) * 2048 + mw * kBwdResWaves * 64 * 16 +
          nw * kBwdResPf * 256 * 4;
 }
 
@@ -114,14 +119,15 @@ __host__ __device__ constexpr long long bwd_res_part_floats(int wgs, int nw) {
   return (long long)wgs * nw * kBwdResMW * 64 * 4;
 }
 
-template <bool BF16, int NW, int NCI>
+template <bool BF16, int NW, int NCI, int MW>
 __global__ void __launch_bounds__(64 * kBwdResWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
 lstm_bwd_res_kernel(const BwdResParams P) {
   typedef typename Dt<BF16>::T T;
   typedef ResOps<BF16> Ops;
   typedef typename Ops::V V;
   constexpr int SZ = Dt<BF16>::SZ, KC = Dt<BF16>::KC;
-  constexpr int KS = kBwdResWaves, MW = kBwdResMW, NRB = bwd_res_nrb(NCI);
+  static_assert(MW == 1 || MW == kBwdResMW, "four M-tiles over a K quarter, or one over all of K");
+  constexpr int KS = kBwdResWaves, NRB = bwd_res_nrb(NCI, MW);
   constexpr int NB = MW * NCI, NLB = NB - NRB, LPC = NLB / NCI, RPC = MW - LPC;
   static_assert(NLB % NCI == 0 && LPC >= 1, "LDS blocks spread evenly over the chunks");
   constexpr int FB = 2048 / SZ, EPH = 16 / SZ;
@@ -132,9 +138,10 @@ lstm_bwd_res_kernel(const BwdResParams P) {
   const int bid = blockIdx.x;
   const int v = P.xcd_remap ? ((bid & 7) * (P.grid >> 3) + (bid >> 3)) : bid;
   if (v >= P.wgs) return;
-  // batch group jg, and within it unit group ug and K quarter kq
+  // batch group jg, and within it unit group ug (MW M-tiles) and K part kq
+  // (of MW: quarters, or all of K)
   const int wgs0 = P.wgs / P.groups, jg = v / wgs0, v0 = v - jg * wgs0;
-  const int ug = v0 >> 2, kq = v0 & 3;
+  const int ug = v0 / MW, kq = v0 % MW;
   const int gw0 = jg * wgs0;  // the group's first workgroup
   const int tid = threadIdx.x, lane = tid & 63;
   const int kg = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -153,7 +160,7 @@ lstm_bwd_res_kernel(const BwdResParams P) {
   struct WB {
     V h[2];
   };
-  WB wreg[NRB];
+  WB wreg[NRB > 0 ? NRB : 1];
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     const int ci = b / MW, i = b % MW;
@@ -178,7 +185,7 @@ lstm_bwd_res_kernel(const BwdResParams P) {
   // M-tile kq, lane `lane` the four units u0 .. u0 + 3 of sequence fb (the
   // lane's four sums of that tile, so every per-step load and store is 16
   // bytes); the other waves only multiply
-  const int u0 = 64 * ug + 16 * kq + 4 * (lane >> 4);
+  const int u0 = 16 * (MW * ug + kq) + 4 * (lane >> 4);
   const int jt = NW * jg + kg;                       // its column tile
   const int fb = min(16 * jt + (lane & 15), B - 1);  // clamped for the loads of padding lanes
   const bool fwave = kg < NW;                        // wave-uniform
@@ -225,10 +232,11 @@ lstm_bwd_res_kernel(const BwdResParams P) {
         pf[(kg * kBwdResPf + 6) * 64 + lane] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     if (s > 0) {
-      // dp_{t+1} of this quarter's units: finished by the quarter's workgroups
-      // in this batch group (H / 64 of them: 64 kq .. 64 kq + 63 at H = 4096)
+      // dp_{t+1} of this K part's units: finished by the part's workgroups in
+      // this batch group (H / 64 of them per quarter: 64 kq .. 64 kq + 63 at
+      // H = 4096; all H / 16 with one M-tile per workgroup)
       if (kg == 0) {
-        const int nq = wgs0 / 4;
+        const int nq = wgs0 / MW;
         const bool ok = wait_counts_serial(P.flags_d + (long)(gw0 + nq * kq) * kFlagStride, nq, s, nullptr, 0, 0, P.err,
                                            P.timeout_ticks);
         if (lane == 0) s_ok = ok ? 1 : 0;
@@ -241,9 +249,8 @@ lstm_bwd_res_kernel(const BwdResParams P) {
       // ---- this workgroup's partial dh_rec = dp_{t+1} R_l over its K quarter
       const T* src = DPx + (long)(t + 1) * P.xslot + ((long)NW * jg * nch + NCI * KS * kq) * FB;
       const __amdgpu_buffer_rsrc_t drs = raw_buffer(src, (int)((long)NW * nch * FB * SZ));
-      const __amdgpu_buffer_rsrc_t prs = raw_buffer(P.part + (long)s * pslot + (long)v * (NW * MW * 256), NW * MW * 1024);
       Frag rb[PD];
-      Frag al[LPC];
+      Frag al[MW == 1 ? 2 : LPC];  // (one M-tile: this chunk's and the next chunk's LDS block)
       auto issue = [&](Frag& dst, int g) {
         const int o = ((g / NCI) * nch + (g % NCI) * KS) * FB * SZ;
         dst.v[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(drs, hlane, o, 0));
@@ -262,8 +269,16 @@ lstm_bwd_res_kernel(const BwdResParams P) {
 #pragma unroll
         for (int ci = 0; ci < NCI; ++ci) {
           const int g = j * NCI + ci, sl = g % PD;
+          if constexpr (MW == 1) {
+            // every block in LDS: the next chunk's read into the other buffer
+            // while this chunk's MFMAs run
+            if (ci + 1 < NCI || j + 1 < NW) al[(g + 1) & 1] = lds_get(As + ((ci + 1) % NCI) * 128, lane);
+            Ops::chunk(acc[0], Ops::cast(al[g & 1].v[0]), Ops::cast(al[g & 1].v[1]), Ops::cast(rb[sl].v[0]),
+                       Ops::cast(rb[sl].v[1]));
+            __builtin_amdgcn_sched_barrier(0);
+          }
 #pragma unroll
-          for (int ii = 0; ii < MW; ++ii) {
+          for (int ii = 0; ii < (MW == 1 ? 0 : MW); ++ii) {
             // the LDS M-tiles first; the next chunk's LDS blocks are then
             // read into the same registers, three products ahead of use
             const int i = (ii + RPC) % MW;
@@ -289,15 +304,26 @@ lstm_bwd_res_kernel(const BwdResParams P) {
         }
         // the four K-groups' sums of the tile meet in LDS; K-group kg adds
         // those of M-tile kg in a fixed order and leaves them in the slot
+        // (one M-tile: wave j, which finishes tile j, adds them into dh_rec)
 #pragma unroll
         for (int i = 0; i < MW; ++i) red[(i * KS + kg) * 64 + lane] = acc[i];
         __syncthreads();
-        f32x4 p = red[(kg * KS) * 64 + lane];
+        if (MW > 1 || kg == j) {
+          f32x4 p = red[((MW > 1 ? kg : 0) * KS) * 64 + lane];
 #pragma unroll
-        for (int r = 1; r < KS; ++r) p += red[(kg * KS + r) * 64 + lane];
-        store16_coherent(prs, ((j * MW + kg) * 64 + lane) * 16, p);
+          for (int r = 1; r < KS; ++r) p += red[((MW > 1 ? kg : 0) * KS + r) * 64 + lane];
+          if constexpr (MW > 1) {
+            const __amdgpu_buffer_rsrc_t prs =
+                raw_buffer(P.part + (long)s * pslot + (long)v * (NW * MW * 256), NW * MW * 1024);
+            store16_coherent(prs, ((j * MW + kg) * 64 + lane) * 16, p);
+          } else {
+            dhr = p;
+          }
+        }
         if (j + 1 < NW) __syncthreads();  // the next tile reuses the area
       }
+    }
+    if (s > 0 && MW > 1) {
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
