@@ -34,15 +34,21 @@
 // chain with its own counters); a small layer then spreads its products over
 // more CUs.
 //
-// Step protocol, two counters per workgroup (agent-scope stores, bounded
-// waits with the error word):
+// One M-tile per workgroup over all of K (MW = 1, small layers whose R_l^T
+// rows fit in LDS) is the same with one unit group per workgroup and no K
+// split: no partial sums, the four waves' sums go straight into the
+// elementwise part.
+//
+// Step protocol, per workgroup one counter (two with K quarters; agent-scope
+// stores, bounded waits with the error word):
 //   flags_d[v] = s + 1 once iteration s's dp (of step T - 1 - s) is written;
-//   flags_p[v] = s + 1 once iteration s's partial sums are written.
-// Iteration s > 0 waits for flags_d >= s of the H / 64 workgroups of its
-// batch group that finish its K quarter's units (64 kq .. 64 kq + 63 at
-// H = 4096), multiplies, publishes its partials and waits for flags_p >= s + 1
-// of its unit group's four workgroups.  The iteration after the last step
-// computes dh0 = dp_0 R_l.
+//   flags_p[v] = s + 1 once iteration s's partial sums are written (MW = 4).
+// Iteration s > 0 waits for flags_d >= s of the workgroups of its batch group
+// that finish its K part's units (H / 64 of them per quarter: 64 kq .. 64 kq
+// + 63 at H = 4096; all H / 16 with MW = 1), multiplies, and with K quarters
+// publishes its partials and waits for flags_p >= s + 1 of its unit group's
+// four workgroups.  The iteration after the last step computes
+// dh0 = dp_0 R_l.
 #pragma once
 
 #include "lstm_rec_res.h"
