@@ -29,6 +29,11 @@ def load_library() -> ctypes.CDLL:
         return _lib
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is not built; run `python -m stacked_lstm_forward_amd.build`")
+    # torch first: it brings its own HIP runtime (soname libamdhip64.so.7),
+    # which the library's dependency then resolves to.  Loaded the other way
+    # round, the process would hold two HIP runtimes and torch's streams and
+    # memory would be foreign to the library's.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     lib.lstm_peak_mfma.argtypes = [i32, i32, i32, vp, i32, vp, vp, vp]

@@ -83,6 +83,21 @@ def test_training_sizes_and_host_checks():
         sl.LSTM_ERR_INVALID_ARG
 
 
+def test_one_hip_runtime_after_loading():
+    """Loading the library before anything imported torch must still leave one
+    HIP runtime in the process (torch's): two would make torch's streams and
+    memory foreign to the library.  Checked in a fresh interpreter; loading
+    touches no GPU."""
+    import subprocess
+    import sys
+    code = ("import stacked_lstm_forward_amd as sl; sl.load_library(); import torch; "
+            "maps = open('/proc/self/maps').read().splitlines(); "
+            "print(len({l.split()[-1] for l in maps if 'libamdhip64' in l}))")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip().splitlines()[-1] == "1", out.stdout
+
+
 def test_backward_chain_selection():
     """Which shapes run the backward's recurrent chain on chip (host rule, no GPU)."""
     on = lambda L, I, H, B, T, dt, cell="lstm": sl.lstm_bwd_chain_on_chip(  # noqa: E731

@@ -93,9 +93,10 @@ def test_gpu_backward_small(dev, shape, dtype):
     run_and_check(inp, dy, dhT, dcT, dev, f"bwd {shape} {dtype}")
 
 
-@pytest.mark.parametrize("name,T", [("c1", None), ("c2", 12), ("c3", 12), ("c5", 64)])
+@pytest.mark.parametrize("name,T", [("c1", None), ("c2", None), ("c3", None), ("c5", None)])
 def test_gpu_backward_workload_shapes(dev, name, T):
-    """The workloads' shapes (T cut where noted), zero initial states, dy only."""
+    """The workloads in full (every step; the fp64 oracle takes about 25 s for
+    c5's 2048 steps), zero initial states, dy only."""
     import stacked_lstm_forward_amd as sl
     cfg = li.CONFIGS[name]
     if T is not None:
