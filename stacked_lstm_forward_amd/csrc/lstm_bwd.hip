@@ -53,6 +53,8 @@ const void* bwd_res_kernel_ptr_shape9(int nw);
 const void* bwd_res_kernel_ptr_shape10(int nw);
 const void* bwd_res_kernel_ptr_shape11(int nw);
 const void* bwd_res_kernel_ptr_shape12(int nw);
+const void* bwd_res_kernel_ptr_shape13(int nw);
+const void* bwd_res_kernel_ptr_shape14(int nw);
 
 namespace {
 
@@ -485,20 +487,21 @@ bool bwd_res_listed(bool bf16, int nci, int mw) {
 
 // The on-chip chain's shape for a problem, when kBwdResShape has it: one
 // M-tile per workgroup over all of K (NCI = H / KC chunks per wave, every
-// block in LDS) when its R_l^T rows fit in LDS, else four M-tiles over a K
-// quarter (NCI = H / (4 KC)); *mw = 0 otherwise (the streamed chain runs).
-// H must be a multiple of 256 (whole unit groups of 64 per K quarter) and B
+// block in LDS; H a multiple of KC) when its R_l^T rows fit in LDS, else four
+// M-tiles over a K quarter (NCI = H / (4 KC); H a multiple of 256, whole unit
+// groups of 64 per quarter); *mw = 0 otherwise (the streamed chain runs).  B
 // at most 64 (32 with four M-tiles and NCI = 16).
 int bwd_resident_nci(const lstm_desc_t* d, int* mw) {
   const bool bf16 = d->dtype == LSTM_BF16;
   const int KC = bf16 ? 64 : 32;
   *mw = 0;
-  if (d->cell != LSTM_CELL_LSTM || d->H % 256 != 0 || d->B > 64) return 0;
+  if (d->cell != LSTM_CELL_LSTM || d->H % KC != 0 || d->B > 64) return 0;
   const int nw = bwd_res_nw(d->B);
   int nci = d->H / KC;
   if (bwd_res_listed(bf16, nci, 1)) {
     *mw = 1;
   } else {
+    if (d->H % 256 != 0) return 0;
     nci = d->H / (4 * KC);
     if (!bwd_res_listed(bf16, nci, 4) || nw > (nci >= 16 ? 2 : 4)) return 0;
     *mw = 4;
@@ -516,8 +519,8 @@ const void* bwd_res_fn(bool bf16, int nci, int mw, int nw) {
       bwd_res_kernel_ptr_shape0, bwd_res_kernel_ptr_shape1,  bwd_res_kernel_ptr_shape2,  bwd_res_kernel_ptr_shape3,
       bwd_res_kernel_ptr_shape4, bwd_res_kernel_ptr_shape5,  bwd_res_kernel_ptr_shape6,  bwd_res_kernel_ptr_shape7,
       bwd_res_kernel_ptr_shape8, bwd_res_kernel_ptr_shape9,  bwd_res_kernel_ptr_shape10, bwd_res_kernel_ptr_shape11,
-      bwd_res_kernel_ptr_shape12};
-  static_assert(kBwdResShapes == 13, "one compile unit per shape");
+      bwd_res_kernel_ptr_shape12, bwd_res_kernel_ptr_shape13, bwd_res_kernel_ptr_shape14};
+  static_assert(kBwdResShapes == 15, "one compile unit per shape");
   for (int k = 0; k < kBwdResShapes; ++k)
     if (kBwdResShape[k].bf16 == (bf16 ? 1 : 0) && kBwdResShape[k].nci == nci && kBwdResShape[k].mw == mw)
       return per_shape[k](nw);

@@ -94,16 +94,16 @@ __host__ __device__ constexpr int bwd_res_nrb(int nci, int mw) { return mw == 1 
 // M-tiles over a K quarter, NCI = H / (4 KC): H = 4096, 256, 512, 1024, 1536
 // and 2048 in bf16, 256, 512 and 1024 in fp32.  MW = 1: each workgroup one
 // M-tile over all of K, its R_l^T rows in LDS (64 H x size of an element
-// bytes), NCI = H / KC: H = 256 and 512 in both dtypes.  Each is built with
-// 1, 2 and 4 batch tiles (MW = 4, NCI = 16: 1 and 2), one compile unit per
-// shape (lstm_bwd_res_inst.hip).
+// bytes), NCI = H / KC: H = 128, 256 and 512 in both dtypes.  Each is built
+// with 1, 2 and 4 batch tiles (MW = 4, NCI = 16: 1 and 2), one compile unit
+// per shape (lstm_bwd_res_inst.hip).
 struct BwdResShape {
   int bf16, nci, mw;
 };
-constexpr int kBwdResShapes = 13;
+constexpr int kBwdResShapes = 15;
 constexpr BwdResShape kBwdResShape[kBwdResShapes] = {
-    {1, 16, 4}, {1, 1, 4}, {1, 2, 4}, {1, 4, 4}, {1, 6, 4}, {1, 8, 4}, {0, 2, 4},
-    {0, 4, 4},  {0, 8, 4}, {1, 4, 1}, {1, 8, 1}, {0, 8, 1}, {0, 16, 1}};
+    {1, 16, 4}, {1, 1, 4}, {1, 2, 4},  {1, 4, 4}, {1, 6, 4}, {1, 8, 4}, {0, 2, 4}, {0, 4, 4},
+    {0, 8, 4},  {1, 4, 1}, {1, 8, 1},  {0, 8, 1}, {0, 16, 1}, {1, 2, 1}, {0, 4, 1}};
 
 // LDS bytes: the LDS weight blocks, one tile's K-group sums, the parked inputs.
 __host__ __device__ constexpr int bwd_res_lds_bytes(int nw, int nci, int mw) {

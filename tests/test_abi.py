@@ -103,19 +103,20 @@ def test_backward_chain_selection():
     on = lambda L, I, H, B, T, dt, cell="lstm": sl.lstm_bwd_chain_on_chip(  # noqa: E731
         sl.make_desc(L, I, H, B, T, dt, cell))
     # the instantiated (dtype, H): H / 16 workgroups, each a quarter of K
-    for H in (256, 512, 1024, 1536, 2048, 4096):
+    for H in (128, 256, 512, 1024, 1536, 2048, 4096):
         assert on(1, 64, H, 16, 4, "bf16"), H
-    for H in (256, 512, 1024):
+    for H in (128, 256, 512, 1024):
         assert on(1, 64, H, 16, 4, "f32"), H
-    for H, dt in ((128, "bf16"), (768, "bf16"), (3072, "bf16"), (2048, "f32"), (4096, "f32"), (300, "bf16")):
+    for H, dt in ((64, "bf16"), (192, "bf16"), (768, "bf16"), (3072, "bf16"), (96, "f32"), (2048, "f32"),
+                  (4096, "f32"), (300, "bf16")):
         assert not on(1, 64, H, 16, 4, dt), (H, dt)
     # batch tiles: up to 4 (64 sequences; a third runs as a padded fourth), 2 at H = 4096
     assert on(1, 64, 256, 64, 4, "bf16") and on(1, 64, 256, 40, 4, "bf16") and not on(1, 64, 256, 65, 4, "bf16")
     assert on(1, 64, 4096, 32, 4, "bf16") and not on(1, 64, 4096, 33, 4, "bf16")
-    # the workloads: c2, c3, c4 and c5 on chip, c1 (H = 128) streamed
+    # every workload
     assert on(4, 512, 512, 64, 100, "f32") and on(8, 256, 256, 64, 200, "bf16")
     assert on(4, 4096, 4096, 32, 50, "bf16") and on(1, 1536, 1536, 4, 2048, "bf16")
-    assert not on(1, 128, 128, 8, 16, "f32")
+    assert on(1, 128, 128, 8, 16, "f32")
     # 32-bit offsets inside the kernel: T B 4H and the T + 1 exchange slots stay below 2^31
     assert on(1, 64, 4096, 32, 4094, "bf16") and not on(1, 64, 4096, 32, 4095, "bf16")
     # LSTM only; invalid descriptors are refused

@@ -101,8 +101,8 @@ def test_gpu_backward_workload_shapes(dev, name, T):
     cfg = li.CONFIGS[name]
     if T is not None:
         cfg = li.Config(f"{cfg.name}-T{T}", cfg.cfg_id, cfg.L, cfg.I, cfg.H, cfg.B, T, cfg.dtype)
-    # c2, c3 and c5 run the chain on chip, c1 (H = 128) streams it
-    assert sl.lstm_bwd_chain_on_chip(sl.make_desc(cfg.L, cfg.I, cfg.H, cfg.B, cfg.T, cfg.dtype)) == (name != "c1")
+    # every workload runs the chain on chip
+    assert sl.lstm_bwd_chain_on_chip(sl.make_desc(cfg.L, cfg.I, cfg.H, cfg.B, cfg.T, cfg.dtype))
     inp = li.make_inputs(cfg)
     dy, _, _ = upstream(cfg, 810, with_states=False)
     say(f"backward workload {cfg.name}")
@@ -134,11 +134,13 @@ def test_gpu_backward_on_chip_chain(dev, B, states):
 # fourth), with and without upstream state gradients
 ON_CHIP = [
     # L, I, H, B, T, dtype, states
+    (2, 48, 128, 24, 5, "bf16", True),
     (2, 64, 256, 40, 5, "bf16", True),
     (1, 96, 512, 20, 6, "bf16", False),
     (1, 128, 1024, 5, 4, "bf16", True),
     (1, 64, 1536, 4, 5, "bf16", False),
     (1, 64, 2048, 64, 3, "bf16", True),
+    (1, 64, 128, 8, 6, "f32", False),
     (2, 48, 256, 33, 5, "f32", True),
     (1, 64, 512, 16, 4, "f32", False),
     (1, 32, 1024, 48, 3, "f32", True),
