@@ -40,8 +40,8 @@
  * Errors: status codes as in lstm_fwd.h, checked on the host before anything
  * is enqueued; a cell other than the LSTM returns LSTM_ERR_UNSUPPORTED.
  *
- * Recurrent chain: for H = 128, 256, 512, 1024, 1536, 2048 or 4096 in bf16
- * and H = 128, 256, 512 or 1024 in fp32, with B <= 64 (32 at H = 4096), it
+ * Recurrent chain: for H = 128, 256, 512, 1024, 1536, 2048, 3072 or 4096 in
+ * bf16 and H = 128, 256, 512 or 1024 in fp32, with B <= 64 (32 at H = 4096), it
  * runs as one persistent launch per layer that keeps R_l^T on chip (when its
  * workgroups fit on the device at once): H / 16 workgroups per batch group,
  * each finishing 16 units, over all of K (H <= 512) or a quarter of it with

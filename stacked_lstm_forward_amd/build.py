@@ -25,7 +25,7 @@ UNITS = [("lstm_kernels.hip", [])] + [
     for bf in (0, 1) for st in (0, 1) for nwv in (4, 8)
 ] + [("lstm_rec_res_inst.hip", [f"-DLSTM_RES_SHAPE={k}"]) for k in range(3)] + [("lstm_fwd.cpp", []), ("lstm_plan.cpp", []), ("lstm_fwd_noalloc.hip", []),
                  ("lstm_bwd.hip", [])] + [
-    ("lstm_bwd_res_inst.hip", [f"-DLSTM_BWD_RES_SHAPE={k}"]) for k in range(15)]
+    ("lstm_bwd_res_inst.hip", [f"-DLSTM_BWD_RES_SHAPE={k}"]) for k in range(16)]
 PEAK_UNITS = [("lstm_peaks.hip", [])]
 BUILD_DIR = os.path.join(HERE, "_build")
 

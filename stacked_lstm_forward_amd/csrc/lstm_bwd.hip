@@ -55,6 +55,7 @@ const void* bwd_res_kernel_ptr_shape11(int nw);
 const void* bwd_res_kernel_ptr_shape12(int nw);
 const void* bwd_res_kernel_ptr_shape13(int nw);
 const void* bwd_res_kernel_ptr_shape14(int nw);
+const void* bwd_res_kernel_ptr_shape15(int nw);
 
 namespace {
 
@@ -519,8 +520,8 @@ const void* bwd_res_fn(bool bf16, int nci, int mw, int nw) {
       bwd_res_kernel_ptr_shape0, bwd_res_kernel_ptr_shape1,  bwd_res_kernel_ptr_shape2,  bwd_res_kernel_ptr_shape3,
       bwd_res_kernel_ptr_shape4, bwd_res_kernel_ptr_shape5,  bwd_res_kernel_ptr_shape6,  bwd_res_kernel_ptr_shape7,
       bwd_res_kernel_ptr_shape8, bwd_res_kernel_ptr_shape9,  bwd_res_kernel_ptr_shape10, bwd_res_kernel_ptr_shape11,
-      bwd_res_kernel_ptr_shape12, bwd_res_kernel_ptr_shape13, bwd_res_kernel_ptr_shape14};
-  static_assert(kBwdResShapes == 15, "one compile unit per shape");
+      bwd_res_kernel_ptr_shape12, bwd_res_kernel_ptr_shape13, bwd_res_kernel_ptr_shape14, bwd_res_kernel_ptr_shape15};
+  static_assert(kBwdResShapes == 16, "one compile unit per shape");
   for (int k = 0; k < kBwdResShapes; ++k)
     if (kBwdResShape[k].bf16 == (bf16 ? 1 : 0) && kBwdResShape[k].nci == nci && kBwdResShape[k].mw == mw)
       return per_shape[k](nw);

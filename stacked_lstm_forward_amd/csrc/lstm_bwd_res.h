@@ -91,8 +91,9 @@ constexpr int kBwdResPf = 7;  // per-step inputs of one (unit, sequence): dY, i,
 __host__ __device__ constexpr int bwd_res_nrb(int nci, int mw) { return mw == 1 ? 0 : nci >= 16 ? 48 : 3 * nci; }
 
 // The instantiated shapes, (bf16, NCI, MW).  MW = 4: each workgroup four
-// M-tiles over a K quarter, NCI = H / (4 KC): H = 4096, 256, 512, 1024, 1536
-// and 2048 in bf16, 256, 512 and 1024 in fp32.  MW = 1: each workgroup one
+// M-tiles over a K quarter, NCI = H / (4 KC): H = 4096, 256, 512, 1024, 1536,
+// 2048 and 3072 in bf16, 256, 512 and 1024 in fp32 (fp32 at H = 2048 would
+// hold 48 blocks in registers and spills).  MW = 1: each workgroup one
 // M-tile over all of K, its R_l^T rows in LDS (64 H x size of an element
 // bytes), NCI = H / KC: H = 128, 256 and 512 in both dtypes.  Each is built
 // with 1, 2 and 4 batch tiles (MW = 4, NCI = 16: 1 and 2), one compile unit
@@ -100,10 +101,10 @@ __host__ __device__ constexpr int bwd_res_nrb(int nci, int mw) { return mw == 1 
 struct BwdResShape {
   int bf16, nci, mw;
 };
-constexpr int kBwdResShapes = 15;
+constexpr int kBwdResShapes = 16;
 constexpr BwdResShape kBwdResShape[kBwdResShapes] = {
-    {1, 16, 4}, {1, 1, 4}, {1, 2, 4},  {1, 4, 4}, {1, 6, 4}, {1, 8, 4}, {0, 2, 4}, {0, 4, 4},
-    {0, 8, 4},  {1, 4, 1}, {1, 8, 1},  {0, 8, 1}, {0, 16, 1}, {1, 2, 1}, {0, 4, 1}};
+    {1, 16, 4}, {1, 1, 4}, {1, 2, 4},  {1, 4, 4}, {1, 6, 4},  {1, 8, 4}, {0, 2, 4},  {0, 4, 4},
+    {0, 8, 4},  {1, 4, 1}, {1, 8, 1},  {0, 8, 1}, {0, 16, 1}, {1, 2, 1}, {0, 4, 1}, {1, 12, 4}};
 
 // LDS bytes: the LDS weight blocks, one tile's K-group sums, the parked inputs.
 __host__ __device__ constexpr int bwd_res_lds_bytes(int nw, int nci, int mw) {

@@ -103,11 +103,11 @@ def test_backward_chain_selection():
     on = lambda L, I, H, B, T, dt, cell="lstm": sl.lstm_bwd_chain_on_chip(  # noqa: E731
         sl.make_desc(L, I, H, B, T, dt, cell))
     # the instantiated (dtype, H): H / 16 workgroups, each a quarter of K
-    for H in (128, 256, 512, 1024, 1536, 2048, 4096):
+    for H in (128, 256, 512, 1024, 1536, 2048, 3072, 4096):
         assert on(1, 64, H, 16, 4, "bf16"), H
     for H in (128, 256, 512, 1024):
         assert on(1, 64, H, 16, 4, "f32"), H
-    for H, dt in ((64, "bf16"), (192, "bf16"), (768, "bf16"), (3072, "bf16"), (96, "f32"), (2048, "f32"),
+    for H, dt in ((64, "bf16"), (192, "bf16"), (768, "bf16"), (2560, "bf16"), (96, "f32"), (2048, "f32"),
                   (4096, "f32"), (300, "bf16")):
         assert not on(1, 64, H, 16, 4, dt), (H, dt)
     # batch tiles: up to 4 (64 sequences; a third runs as a padded fourth), 2 at H = 4096

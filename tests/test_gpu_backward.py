@@ -140,6 +140,7 @@ ON_CHIP = [
     (1, 128, 1024, 5, 4, "bf16", True),
     (1, 64, 1536, 4, 5, "bf16", False),
     (1, 64, 2048, 64, 3, "bf16", True),
+    (1, 64, 3072, 32, 3, "bf16", False),
     (1, 64, 128, 8, 6, "f32", False),
     (2, 48, 256, 33, 5, "f32", True),
     (1, 64, 512, 16, 4, "f32", False),
