@@ -2,17 +2,20 @@
 // gfx950: kernels and the lstm_bwd entry point (include/lstm_bwd.h).
 //
 // Per layer, from the top:
-//   1. the recurrent chain, strictly serial in t: for t = T-1 .. 0 an
-//      elementwise kernel turns dh = dY[t] + dh_rec and dc_rec into the gate
-//      derivatives dp_t (fp32, and copies in the workload's dtype) and the next
-//      dc_rec; then dh_rec = dp_t R_l, an MFMA product over K = 4H split across
-//      workgroups so it fills the GPU (the K-split partial sums are added by the
-//      next step's elementwise kernel, in a fixed order).  That product reads
-//      all of R_l every step, so it is bound by memory: R_l^T is rewritten once
-//      per layer, and dp_t every step, in the order the MFMA fragments are
-//      loaded (every wave-wide load reads 1 KiB in one piece), each workgroup
-//      keeps its slice of dp_t in LDS and streams its slice of R_l^T with eight
-//      chunks of loads in flight per wave;
+//   1. the recurrent chain, strictly serial in t = T-1 .. 0: dh = dY[t] +
+//      dh_rec and dc_rec give the gate derivatives dp_t (fp32, and copies in
+//      the workload's dtype) and the next dc_rec; dh_rec = dp_t R_l, an MFMA
+//      product over K = 4H.  For the shapes lstm_bwd_res.h is built for, one
+//      persistent launch per layer runs the whole chain with R_l^T on chip
+//      (R_l^T rewritten once per layer in MFMA load order, K unit-major).
+//      Otherwise (the streamed chain) each step is an elementwise kernel and
+//      the product split over K across workgroups so it fills the GPU (the
+//      K-split partial sums are added by the next step's elementwise kernel,
+//      in a fixed order); that product reads all of R_l every step, so it is
+//      bound by memory: R_l^T and dp_t are laid out in the order the MFMA
+//      fragments are loaded (every wave-wide load reads 1 KiB in one piece),
+//      each workgroup keeps its slice of dp_t in LDS and streams its slice of
+//      R_l^T with eight chunks of loads in flight per wave;
 //   2. once every step's dp is known, the weight and input gradients as single
 //      MFMA products over all T*B columns -- dW_l = dP^T U, dR_l = dP^T H_prev,
 //      dU = dP W_l ("Optimizing Performance of Recurrent Neural Networks on
