@@ -226,3 +226,30 @@ def test_gpu_backward_plain_launch_options(dev):
     assert sl.lstm_bwd_last_error(b.bws) == sl.LSTM_OK
     for x, y in ((a.dx, b.dx), (a.dh0, b.dh0), (a.dc0, b.dc0), (a.dW, b.dW), (a.dR, b.dR), (a.db, b.db)):
         assert torch.equal(x.view(torch.int32), y.view(torch.int32))
+
+
+# bitwise determinism of the on-chip chain's shapes (fixed summation orders:
+# the K-group sums in LDS, the partial sums across workgroups, the K ranges of
+# the gradient products): two backward passes on one workspace
+@pytest.mark.parametrize("shape", [(2, 64, 256, 40, 5, "bf16"), (1, 64, 1536, 4, 6, "bf16"), (1, 32, 1024, 48, 3, "f32")],
+                         ids=["bf16-H256-groups", "bf16-H1536-quarters", "f32-H1024-quarters-groups"])
+def test_gpu_backward_bitwise_repeatable(dev, shape):
+    import torch
+    import stacked_lstm_forward_amd as sl
+    from stacked_lstm_forward_amd import runner
+    L, I, H, B, T, dtype = shape
+    assert sl.lstm_bwd_chain_on_chip(sl.make_desc(L, I, H, B, T, dtype))
+    cfg = li.custom_config(L, I, H, B, T, dtype, cfg_id=950 + H + B)
+    inp = li.make_inputs(cfg, random_state=True)
+    dy, dhT, dcT = upstream(cfg, 960 + H)
+    say(f"backward repeatability {shape}")
+    tp = runner.prepare_train(inp, dy, dhT, dcT, dev)
+    tp.forward()
+    tp.backward()
+    first = [t.clone() for t in (tp.dx, tp.dh0, tp.dc0, tp.dW, tp.dR, tp.db)]
+    for t in (tp.dx, tp.dh0, tp.dc0, tp.dW, tp.dR, tp.db):
+        t.fill_(0)
+    tp.backward()
+    assert sl.lstm_bwd_last_error(tp.bws) == sl.LSTM_OK
+    for a, b in zip(first, (tp.dx, tp.dh0, tp.dc0, tp.dW, tp.dR, tp.db)):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32)), shape
