@@ -425,7 +425,9 @@ __device__ __forceinline__ void dma_tile(const GemmParams& P, int mtb, long n0, 
       f32x4 g;
 #pragma unroll
       for (int k = 0; k < 4; ++k) g[k] = wrow[k] ? acc[i][j][k] + bv[k] : bv[k];
-      *reinterpret_cast<f32x4*>(dst) = g;
+      // streamed past the caches: the recurrence reads each step's rows once,
+      // long after, and the caches keep serving this product's operands
+      __builtin_nontemporal_store(g, reinterpret_cast<f32x4*>(dst));
     }
   }
 }
