@@ -401,7 +401,8 @@ __global__ void __launch_bounds__(64 * NWV) lstm_rec_kernel(const RecParams P) {
 #pragma unroll
       for (int i = 0; i < MW; ++i)
 #pragma unroll
-        for (int j = 0; j < NW; ++j) gq[i][j] = *reinterpret_cast<const f32x4*>(gt + goff[i][j]);
+        for (int j = 0; j < NW; ++j)  // (non-temporal: read once)
+          gq[i][j] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(gt + goff[i][j]));
     }
 
     // ---- wait for h^l_{t-1} (own layer) and h^{l-1}_t (producer in this launch)

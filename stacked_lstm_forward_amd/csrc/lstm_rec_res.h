@@ -217,11 +217,12 @@ lstm_rec_res_kernel(const RecParams P) {
     stamp_clk(t, 6);
     // hoisted pre-activations of this lane's unit in column tile j: with up
     // to two tiles all are loaded before the wait, with more each one at the
-    // start of its pass (registers)
+    // start of its pass (registers).  Non-temporal: read once, they would
+    // otherwise crowd h out of the caches.
     const float* gt = Gp + (long)t * P.Mt * B * 16;
     auto gload = [&](int j) {
       const long off = ((long)min(mt0 + kg, P.Mt - 1) * B + min(16 * j + (lane & 15), B - 1)) * 16 + 4 * q;
-      return *reinterpret_cast<const f32x4*>(gt + off);
+      return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(gt + off));
     };
     constexpr bool kEarlyG = NW <= 2;
     f32x4 gq[kEarlyG ? NW : 1];
