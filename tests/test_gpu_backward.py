@@ -79,6 +79,7 @@ SHAPES = [
     (3, 33, 17, 17, 4),
     (2, 64, 64, 16, 6),
     (2, 130, 66, 20, 7),
+    (1, 64, 256, 80, 4),  # more than 64 sequences: the streamed chain at a size the on-chip one takes up to B = 64
 ]
 
 
@@ -253,3 +254,35 @@ def test_gpu_backward_bitwise_repeatable(dev, shape):
     assert sl.lstm_bwd_last_error(tp.bws) == sl.LSTM_OK
     for a, b in zip(first, (tp.dx, tp.dh0, tp.dc0, tp.dW, tp.dR, tp.db)):
         assert torch.equal(a.view(torch.int32), b.view(torch.int32)), shape
+
+
+def test_gpu_backward_unaligned_upstream_gradient(dev):
+    """dy not 16-byte aligned (a view 4 bytes into a buffer): the on-chip
+    chain, which moves the per-step tensors 16 bytes at a time, is passed over
+    for the streamed chain, and the gradients still match the oracle."""
+    import torch
+    import stacked_lstm_forward_amd as sl
+    from stacked_lstm_forward_amd import runner
+    cfg = li.custom_config(1, 64, 256, 16, 4, "bf16", cfg_id=990)
+    assert sl.lstm_bwd_chain_on_chip(sl.make_desc(cfg.L, cfg.I, cfg.H, cfg.B, cfg.T, cfg.dtype))
+    inp = li.make_inputs(cfg, random_state=True)
+    dy, dhT, dcT = upstream(cfg, 991)
+    say("backward with a misaligned dy")
+    tp = runner.prepare_train(inp, dy, dhT, dcT, dev)
+    buf = torch.empty(tp.dy.numel() + 1, dtype=torch.float32, device=dev)
+    view = buf[1:].view_as(tp.dy)
+    view.copy_(tp.dy)
+    assert view.data_ptr() % 16 != 0
+    tp.dy = view
+    tp.forward()
+    tp.backward()
+    assert sl.lstm_bwd_last_error(tp.bws) == sl.LSTM_OK
+    got = tp.grads_f64()
+    f32 = lambda a: None if a is None else np.asarray(a, dtype=np.float32).astype(np.float64)  # noqa: E731
+    ref = orcb.lstm_backward_inputs(inp, f32(dy), f32(dhT), f32(dcT))
+    errs = {k: rel_err(got[k], ref[k]) for k in ("dx", "dh0", "dc0")}
+    for k in ("dW", "dR", "db"):
+        errs[k] = max(rel_err(g, r) for g, r in zip(got[k], ref[k]))
+    say("misaligned dy: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    for k, v in errs.items():
+        assert np.isfinite(v) and v <= TOL["bf16"], (k, v)
