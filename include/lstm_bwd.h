@@ -43,12 +43,15 @@
  * Recurrent chain: for H = 128, 256, 512, 1024, 1536, 2048, 3072 or 4096 in
  * bf16 and H = 128, 256, 512 or 1024 in fp32, with B <= 64 (32 at H = 4096), it
  * runs as one persistent launch per layer that keeps R_l^T on chip (when its
- * workgroups fit on the device at once): H / 16 workgroups per batch group,
- * each finishing 16 units, over all of K (H <= 512) or a quarter of it with
- * partial sums added across four workgroups; dp_t and the partial sums go
- * through `ws` with per-workgroup step counters, and a step wait longer than
- * 2 s sets the error word that lstm_bwd_last_error reports.  Other shapes run it as two
- * launches per step that stream R_l^T from memory.
+ * workgroups fit on the device at once and dy, reserve and the state
+ * tensors are 16-byte aligned): H / 16 workgroups per batch group (up to four
+ * groups, each an independent copy over part of the batch), each finishing
+ * 16 units, over all of K (H <= 512) or a quarter of it with partial sums
+ * added across four workgroups; dp_t and the partial sums go through `ws`
+ * with per-workgroup step counters, and a step wait longer than 2 s sets the
+ * error word that lstm_bwd_last_error reports.  Other shapes run it as two
+ * launches per step that stream R_l^T from memory.  Either way the results
+ * are deterministic: every sum is taken in a fixed order.
  */
 #ifndef LSTM_BWD_H
 #define LSTM_BWD_H
