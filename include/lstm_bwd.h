@@ -81,10 +81,14 @@ lstm_status_t lstm_fwd_train_ex(const lstm_desc_t *d,
 
 /* Options for lstm_bwd_ex.  Zero-initialise and set what you need. */
 typedef struct {
-  int32_t plain_launch;  /* 1: start the on-chip recurrent chain with an ordinary launch instead of a
-                            cooperative one (for profilers that do not handle cooperative launches);
-                            co-residency is still checked against the occupancy limit          */
-  int32_t reserved[7];   /* zero */
+  int32_t plain_launch;     /* 1: start the on-chip recurrent chain with an ordinary launch instead of a
+                               cooperative one (for profilers that do not handle cooperative launches);
+                               co-residency is still checked against the occupancy limit          */
+  int32_t reserved0;        /* zero */
+  int64_t wait_timeout_us;  /* the on-chip chain's step-wait limit in microseconds; 0 selects the
+                               default (2 s); negative makes every wait that is not already
+                               satisfied fail at once (exercises the timeout path without waiting) */
+  int32_t reserved[4];      /* zero */
 } lstm_bwd_opts_t;
 
 /* Bytes of the workspace lstm_bwd needs for `d` (0: invalid or unsupported). */

@@ -53,7 +53,8 @@ class LstmDesc(ctypes.Structure):
 
 
 class BwdOpts(ctypes.Structure):
-    _fields_ = [("plain_launch", ctypes.c_int32), ("reserved", ctypes.c_int32 * 7)]
+    _fields_ = [("plain_launch", ctypes.c_int32), ("reserved0", ctypes.c_int32), ("wait_timeout_us", ctypes.c_int64),
+                ("reserved", ctypes.c_int32 * 4)]
 
 
 class LstmOpts(ctypes.Structure):

@@ -668,7 +668,7 @@ template <bool BF16>
 lstm_status_t bwd_run(const lstm_desc_t* d, const void* x, const void* h0, const float* c0, const void* W,
                       const void* R, const void* reserve, const float* dy, const float* dhT, const float* dcT,
                       float* dx, float* dh0, float* dc0, float* dW, float* dR, float* db, void* ws, const BwdLayout& o,
-                      bool plain, hipStream_t st) {
+                      bool plain, long long timeout_us, hipStream_t st) {
   const int L = d->L, I = d->I, H = d->H, B = d->B, T = d->T;
   const long TB = (long)T * B, G = 4L * H;
   const size_t s = BF16 ? 2 : 4;
@@ -774,7 +774,7 @@ lstm_status_t bwd_run(const lstm_desc_t* d, const void* x, const void* h0, const
       P.flags_d = reinterpret_cast<int*>(w + o.flg);
       P.flags_p = P.flags_d + (long)res_all * kFlagStride;
       P.err = reinterpret_cast<int*>(w + o.ctl);
-      P.timeout_ticks = kBwdTimeoutUs * clk_khz / 1000;
+      P.timeout_ticks = timeout_us * clk_khz / 1000;
       P.T = T, P.B = B, P.H = H, P.nch = rs.nch, P.wgs = res_all, P.groups = res_groups;
       P.grid = (res_all + 7) & ~7;
       P.xcd_remap = 1;
@@ -891,9 +891,14 @@ lstm_status_t lstm_bwd_ex(const lstm_desc_t* d, const void* x, const void* h0, c
   // keep every dimension below 2^31 elements
   if ((long long)d->T * d->B * 4 * d->H >= (1LL << 31)) return LSTM_ERR_UNSUPPORTED;
   const bool plain = opts && opts->plain_launch;
-  return d->dtype == LSTM_BF16
-             ? bwd_run<true>(d, x, h0, c0, W, R, reserve, dy, dhT, dcT, dx, dh0, dc0, dW, dR, db, ws, o, plain, stream)
-             : bwd_run<false>(d, x, h0, c0, W, R, reserve, dy, dhT, dcT, dx, dh0, dc0, dW, dR, db, ws, o, plain, stream);
+  // the step-wait limit: the default, the caller's, or (negative) none at all
+  const long long timeout_us = (opts && opts->wait_timeout_us > 0) ? opts->wait_timeout_us
+                               : (opts && opts->wait_timeout_us < 0) ? 0
+                                                                     : kBwdTimeoutUs;
+  return d->dtype == LSTM_BF16 ? bwd_run<true>(d, x, h0, c0, W, R, reserve, dy, dhT, dcT, dx, dh0, dc0, dW, dR, db,
+                                               ws, o, plain, timeout_us, stream)
+                               : bwd_run<false>(d, x, h0, c0, W, R, reserve, dy, dhT, dcT, dx, dh0, dc0, dW, dR, db,
+                                                ws, o, plain, timeout_us, stream);
 }
 
 lstm_status_t lstm_bwd(const lstm_desc_t* d, const void* x, const void* h0, const float* c0, const void* W,

@@ -286,3 +286,39 @@ def test_gpu_backward_unaligned_upstream_gradient(dev):
     say("misaligned dy: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     for k, v in errs.items():
         assert np.isfinite(v) and v <= TOL["bf16"], (k, v)
+
+
+@pytest.mark.parametrize("shape", [(1, 64, 256, 16, 4, "bf16"), (1, 64, 1024, 16, 3, "bf16")],
+                         ids=["one-M-tile", "K-quarters"])
+def test_gpu_backward_forced_wait_timeout(dev, shape):
+    """A negative wait limit fails every blocked step wait of the on-chip chain
+    at once: the kernel exits normally, lstm_bwd_last_error reports the
+    timeout, and the next call on the same workspace is clean and correct."""
+    import stacked_lstm_forward_amd as sl
+    from stacked_lstm_forward_amd import runner
+    L, I, H, B, T, dtype = shape
+    assert sl.lstm_bwd_chain_on_chip(sl.make_desc(L, I, H, B, T, dtype))
+    cfg = li.custom_config(L, I, H, B, T, dtype, cfg_id=995 + H)
+    inp = li.make_inputs(cfg, random_state=True)
+    dy, dhT, dcT = upstream(cfg, 996)
+    say(f"backward forced timeout {shape}")
+    tp = runner.prepare_train(inp, dy, dhT, dcT, dev)
+    tp.forward()
+    o = sl.BwdOpts()
+    o.wait_timeout_us = -1
+    p = tp.fwd
+    st = sl.lstm_bwd_ex(p.desc, p.x, p.h0, p.c0, p.W, p.R, tp.reserve, tp.dy, tp.dhT, tp.dcT, tp.dx, tp.dh0, tp.dc0,
+                        tp.dW, tp.dR, tp.db, tp.bws, None, o)
+    assert st == sl.LSTM_OK
+    assert sl.lstm_bwd_last_error(tp.bws) == sl.LSTM_ERR_BARRIER_TIMEOUT
+    tp.backward()  # the same workspace and buffers, default limit
+    assert sl.lstm_bwd_last_error(tp.bws) == sl.LSTM_OK
+    got = tp.grads_f64()
+    f32 = lambda a: None if a is None else np.asarray(a, dtype=np.float32).astype(np.float64)  # noqa: E731
+    ref = orcb.lstm_backward_inputs(inp, f32(dy), f32(dhT), f32(dcT))
+    errs = {k: rel_err(got[k], ref[k]) for k in ("dx", "dh0", "dc0")}
+    for k in ("dW", "dR", "db"):
+        errs[k] = max(rel_err(g, r) for g, r in zip(got[k], ref[k]))
+    say(f"after forced timeout {shape}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    for k, v in errs.items():
+        assert np.isfinite(v) and v <= TOL[dtype], (k, v)
